@@ -1,0 +1,429 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself -- hand-derived closed forms (tests/golden), an independent bit-level
+reference built on Python big integers, exact rational arithmetic, a library
+Hadamard matrix, and brute force on tiny inputs.  A dropped term, a wrong
+sign, offset, bit order, group index or transposed operand in the oracle fails
+at least one of them."""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle as O
+import qg_synth as S
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# independent bit-level references (Python integers, no NumPy bit ops)
+# ---------------------------------------------------------------------------
+def bigint_unpack_group(words, bits):
+    """Codes of one group from its 4*b words via one Python integer."""
+    v = int.from_bytes(np.asarray(words, dtype="<u4").tobytes(), "little")
+    return [(v >> (bits * j)) & ((1 << bits) - 1) for j in range(128)]
+
+
+def bigint_trellis_tile(words16):
+    """States of one 16x16 tile: the 768-bit stream as one integer, MSB first."""
+    v = int.from_bytes(np.asarray(words16, dtype=">u2").tobytes(), "big")
+    vv = (v << 768) | v                       # cyclic continuation
+    out = []
+    for i in range(256):
+        start = 3 * i
+        out.append((vv >> (1536 - start - 16)) & 0xFFFF)
+    return out
+
+
+def half_from_hex(h):
+    return float(np.array([int(h, 16)], dtype=np.uint16).view(np.float16)[0])
+
+
+# ---------------------------------------------------------------------------
+# packing
+# ---------------------------------------------------------------------------
+def test_unpack_golden_closed_forms():
+    n_cases = 0
+    with open(os.path.join(GOLD, "packing_closed_forms.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            b, words, codes = [p.strip() for p in line.split("|")]
+            b = int(b)
+            w = np.array([int(t, 16) for t in words.split()], dtype=np.uint32)
+            assert w.size == 4 * b
+            want = np.zeros(128, dtype=np.int64)
+            for kv in codes.split():
+                j, c = kv.split("=")
+                want[int(j)] = int(c)
+            got = O.unpack_uniform(w, 1, 128, b)[0]
+            np.testing.assert_array_equal(got, want)
+            n_cases += 1
+    assert n_cases >= 9
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_unpack_matches_bigint_reference(bits):
+    N, K = 5, 384
+    w = S.uniform_code_words(N, K, bits, cfg_id=99, tensor_id=bits)
+    codes = O.unpack_uniform(w, N, K, bits)
+    G = K // 128
+    ww = w.reshape(N, G, 4 * bits)
+    for n in range(N):
+        for g in range(G):
+            ref = bigint_unpack_group(ww[n, g], bits)
+            np.testing.assert_array_equal(codes[n, 128 * g:128 * g + 128], ref)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_unpack_round_trip(bits):
+    rng = np.random.default_rng(5)
+    # every value at every in-group position (3-bit hits all 8 word straddles)
+    codes = np.array([[(j + v) % (1 << bits) for j in range(128)] for v in range(1 << bits)])
+    np.testing.assert_array_equal(O.unpack_uniform(O.pack_uniform(codes, bits), codes.shape[0], 128, bits), codes)
+    # random codes, several groups
+    codes = rng.integers(0, 1 << bits, size=(7, 640))
+    np.testing.assert_array_equal(O.unpack_uniform(O.pack_uniform(codes, bits), 7, 640, bits), codes)
+    # words -> codes -> words (no padding: every word pattern is a valid group)
+    w = rng.integers(0, 2**32, size=20 * 4 * bits, dtype=np.uint64).astype(np.uint32)
+    np.testing.assert_array_equal(O.pack_uniform(O.unpack_uniform(w, 20, 128, bits), bits), w)
+
+
+def test_three_bit_straddles_cover_all_word_boundaries():
+    # fields that cross a 32-bit word boundary in a 3-bit group
+    straddle = [j for j in range(128) if (3 * j) // 32 != (3 * j + 2) // 32]
+    assert straddle == [10, 21, 42, 53, 74, 85, 106, 117]
+    for j in straddle:
+        codes = np.zeros((1, 128), dtype=np.int64)
+        codes[0, j] = 5
+        w = O.pack_uniform(codes, 3)
+        assert bigint_unpack_group(w, 3)[j] == 5
+        assert O.unpack_uniform(w, 1, 128, 3)[0, j] == 5
+
+
+def test_mixed_rows_concatenate_in_order():
+    K = 256
+    cb = np.array([3, 4, 2, 3, 4], dtype=np.uint8)
+    w = S.mixed_code_words(cb, K, cfg_id=98)
+    off = O.row_word_offsets(cb, K)
+    assert off[-1] == w.size
+    got = O.unpack_mixed(w, cb, K)
+    for n, b in enumerate(cb):
+        seg = w[off[n]:off[n + 1]].reshape(2, 4 * int(b))
+        ref = bigint_unpack_group(seg[0], int(b)) + bigint_unpack_group(seg[1], int(b))
+        np.testing.assert_array_equal(got[n], ref)
+
+
+# ---------------------------------------------------------------------------
+# dequantisation
+# ---------------------------------------------------------------------------
+def test_dequant_golden_closed_forms():
+    n = 0
+    with open(os.path.join(GOLD, "dequant_closed_forms.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            b, c, sh, val = line.split()
+            s = np.array([[int(sh, 16)]], dtype=np.uint16).view(np.float16)
+            codes = np.full((1, 128), int(c))
+            w = O.dequant_uniform(codes, s, int(b))
+            assert w[0, 0] == float(val) and w[0, 127] == float(val)
+            n += 1
+    assert n >= 10
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_dequant_exact_for_every_fp16_scale(bits):
+    """(c - o_b) * s against integer arithmetic: s = m * 2^(e-11) exactly, so
+    w = (2c - (2^b - 1)) * m * 2^(e - 12) with an integer product.  Exhaustive over
+    every finite positive fp16 scale and every code; also checks w fits fp32."""
+    s16 = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16)
+    s = s16.astype(np.float64)
+    f, e = np.frexp(s)                       # s = f * 2^e, f in [0.5, 1)
+    m = (f * 2048).astype(np.int64)          # 11-bit integer significand
+    assert np.all(np.ldexp(m.astype(np.float64), e - 11) == s)
+    for c in range(1 << bits):
+        codes = np.full((s.size, 128), c)
+        w = O.dequant_uniform(codes, s.reshape(-1, 1), bits)[:, 0]
+        exact = np.ldexp(((2 * c - ((1 << bits) - 1)) * m).astype(np.float64), e - 12)
+        np.testing.assert_array_equal(w, exact)
+        np.testing.assert_array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+def test_dequant_group_index_and_rows():
+    N, K, b = 3, 512, 3
+    rng = np.random.default_rng(1)
+    codes = rng.integers(0, 8, size=(N, K))
+    s = (rng.random((N, K // 128)) + 0.5).astype(np.float16)
+    w = O.dequant_uniform(codes, s, b)
+    for n in range(N):
+        for k in range(0, K, 37):
+            want = (Fraction(int(codes[n, k])) - Fraction(7, 2)) * Fraction(float(s[n, k // 128]))
+            assert Fraction(w[n, k]) == want
+
+
+# ---------------------------------------------------------------------------
+# contraction: brute force with exact rationals
+# ---------------------------------------------------------------------------
+def brute_gemv(x16, words, s16, N, K, bits):
+    xs = [[Fraction(float(v)) for v in row] for row in x16]
+    G = K // 128
+    ww = np.asarray(words).reshape(N, G, 4 * bits)
+    o = Fraction((1 << bits) - 1, 2)
+    out = []
+    for xr in xs:
+        row = []
+        for n in range(N):
+            acc = Fraction(0)
+            for g in range(G):
+                sc = Fraction(float(s16[n, g]))
+                cs = bigint_unpack_group(ww[n, g], bits)
+                for j in range(128):
+                    acc += xr[128 * g + j] * (cs[j] - o) * sc
+            row.append(acc)
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("bits,K,N,M", [(3, 128, 4, 1), (3, 256, 3, 2), (2, 384, 2, 1), (4, 256, 2, 2)])
+def test_gemv_brute_force_exact(bits, K, N, M):
+    x = S.activations(M, K, cfg_id=97, tensor_id=bits)
+    s = S.scales(N, K, cfg_id=97, tensor_id=10 + bits)
+    w = S.uniform_code_words(N, K, bits, cfg_id=97, tensor_id=20 + bits)
+    y = O.gemv_uniform(x, w, s, N, K, bits)
+    ref = brute_gemv(x, w, s, N, K, bits)
+    for m in range(M):
+        for n in range(N):
+            r = float(ref[m][n])
+            assert abs(y[m, n] - r) <= 1e-13 * max(1.0, abs(r))
+
+
+def test_gemv_closed_forms():
+    K, N, b = 512, 8, 3
+    G = K // 128
+    x = S.activations(2, K, cfg_id=96)
+    s = S.scales(N, K, cfg_id=96)
+    xs = x.astype(np.float64).reshape(2, G, 128).sum(-1)          # [M][G]
+    for c in (0, 5, 7):
+        codes = np.full((N, K), c)
+        y = O.gemv_uniform(x, O.pack_uniform(codes, b), s, N, K, b)
+        want = (c - 3.5) * (xs @ s.astype(np.float64).T)
+        np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+    # one-hot x picks a weight column: y[n] = w[n][k]
+    codes = np.random.default_rng(2).integers(0, 8, size=(N, K))
+    w = O.pack_uniform(codes, b)
+    for k in (0, 127, 128, 300, 511):
+        e = np.zeros((1, K), dtype=np.float16)
+        e[0, k] = 1.0
+        y = O.gemv_uniform(e, w, s, N, K, b)[0]
+        np.testing.assert_array_equal(y, (codes[:, k] - 3.5) * s[:, k // 128].astype(np.float64))
+    # x = 0 gives exactly 0
+    assert np.all(O.gemv_uniform(np.zeros((1, K), np.float16), w, s, N, K, b) == 0.0)
+
+
+def test_gemv_rows_subset_matches_full():
+    N, K, b = 64, 384, 3
+    x = S.activations(3, K, cfg_id=95)
+    s = S.scales(N, K, cfg_id=95)
+    w = S.uniform_code_words(N, K, b, cfg_id=95)
+    full = O.gemv_uniform(x, w, s, N, K, b)
+    rows = np.array([0, 5, 17, 63])
+    np.testing.assert_array_equal(O.gemv_uniform_rows(x, w, s, N, K, b, rows), full[:, rows])
+
+
+def test_gemv_mixed_matches_uniform_rows():
+    K = 256
+    cb = S.column_bits(40, 0.2, 4, cfg_id=94)
+    assert int((cb == 4).sum()) == 8
+    x = S.activations(2, K, cfg_id=94)
+    s = S.scales(40, K, cfg_id=94)
+    w = S.mixed_code_words(cb, K, cfg_id=94)
+    y = O.gemv_mixed(x, w, s, cb, K)
+    off = O.row_word_offsets(cb, K)
+    for n in range(40):
+        b = int(cb[n])
+        yn = O.gemv_uniform(x, w[off[n]:off[n + 1]], s[n:n + 1], 1, K, b)
+        np.testing.assert_array_equal(y[:, n:n + 1], yn)
+
+
+# ---------------------------------------------------------------------------
+# Hadamard rotation
+# ---------------------------------------------------------------------------
+def test_hadamard_matches_scipy_sylvester():
+    H = O.hadamard128()
+    np.testing.assert_array_equal(H, scipy.linalg.hadamard(128) * 2.0 ** -3.5)
+
+
+def test_rotation_closed_forms_and_involution():
+    vals = {}
+    with open(os.path.join(GOLD, "hadamard_closed_forms.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = float(v)
+    e0 = np.zeros((1, 256))
+    e0[0, 128] = 1.0                                   # e_0 of the second group
+    r = O.rotate(e0)
+    assert np.all(r[0, :128] == 0.0)
+    np.testing.assert_allclose(r[0, 128:], vals["e0_entry"], rtol=0, atol=1e-16)
+    ones = np.ones((1, 128))
+    r = O.rotate(ones)[0]
+    assert abs(r[0] - vals["ones_entry0"]) < 1e-12 and np.all(np.abs(r[1:]) < 1e-12)
+    # involution H(Hx) = x (2^-3.5 is irrational, so up to fp64 rounding)
+    x = S.activations(3, 384, cfg_id=93).astype(np.float64)
+    np.testing.assert_allclose(O.rotate(O.rotate(x)), x, rtol=0, atol=4e-15 * np.abs(x).max())
+
+
+def test_rotation_uses_per_group_blocks():
+    x = S.activations(1, 256, cfg_id=92).astype(np.float64)
+    H = scipy.linalg.hadamard(128) / math.sqrt(128)
+    want = np.concatenate([H @ x[0, :128], H @ x[0, 128:]])
+    np.testing.assert_allclose(O.rotate(x)[0], want, rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# trellis
+# ---------------------------------------------------------------------------
+def _golden_trellis_tiles():
+    cases = []
+    with open(os.path.join(GOLD, "trellis_closed_forms.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            name, pat, states = [p.strip() for p in line.split("|")]
+            w = np.zeros(48, dtype=np.uint16)
+            if pat.startswith("all "):
+                w[:] = int(pat.split()[1], 16)
+            elif pat.startswith("repeat "):
+                p = [int(t, 16) for t in pat.split()[1:]]
+                w[:] = np.array(p * (48 // len(p)), dtype=np.uint16)
+            else:
+                first = pat.split()[0]
+                idx, val = first.split("=")
+                w[int(idx.replace("word", ""))] = int(val, 16)
+            want = {int(a): int(b, 16) for a, b in (kv.split("=") for kv in states.split())}
+            cases.append((name, w, want))
+    return cases
+
+
+def test_trellis_golden_closed_forms():
+    cases = _golden_trellis_tiles()
+    assert len(cases) == 5
+    for name, w, want in cases:
+        st = O.trellis_states(w.reshape(1, 1, 48), 16, 16)        # [n=r][k=c]
+        for i, v in want.items():
+            r, c = divmod(i, 16)
+            assert int(st[r, c]) == v, (name, i)
+        ref = bigint_trellis_tile(w)
+        for i, v in want.items():
+            assert ref[i] == v, (name, i)
+
+
+def test_trellis_matches_bigint_and_recurrence():
+    N, K = 32, 48
+    words = S.trellis_words(N, K, cfg_id=91)
+    st = O.trellis_states(words, N, K)
+    for tn in range(N // 16):
+        for tk in range(K // 16):
+            ref = bigint_trellis_tile(words[tn, tk])
+            v = int.from_bytes(words[tn, tk].astype(">u2").tobytes(), "big")
+            for i in range(256):
+                r, c = divmod(i, 16)
+                assert int(st[16 * tn + r, 16 * tk + c]) == ref[i]
+                # shift-register recurrence, including the wrap 255 -> 0
+                nxt = ref[(i + 1) % 256]
+                pos = (3 * i + 16) % 768
+                three = 0
+                for u in range(3):
+                    three = (three << 1) | ((v >> (767 - ((pos + u) % 768))) & 1)
+                assert nxt == ((ref[i] << 3) | three) & 0xFFFF
+
+
+def test_trellis_dequant_uses_codebook_and_group_scale():
+    N, K = 16, 256
+    words = S.trellis_words(N, K, cfg_id=90)
+    cb = S.codebook(cfg_id=90)
+    s = S.scales(N, K, cfg_id=90)
+    st = O.trellis_states(words, N, K)
+    w = O.trellis_dequant(st, cb, s)
+    for n in (0, 7, 15):
+        for k in (0, 127, 128, 255):
+            assert w[n, k] == float(cb[st[n, k]]) * float(s[n, k // 128])
+            assert w[n, k] == float(np.float32(cb[st[n, k]]) * np.float32(s[n, k // 128]))
+
+
+def test_trellis_gemv_brute_force():
+    N, K = 16, 128
+    words = S.trellis_words(N, K, cfg_id=89)
+    cb = S.codebook(cfg_id=89)
+    s = S.scales(N, K, cfg_id=89)
+    x = S.activations(1, K, cfg_id=89)
+    y = O.gemv_trellis(x, words, cb, s, N, K)
+    H = scipy.linalg.hadamard(128) / math.sqrt(128)
+    xr = H @ x[0].astype(np.float64)
+    for n in range(N):
+        acc = []
+        for k in range(K):
+            tk, c = divmod(k, 16)
+            r = n % 16
+            state = bigint_trellis_tile(words[n // 16, tk])[16 * r + c]
+            acc.append(xr[k] * float(cb[state]) * float(s[n, 0]))
+        assert abs(y[0, n] - math.fsum(acc)) <= 1e-12 * max(1.0, abs(y[0, n]))
+
+
+# ---------------------------------------------------------------------------
+# MLP
+# ---------------------------------------------------------------------------
+def test_mlp_brute_force_tiny():
+    H, I = 128, 256
+    rng = np.random.default_rng(3)
+    wg = rng.standard_normal((I, H)) * 0.05
+    wu = rng.standard_normal((I, H)) * 0.05
+    wd = rng.standard_normal((H, I)) * 0.05
+    x = S.activations(1, H, cfg_id=88)
+    out = O.mlp(x, wg, wu, wd)[0]
+    xv = x[0].astype(np.float64)
+    h = []
+    for i in range(I):
+        g = math.fsum(xv * wg[i])
+        u = math.fsum(xv * wu[i])
+        h.append(g / (1.0 + math.exp(-g)) * u)
+    for n in range(H):
+        ref = math.fsum(np.array(h) * wd[n])
+        assert abs(out[n] - ref) <= 1e-12 * max(1.0, abs(ref))
+    assert np.all(O.mlp(np.zeros((1, H)), wg, wu, wd) == 0.0)
+
+
+def test_silu_definition_points():
+    z = np.array([0.0, 1.0, -1.0, 20.0, -20.0])
+    want = [0.0, 1 / (1 + math.exp(-1)), -1 / (1 + math.exp(1)), 20 / (1 + math.exp(-20)), -20 / (1 + math.exp(20))]
+    np.testing.assert_allclose(O.silu(z), want, rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# mixed-precision mask (20 % of columns) and its bits/weight
+# ---------------------------------------------------------------------------
+def test_mixed_mask_counts_and_bpw():
+    gu = S.column_bits(17408, 0.2, 4, cfg_id=S.CFG_MLP, tensor_id=S.T_MASK)
+    dn = S.column_bits(5120, 0.2, 2, cfg_id=S.CFG_MLP, tensor_id=S.T_MASK + 100)
+    assert int((gu == 4).sum()) == 3482 and int((gu == 3).sum()) == 17408 - 3482
+    assert int((dn == 2).sum()) == 1024 and int((dn == 3).sum()) == 4096
+    K_gu, K_dn = 5120, 17408
+    bytes_gu = (int(gu.astype(np.int64).sum()) * K_gu) // 8 + 17408 * (K_gu // 128) * 2
+    bytes_dn = (int(dn.astype(np.int64).sum()) * K_dn) // 8 + 5120 * (K_dn // 128) * 2
+    assert bytes_gu == 37044480 and bytes_dn == 32587776
+    total = 2 * bytes_gu + bytes_dn
+    assert total == 106676736
+    bpw = total * 8 / (2 * 17408 * 5120 + 5120 * 17408)
+    assert abs(bpw - 3.1917) < 5e-5
+
+
+def test_normwise_error_metric():
+    r = np.array([[1.0, -4.0, 2.0]])
+    y = np.array([[1.0, -4.002, 2.001]])
+    assert abs(O.normwise_rel_err(y, r) - 0.002 / 4.0) < 1e-15
