@@ -1,0 +1,120 @@
+// qg_decode.h -- device layout of packed codes and the in-register decode used by
+// every kernel of the library (run kernels and checking kernels alike).
+//
+// Device layout (written once by the repack kernel at create time).
+//   Columns are grouped in tiles of 16.  For tile t and 128-group g the 64 lanes
+//   of a wave own 64*B consecutive uint32 words: lane l holds column
+//   16*t + (l & 15), quarter q = l >> 4, i.e. the 32 codes c_0..c_31 of that
+//   column at k = 128*g + 32*q + j.  One wave-wide load of B words per lane
+//   therefore reads one contiguous 256*B-byte block (fully coalesced).
+//   Within a lane the codes are stored as 16 pairs (c_{2i}, c_{2i+1}); pair i
+//   keeps c_{2i} in the low 16-bit half and c_{2i+1} at the same bit offset in
+//   the high half:
+//     B = 2: word i/8, offset 2*(i%8)         (8 pairs per word)
+//     B = 4: word i/4, offset 4*(i%4)         (4 pairs per word)
+//     B = 3: i < 15: word i/5, offset 3*(i%5) (5 pairs per word, bit 15/31 spare)
+//            i = 15: bit u of c30 is bit 15 of word u, bit u of c31 bit 31 of word u.
+//   Scales: fp16 [tile][g][16].
+//
+// Decode.  An fp16 whose bits are an integer v < 2048 has the value v * 2^-24
+// exactly (exponent field 0: subnormal m * 2^-24; exponent field 1:
+// (1024 + m) * 2^-24).  So masking a B-bit code field that sits at bit offset p
+// (p + B <= 11) in both halves of a word yields, with one AND, the fp16 pair
+// (c_lo * 2^(p-24), c_hi * 2^(p-24)) -- exact, no conversion instruction.
+// gfx950's v_dot2_f32_f16 and v_mfma_f32_16x16x32_f16 consume such subnormal
+// fp16 operands exactly.  Codes at offsets beyond the exact range are first
+// shifted down.  The GEMV keeps one fp32 accumulator per offset ("class") and
+// rescales them per group; the MFMA path shifts every pair to offset 1 so a
+// whole operand shares one scale.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+template <int B> struct Pair {
+  // word holding pair i, its bit offset, and (GEMV) the shift applied before masking
+  static constexpr int word(int i) { return B == 2 ? i / 8 : B == 4 ? i / 4 : (i < 15 ? i / 5 : 0); }
+  static constexpr int off(int i) { return B == 2 ? 2 * (i % 8) : B == 4 ? 4 * (i % 4) : 3 * (i % 5); }
+  static constexpr int gshift(int i) {
+    return B == 2 ? (i % 8 < 5 ? 0 : 10) : B == 4 ? (i % 4 < 2 ? 0 : 8) : (i % 5 < 3 ? 0 : 9);
+  }
+  // GEMV class of pair i: bit offset after the shift (3-bit pair 15 is built at 6)
+  static constexpr int cls(int i) { return (B == 3 && i == 15) ? 6 : off(i) - gshift(i); }
+  static constexpr uint32_t mask() { return (1u << B) - 1u; }
+  static constexpr uint32_t m2(int p) { return (mask() << p) * 0x10001u; }  // field at p in both halves
+};
+
+// ---- GEMV decode: pair registers at their class offsets (1 AND per pair, shifts shared per word)
+template <int B>
+__device__ __forceinline__ void decode_classes(const uint32_t (&w)[B], uint32_t (&r)[16]) {
+  using P = Pair<B>;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (B == 3 && i == 15) continue;
+    const uint32_t v = w[P::word(i)] >> P::gshift(i);
+    r[i] = v & P::m2(P::cls(i));
+  }
+  if constexpr (B == 3) {
+    // spare bits 15/31 of the three words -> (c30, c31) at offset 6
+    r[15] = ((w[0] >> 9) & 0x00400040u) | ((w[1] >> 8) & 0x00800080u) | ((w[2] >> 7) & 0x01000100u);
+  }
+}
+
+// ---- MFMA decode: every pair at offset 1 (value 2*c*2^-24 = c*2^-23)
+template <int B>
+__device__ __forceinline__ void decode_off1(const uint32_t (&w)[B], uint32_t (&r)[16]) {
+  using P = Pair<B>;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (B == 3 && i == 15) continue;
+    const int o = P::off(i);
+    const uint32_t v = (o == 0) ? (w[P::word(i)] << 1) : (w[P::word(i)] >> (o - 1));
+    r[i] = v & P::m2(1);
+  }
+  if constexpr (B == 3) {
+    r[15] = ((w[0] >> 14) & 0x00020002u) | ((w[1] >> 13) & 0x00040004u) | ((w[2] >> 12) & 0x00080008u);
+  }
+}
+
+// fp16 bits of -o_b * 2^-23 = -(2^B - 1) * 2^-24: the per-weight offset at the MFMA scale
+template <int B> __device__ constexpr uint32_t off1_offset_pair() {
+  return ((0x8000u | ((1u << B) - 1u)) * 0x10001u);
+}
+
+__device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+}
+
+__device__ __forceinline__ h8_t as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint4 v = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(h8_t, v);
+}
+
+__device__ __forceinline__ f4_t mfma16(h8_t a, h8_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+template <int B> __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[B]) {
+  if constexpr (B == 2) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (B == 3) {
+    // 12-byte aligned-to-4 load
+    w[0] = p[0]; w[1] = p[1]; w[2] = p[2];
+  } else {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+}
+
+}  // namespace qg

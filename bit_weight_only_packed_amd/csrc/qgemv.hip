@@ -1,0 +1,484 @@
+// qgemv.hip -- host side of the C ABI declared in include/qgemv.h: descriptor
+// validation, device check, weight re-layout into handle-owned memory, launch
+// planning per (shape, row count) and dispatch onto the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/qgemv.h"
+#include "qg_kernels.h"
+
+using namespace qg;
+
+namespace {
+
+thread_local std::string g_err;
+
+qg_status fail(qg_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define QG_HIP(call)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess) return fail(QG_ERR_DEVICE, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+struct Launch {
+  int T = 0, NW = 0, S = 0;  // 0 = built-in choice
+};
+
+struct HostSeg {
+  int bits, tiles, tile0, ncols;
+  uint32_t* codes = nullptr;
+  uint16_t* scales = nullptr;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int mclass(int M) { return M <= 1 ? 0 : (M <= 16 ? 1 : 2); }
+
+}  // namespace
+
+struct qg_plan {
+  int K = 0, N = 0, G = 0, format = 0, max_M = 0;
+  uint32_t flags = 0;
+  int device = 0;
+  std::vector<HostSeg> segs;
+  std::vector<uint8_t> col_bits;  // host copy (uniform: per column)
+  int total_tiles = 0;
+  int32_t* col_map = nullptr;     // device [16*total_tiles]
+  int64_t weight_bytes = 0;
+  float* partial = nullptr;       // device workspace
+  size_t partial_floats = 0;
+  uint16_t* hbuf = nullptr;       // device [max_M][N] fp16, MLP intermediate
+  Launch over[3];
+  // trellis
+  uint32_t* tcodes = nullptr;     // device layout of trellis tiles
+  uint16_t* tscales = nullptr;    // [N/16 tiles][G][16]
+  uint16_t* codebook = nullptr;   // device copy, 65536 fp16
+};
+
+namespace {
+
+// ---- launch planning --------------------------------------------------------
+Launch choose(const qg_plan* h, int M) {
+  Launch L = h->over[mclass(M)];
+  const int G = h->G;
+  if (h->format == QG_FMT_TRELLIS3) {
+    if (L.T <= 0) L.T = 1;
+    if (L.NW <= 0) L.NW = 4;
+    if (L.S <= 0) L.S = 1;
+    return L;
+  }
+  if (M == 1) {
+    if (L.T <= 0) L.T = 1;
+    if (L.NW <= 0) L.NW = 8;
+    if (L.S <= 0) {
+      const int tilesets = (h->total_tiles + L.T - 1) / L.T;
+      int S = std::max(1, 1024 / std::max(1, tilesets));
+      S = std::min(S, std::max(1, G / L.NW));
+      S = std::min(S, 16);
+      L.S = S;
+    }
+  } else {
+    if (L.T <= 0) L.T = 2;
+    if (L.NW <= 0) L.NW = 4;
+    if (L.S <= 0) {
+      const int tilesets = (h->total_tiles + L.T - 1) / L.T;
+      int S = std::max(1, 512 / std::max(1, tilesets));
+      S = std::min(S, std::max(1, G / L.NW));
+      S = std::min(S, 8);
+      L.S = S;
+    }
+  }
+  L.S = std::min(L.S, G);
+  if (M == 1) {
+    // the K slice of x plus its sums must fit the 64 KiB LDS window: 272 B per group
+    const int min_s = (G + 199) / 200;
+    L.S = std::max(L.S, std::min(min_s, G));
+  }
+  return L;
+}
+
+size_t partial_need(const qg_plan* h, int S, int M) {
+  return S <= 1 ? 0 : (size_t)2 * S * M * (size_t)(16 * h->total_tiles);
+}
+
+qg_status ensure_workspace(qg_plan* h) {
+  size_t need = 0;
+  for (int c = 0; c < 3; ++c) {
+    const int Mc = c == 0 ? 1 : (c == 1 ? 16 : 32);
+    if (Mc > h->max_M && c > 0 && (c == 1 ? 2 : 17) > h->max_M) continue;
+    const int Mm = std::min(Mc, h->max_M);
+    need = std::max(need, partial_need(h, choose(h, Mm).S, Mm));
+  }
+  if (need > h->partial_floats) {
+    if (h->partial) hipFree(h->partial);
+    h->partial = nullptr;
+    h->partial_floats = 0;
+    if (hipMalloc(&h->partial, need * sizeof(float)) != hipSuccess)
+      return fail(QG_ERR_OOM, "workspace allocation of %zu bytes failed", need * sizeof(float));
+    h->partial_floats = need;
+  }
+  return QG_OK;
+}
+
+qg_status check_device(int* dev) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess) return fail(QG_ERR_UNSUPPORTED, "no HIP device available");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, d) != hipSuccess) return fail(QG_ERR_UNSUPPORTED, "cannot query HIP device");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(QG_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", d, prop.gcnArchName);
+  *dev = d;
+  return QG_OK;
+}
+
+void free_plan(qg_plan* h) {
+  if (!h) return;
+  for (auto& s : h->segs) {
+    if (s.codes) hipFree(s.codes);
+    if (s.scales) hipFree(s.scales);
+  }
+  if (h->col_map) hipFree(h->col_map);
+  if (h->partial) hipFree(h->partial);
+  if (h->hbuf) hipFree(h->hbuf);
+  if (h->tcodes) hipFree(h->tcodes);
+  if (h->tscales) hipFree(h->tscales);
+  if (h->codebook) hipFree(h->codebook);
+  delete h;
+}
+
+WSet wset_of(const qg_plan* h) {
+  WSet w{};
+  w.nseg = (int)h->segs.size();
+  for (int i = 0; i < w.nseg; ++i) {
+    const HostSeg& s = h->segs[i];
+    w.seg[i] = SegDev{s.codes, s.scales, s.bits, s.tiles, s.tile0};
+  }
+  w.col_map = h->col_map;
+  return w;
+}
+
+
+// ---- trellis (filled in by the trellis kernels) ----------------------------------
+qg_status create_trellis(qg_plan*, const qg_weight_desc*, hipStream_t) {
+  return fail(QG_ERR_UNSUPPORTED, "trellis format not built yet");
+}
+qg_status run_trellis(const qg_plan*, const uint16_t*, int, uint16_t*, hipStream_t) {
+  return fail(QG_ERR_UNSUPPORTED, "trellis format not built yet");
+}
+qg_status debug_trellis(const qg_plan*, uint16_t*, float*, hipStream_t) {
+  return fail(QG_ERR_UNSUPPORTED, "trellis format not built yet");
+}
+
+// ---- uniform create -----------------------------------------------------------
+qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
+  const int N = d->N, K = d->K, G = K / QG_GROUP;
+  h->col_bits.resize(N);
+  if (d->bits == 0) {
+    if (!d->col_bits) return fail(QG_ERR_INVALID_ARG, "bits == 0 needs col_bits (host, N entries)");
+    for (int n = 0; n < N; ++n) {
+      const int b = d->col_bits[n];
+      if (b < 2 || b > 4) return fail(QG_ERR_INVALID_ARG, "col_bits[%d] = %d is not in {2,3,4}", n, b);
+      h->col_bits[n] = (uint8_t)b;
+    }
+  } else {
+    if (d->bits < 2 || d->bits > 4) return fail(QG_ERR_INVALID_ARG, "bits = %d is not in {0,2,3,4}", d->bits);
+    std::fill(h->col_bits.begin(), h->col_bits.end(), (uint8_t)d->bits);
+  }
+  // segments: columns grouped by width (ascending column order inside each)
+  std::vector<int32_t> cmap;
+  std::vector<int64_t> row_off(N);
+  int64_t acc = 0;
+  for (int n = 0; n < N; ++n) {
+    row_off[n] = acc;
+    acc += (int64_t)h->col_bits[n] * K / 32;
+  }
+  h->weight_bytes = acc * 4 + (int64_t)N * G * 2;
+  int tile0 = 0;
+  for (int b = 2; b <= 4; ++b) {
+    std::vector<int32_t> cols;
+    for (int n = 0; n < N; ++n)
+      if (h->col_bits[n] == b) cols.push_back(n);
+    if (cols.empty()) continue;
+    HostSeg s;
+    s.bits = b;
+    s.ncols = (int)cols.size();
+    s.tiles = (s.ncols + 15) / 16;
+    s.tile0 = tile0;
+    tile0 += s.tiles;
+    cols.resize((size_t)16 * s.tiles, -1);
+    cmap.insert(cmap.end(), cols.begin(), cols.end());
+    h->segs.push_back(s);
+  }
+  h->total_tiles = tile0;
+  QG_HIP(hipMalloc(&h->col_map, cmap.size() * sizeof(int32_t)));
+  QG_HIP(hipMemcpyAsync(h->col_map, cmap.data(), cmap.size() * sizeof(int32_t), hipMemcpyHostToDevice, st));
+  int64_t* d_off = nullptr;
+  QG_HIP(hipMalloc(&d_off, N * sizeof(int64_t)));
+  hipError_t e = hipMemcpyAsync(d_off, row_off.data(), N * sizeof(int64_t), hipMemcpyHostToDevice, st);
+  for (auto& s : h->segs) {
+    if (e != hipSuccess) break;
+    const size_t nslot = (size_t)s.tiles * G * 64;
+    if (hipMalloc(&s.codes, nslot * s.bits * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&s.scales, (size_t)s.tiles * G * 16 * sizeof(uint16_t)) != hipSuccess) {
+      hipFree(d_off);
+      return fail(QG_ERR_OOM, "device allocation for the weight layout failed");
+    }
+    const int threads = 256;
+    const unsigned blocks = (unsigned)((nslot + threads - 1) / threads);
+    k_repack_uniform<<<blocks, threads, 0, st>>>((const uint32_t*)d->codes, d_off, d->scales,
+                                                 h->col_map + 16 * s.tile0, s.bits, s.tiles, G, s.codes, s.scales);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  hipFree(d_off);
+  if (e != hipSuccess) return fail(QG_ERR_DEVICE, "weight re-layout failed: %s", hipGetErrorString(e));
+  return QG_OK;
+}
+
+// ---- dispatch ------------------------------------------------------------------
+template <int T>
+void launch_m1(const RunArgs& a, int NW, size_t lds, unsigned grid, bool dual, hipStream_t st) {
+  if (dual) k_gemv_m1<T, true><<<grid, NW * 64, lds, st>>>(a);
+  else k_gemv_m1<T, false><<<grid, NW * 64, lds, st>>>(a);
+}
+
+template <int T, int MT>
+void launch_mfma_t(const RunArgs& a, int NW, size_t lds, unsigned grid, bool dual, hipStream_t st) {
+  if (dual) k_gemm_mfma<T, MT, true><<<grid, NW * 64, lds, st>>>(a);
+  else k_gemm_mfma<T, MT, false><<<grid, NW * 64, lds, st>>>(a);
+}
+
+template <int MT>
+void launch_mfma(const RunArgs& a, int T, int NW, size_t lds, unsigned grid, bool dual, hipStream_t st) {
+  switch (T) {
+    case 1: launch_mfma_t<1, MT>(a, NW, lds, grid, dual, st); break;
+    case 2: launch_mfma_t<2, MT>(a, NW, lds, grid, dual, st); break;
+    default: launch_mfma_t<4, MT>(a, NW, lds, grid, dual, st); break;
+  }
+}
+
+// one GEMV/GEMM over a uniform handle (or the fused gate+up pair when h2 != NULL)
+qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, int M, uint16_t* y, int ldy,
+                      hipStream_t st) {
+  Launch L = choose(h, M);
+  int T = L.T;
+  if (M == 1) T = (T >= 2) ? 2 : 1;
+  else T = (T >= 4) ? 4 : (T >= 2 ? 2 : 1);
+  int NW = (L.NW >= 8) ? 8 : 4;
+  const int S = L.S;
+  if (M > 1) {
+    const int MT = M <= 16 ? 1 : 2;
+    while ((h2 ? 2 : 1) * NW * T * MT * 1024 > 65536) {
+      if (NW == 8) NW = 4;
+      else T /= 2;
+    }
+  }
+  RunArgs a{};
+  a.w[0] = wset_of(h);
+  if (h2) a.w[1] = wset_of(h2);
+  a.x = x;
+  a.y = y;
+  a.partial = h->partial;
+  a.M = M;
+  a.K = h->K;
+  a.G = h->G;
+  a.ldy = ldy;
+  a.NP = 16 * h->total_tiles;
+  a.T = T;
+  a.S = S;
+  int pre = 0;
+  for (int i = 0; i < (int)h->segs.size(); ++i) {
+    a.ts_prefix[i] = pre;
+    pre += (h->segs[i].tiles + T - 1) / T;
+  }
+  for (int i = (int)h->segs.size(); i <= MAX_SEG; ++i) a.ts_prefix[i] = pre;
+  if (S > 1 && partial_need(h, S, M) > h->partial_floats)
+    return fail(QG_ERR_INVALID_ARG, "workspace too small for %d K-slices at M=%d", S, M);
+  const unsigned grid = (unsigned)pre * (unsigned)S;
+  const bool dual = h2 != nullptr;
+  if (M == 1) {
+    const int Gs = (h->G + S - 1) / S + 1;
+    const size_t lds = (size_t)Gs * 256 + (size_t)Gs * 16 + (size_t)2 * NW * T * 16 * sizeof(float);
+    if (T == 2) launch_m1<2>(a, NW, lds, grid, dual, st);
+    else launch_m1<1>(a, NW, lds, grid, dual, st);
+  } else {
+    const int MT = M <= 16 ? 1 : 2;
+    const size_t lds = (size_t)(dual ? 2 : 1) * NW * T * MT * 4 * 64 * sizeof(float);
+    if (lds > 65536) return fail(QG_ERR_INVALID_ARG, "launch needs %zu B of LDS (max 65536): fewer tiles or waves", lds);
+    if (MT == 1) launch_mfma<1>(a, T, NW, lds, grid, dual, st);
+    else launch_mfma<2>(a, T, NW, lds, grid, dual, st);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  if (S > 1) {
+    const int64_t n = (int64_t)M * a.NP;
+    const int threads = 256;
+    const unsigned blocks = (unsigned)((n + threads - 1) / threads);
+    if (dual) k_splitk_reduce<true><<<blocks, threads, 0, st>>>(h->partial, S, M, a.NP, h->col_map, y, ldy);
+    else k_splitk_reduce<false><<<blocks, threads, 0, st>>>(h->partial, S, M, a.NP, h->col_map, y, ldy);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_ERR_DEVICE, "reduce launch failed: %s", hipGetErrorString(e));
+  }
+  if (getenv("QG_DEBUG_SYNC")) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel failed: %s", hipGetErrorString(e));
+  }
+  return QG_OK;
+}
+
+}  // namespace
+
+// =================================================================================
+// C ABI
+// =================================================================================
+extern "C" {
+
+const char* qg_last_error(void) { return g_err.c_str(); }
+
+qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, void* stream) {
+  g_err.clear();
+  if (!out) return fail(QG_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!d) return fail(QG_ERR_INVALID_ARG, "desc is NULL");
+  if (d->group_size != QG_GROUP) return fail(QG_ERR_INVALID_ARG, "group_size must be 128 (got %d)", d->group_size);
+  if (d->K <= 0 || d->K % QG_GROUP) return fail(QG_ERR_INVALID_ARG, "K = %d is not a positive multiple of 128", d->K);
+  if (d->N <= 0 || d->N % 16) return fail(QG_ERR_INVALID_ARG, "N = %d is not a positive multiple of 16", d->N);
+  if (max_M < 1 || max_M > QG_MAX_M) return fail(QG_ERR_INVALID_ARG, "max_M = %d is not in [1, 32]", max_M);
+  if (!d->codes || !d->scales) return fail(QG_ERR_INVALID_ARG, "codes and scales must be device pointers");
+  if (!aligned16(d->codes) || !aligned16(d->scales)) return fail(QG_ERR_INVALID_ARG, "codes/scales must be 16-byte aligned");
+  if (d->format != QG_FMT_UNIFORM && d->format != QG_FMT_TRELLIS3)
+    return fail(QG_ERR_INVALID_ARG, "unknown format %d", d->format);
+  if (d->format == QG_FMT_TRELLIS3) {
+    if (!d->codebook || !aligned16(d->codebook)) return fail(QG_ERR_INVALID_ARG, "trellis needs a 16-byte aligned codebook");
+  }
+  int dev = 0;
+  qg_status s = check_device(&dev);
+  if (s != QG_OK) return s;
+  qg_plan* h = new (std::nothrow) qg_plan();
+  if (!h) return fail(QG_ERR_OOM, "host allocation failed");
+  h->K = d->K;
+  h->N = d->N;
+  h->G = d->K / QG_GROUP;
+  h->format = d->format;
+  h->max_M = max_M;
+  h->flags = d->flags;
+  h->device = dev;
+  hipStream_t st = (hipStream_t)stream;
+  s = d->format == QG_FMT_UNIFORM ? create_uniform(h, d, st) : create_trellis(h, d, st);
+  if (s == QG_OK) s = ensure_workspace(h);
+  if (s == QG_OK && hipMalloc(&h->hbuf, (size_t)max_M * d->N * sizeof(uint16_t)) != hipSuccess)
+    s = fail(QG_ERR_OOM, "staging allocation failed");
+  if (s == QG_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(QG_ERR_DEVICE, "stream synchronisation failed");
+  if (s != QG_OK) {
+    free_plan(h);
+    return s;
+  }
+  *out = h;
+  return QG_OK;
+}
+
+qg_status qgemv_destroy(qg_handle h) {
+  g_err.clear();
+  free_plan(h);
+  return QG_OK;
+}
+
+qg_status qgemv_weight_bytes(qg_handle h, int64_t* bytes) {
+  g_err.clear();
+  if (!h || !bytes) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  *bytes = h->weight_bytes;
+  return QG_OK;
+}
+
+qg_status qgemv_set_launch(qg_handle h, int32_t M, int32_t tiles, int32_t waves, int32_t splits) {
+  g_err.clear();
+  if (!h) return fail(QG_ERR_INVALID_ARG, "NULL handle");
+  if (M < 1 || M > QG_MAX_M) return fail(QG_ERR_INVALID_ARG, "M = %d is not in [1, 32]", M);
+  if (waves > 0 && waves != 4 && waves != 8) return fail(QG_ERR_INVALID_ARG, "waves must be 4 or 8");
+  if (splits > 16) return fail(QG_ERR_INVALID_ARG, "splits must be <= 16");
+  Launch& L = h->over[mclass(M)];
+  L.T = tiles;
+  L.NW = waves;
+  L.S = splits;
+  return ensure_workspace(h);
+}
+
+qg_status qgemv_run(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* stream) {
+  g_err.clear();
+  if (!h || !x || !y) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  if (M < 1 || M > h->max_M) return fail(QG_ERR_INVALID_ARG, "M = %d is not in [1, %d]", M, h->max_M);
+  if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (h->format == QG_FMT_TRELLIS3) return run_trellis(h, x, M, y, st);
+  return run_uniform(h, nullptr, x, M, y, h->N, st);
+}
+
+qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t* x, int32_t M, uint16_t* out,
+                   void* stream) {
+  g_err.clear();
+  if (!gate || !up || !down || !x || !out) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  if (gate->format != QG_FMT_UNIFORM || up->format != QG_FMT_UNIFORM || down->format != QG_FMT_UNIFORM)
+    return fail(QG_ERR_UNSUPPORTED, "the fused MLP takes uniform-code handles");
+  if (gate->K != up->K || gate->N != up->N) return fail(QG_ERR_INVALID_ARG, "gate and up shapes differ");
+  if (gate->col_bits != up->col_bits) return fail(QG_ERR_INVALID_ARG, "gate and up need the same per-column widths");
+  if (down->K != gate->N) return fail(QG_ERR_INVALID_ARG, "down K (%d) != gate N (%d)", down->K, gate->N);
+  if (M < 1 || M > gate->max_M || M > down->max_M) return fail(QG_ERR_INVALID_ARG, "M = %d out of range", M);
+  if (!aligned16(x) || !aligned16(out)) return fail(QG_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  qg_status s = run_uniform(gate, up, x, M, gate->hbuf, gate->N, st);
+  if (s != QG_OK) return s;
+  return run_uniform(down, nullptr, gate->hbuf, M, out, down->N, st);
+}
+
+qg_status qgemv_debug_unpack(qg_handle h, int32_t* codes, void* stream) {
+  g_err.clear();
+  if (!h || !codes) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  if (h->format != QG_FMT_UNIFORM) return fail(QG_ERR_INVALID_ARG, "debug_unpack takes a uniform-code handle");
+  hipStream_t st = (hipStream_t)stream;
+  for (const auto& s : h->segs) {
+    SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0};
+    const int64_t n = (int64_t)s.tiles * h->G * 64;
+    k_debug_uniform<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(sd, h->col_map, h->G, h->K, codes, nullptr, nullptr);
+  }
+  QG_HIP(hipGetLastError());
+  return QG_OK;
+}
+
+qg_status qgemv_debug_dequant(qg_handle h, float* w, uint16_t* q16, void* stream) {
+  g_err.clear();
+  if (!h || !w) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  hipStream_t st = (hipStream_t)stream;
+  if (h->format == QG_FMT_TRELLIS3) return debug_trellis(h, nullptr, w, st);
+  for (const auto& s : h->segs) {
+    SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0};
+    const int64_t n = (int64_t)s.tiles * h->G * 64;
+    k_debug_uniform<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(sd, h->col_map, h->G, h->K, nullptr, w, q16);
+  }
+  QG_HIP(hipGetLastError());
+  return QG_OK;
+}
+
+qg_status qgemv_debug_trellis(qg_handle h, uint16_t* states, void* stream) {
+  g_err.clear();
+  if (!h || !states) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  if (h->format != QG_FMT_TRELLIS3) return fail(QG_ERR_INVALID_ARG, "debug_trellis takes a trellis handle");
+  return debug_trellis(h, states, nullptr, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before touching a device."""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+import bit_weight_only_packed_amd as Q
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return Q.lib()
+    except ImportError as e:  # the build step must have run first
+        pytest.fail(str(e))
+
+
+def test_exports_every_declared_symbol(L):
+    names = Q.declared_symbols()
+    assert {"qgemv_create", "qgemv_run", "qmlp_run", "qgemv_destroy", "qg_last_error",
+            "qgemv_debug_unpack", "qgemv_debug_dequant", "qgemv_debug_trellis",
+            "qgemv_weight_bytes", "qgemv_set_launch"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _desc(**kw):
+    d = Q._Desc()
+    d.K, d.N, d.group_size, d.format, d.bits = 512, 512, 128, 0, 3
+    d.codes, d.scales = 0x100000, 0x200000      # never dereferenced: validation fails first
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(K=500), "K"), (dict(K=0), "K"), (dict(N=20), "N"), (dict(group_size=64), "group_size"),
+    (dict(codes=0), "codes"), (dict(scales=0x200004), "aligned"), (dict(format=7), "format"),
+    (dict(format=1, codebook=None), "codebook"),
+])
+def test_create_rejects_bad_descriptor(L, kw, frag):
+    h = ctypes.c_void_p(1)
+    d = _desc(**kw)
+    st = L.qgemv_create(ctypes.byref(h), ctypes.byref(d), 8, None)
+    assert st == Q.QG_ERR_INVALID_ARG
+    assert h.value is None
+    assert frag in L.qg_last_error().decode()
+
+
+@pytest.mark.parametrize("max_M", [0, 33, -1])
+def test_create_rejects_bad_max_m(L, max_M):
+    h = ctypes.c_void_p()
+    d = _desc()
+    assert L.qgemv_create(ctypes.byref(h), ctypes.byref(d), max_M, None) == Q.QG_ERR_INVALID_ARG
+
+
+def test_null_arguments(L):
+    d = _desc()
+    assert L.qgemv_create(None, ctypes.byref(d), 8, None) == Q.QG_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert L.qgemv_create(ctypes.byref(h), None, 8, None) == Q.QG_ERR_INVALID_ARG
+    assert L.qgemv_run(None, 0x1000, 1, 0x2000, None) == Q.QG_ERR_INVALID_ARG
+    assert L.qmlp_run(None, None, None, 0x1000, 1, 0x2000, None) == Q.QG_ERR_INVALID_ARG
+    assert L.qgemv_debug_unpack(None, 0x1000, None) == Q.QG_ERR_INVALID_ARG
+    assert L.qgemv_debug_dequant(None, 0x1000, None, None) == Q.QG_ERR_INVALID_ARG
+    assert L.qgemv_debug_trellis(None, 0x1000, None) == Q.QG_ERR_INVALID_ARG
+    assert L.qgemv_set_launch(None, 1, 1, 4, 1) == Q.QG_ERR_INVALID_ARG
+    assert L.qgemv_weight_bytes(None, None) == Q.QG_ERR_INVALID_ARG
+    assert L.qgemv_destroy(None) == Q.QG_OK
+    assert L.qg_last_error() == b""
+
+
+def test_bad_col_bits_rejected_before_device(L):
+    import numpy as np
+    cb = np.full(512, 3, dtype=np.uint8)
+    cb[7] = 5
+    d = _desc(bits=0, col_bits=cb.ctypes.data)
+    h = ctypes.c_void_p()
+    st = L.qgemv_create(ctypes.byref(h), ctypes.byref(d), 8, None)
+    # either the device check (no GPU here) or the width check rejects it; never OK
+    assert st in (Q.QG_ERR_INVALID_ARG, Q.QG_ERR_UNSUPPORTED)
