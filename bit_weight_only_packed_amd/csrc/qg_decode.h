@@ -2,19 +2,23 @@
 // every kernel of the library (run kernels and checking kernels alike).
 //
 // Device layout (written once by the repack kernel at create time).
-//   Columns are grouped in tiles of 16.  For tile t and 128-group g the 64 lanes
-//   of a wave own 64*B consecutive uint32 words: lane l holds column
-//   16*t + (l & 15), quarter q = l >> 4, i.e. the 32 codes c_0..c_31 of that
-//   column at k = 128*g + 32*q + j.  One wave-wide load of B words per lane
-//   therefore reads one contiguous 256*B-byte block (fully coalesced).
-//   Within a lane the codes are stored as 16 pairs (c_{2i}, c_{2i+1}); pair i
+//   Columns are grouped in tiles of 16.  Lane l of a wave owns column
+//   16*t + (l & 15) and quarter q = l >> 4 of each 128-group: the 32 codes
+//   c_0..c_31 at k = 128*g + 32*q + j, stored in B words (see below).  Groups
+//   are bundled by four ("quads", the group count padded to a multiple of 4
+//   with zero codes and zero scales): a lane's quad is 4*B words = B uint4
+//   "parts", group i of the quad being words [i*B, i*B + B).  For tile t and
+//   quad u the 64 lanes' part p is one contiguous 1 KiB block at uint4 index
+//   ((t*G4 + u)*B + p)*64 + l, so every wave-wide load is a full-width
+//   (16 B per lane), fully coalesced 1 KiB read.
+//   Within a group the codes are stored as 16 pairs (c_{2i}, c_{2i+1}); pair i
 //   keeps c_{2i} in the low 16-bit half and c_{2i+1} at the same bit offset in
 //   the high half:
 //     B = 2: word i/8, offset 2*(i%8)         (8 pairs per word)
 //     B = 4: word i/4, offset 4*(i%4)         (4 pairs per word)
 //     B = 3: i < 15: word i/5, offset 3*(i%5) (5 pairs per word, bit 15/31 spare)
 //            i = 15: bit u of c30 is bit 15 of word u, bit u of c31 bit 31 of word u.
-//   Scales: fp16 [tile][g][16].
+//   Scales: fp16 [tile][4*G4][16].
 //
 // Decode.  An fp16 whose bits are an integer v < 2048 has the value v * 2^-24
 // exactly (exponent field 0: subnormal m * 2^-24; exponent field 1:
@@ -103,6 +107,55 @@ __device__ __forceinline__ f4_t mfma16(h8_t a, h8_t b, f4_t c) {
 
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Buffer resource over [base, base + bytes): raw loads outside the range return 0
+// and touch no memory, so a load can be issued unconditionally.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+// B words at byte offset voff + soff of the resource (voff per lane, soff uniform)
+template <int B>
+__device__ __forceinline__ void buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t (&w)[B]) {
+  if constexpr (B == 2) {
+    const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (B == 3) {
+    const u3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z;
+  } else {
+    const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+}
+
+// A lane's quad (4 groups, 4*B words) through a buffer resource whose byte 0 is
+// part 0 of the wave's first quad; `qu` is the quad index relative to it.
+template <int B>
+__device__ __forceinline__ void buffer_quad(__amdgpu_buffer_rsrc_t r, uint32_t lane, int qu, uint32_t (&w)[4 * B]) {
+#pragma unroll
+  for (int p = 0; p < B; ++p) {
+    const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, (uint32_t)(qu * B + p) * 1024u, 0);
+    w[4 * p + 0] = v.x; w[4 * p + 1] = v.y; w[4 * p + 2] = v.z; w[4 * p + 3] = v.w;
+  }
+}
+
+// Group i of a quad as a B-word array
+template <int B>
+__device__ __forceinline__ void quad_group(const uint32_t (&w)[4 * B], int i, uint32_t (&g)[B]) {
+#pragma unroll
+  for (int u = 0; u < B; ++u) g[u] = w[i * B + u];
+}
+
+// Word u of group g of lane `lane` in tile t (plain pointer form; G4 quads per tile)
+__device__ __forceinline__ size_t code_word_index(int t, int G4, int g, int lane, int u, int B) {
+  const int qu = g >> 2, wi = (g & 3) * B + u;  // word within the lane's quad
+  return ((((size_t)t * G4 + qu) * B + (wi >> 2)) * 64 + lane) * 4 + (wi & 3);
+}
 
 template <int B> __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[B]) {
   if constexpr (B == 2) {

@@ -38,7 +38,16 @@ qg_status fail(qg_status st, const char* fmt, ...) {
 
 struct Launch {
   int T = 0, NW = 0, S = 0;  // 0 = built-in choice
+  int NQ = 0;                // M = 1: quads per wave (derived)
 };
+
+// quads-per-wave counts the M = 1 kernel is compiled for
+constexpr int kNQ[] = {1, 2, 3, 4, 5};
+int nq_round_up(int nq) {
+  for (int v : kNQ)
+    if (v >= nq) return v;
+  return 0;
+}
 
 struct HostSeg {
   int bits, tiles, tile0, ncols;
@@ -53,7 +62,7 @@ int mclass(int M) { return M <= 1 ? 0 : (M <= 16 ? 1 : 2); }
 }  // namespace
 
 struct qg_plan {
-  int K = 0, N = 0, G = 0, format = 0, max_M = 0;
+  int K = 0, N = 0, G = 0, G4 = 0, format = 0, max_M = 0;
   uint32_t flags = 0;
   int device = 0;
   std::vector<HostSeg> segs;
@@ -63,6 +72,7 @@ struct qg_plan {
   int64_t weight_bytes = 0;
   float* partial = nullptr;       // device workspace
   size_t partial_floats = 0;
+  int* counters = nullptr;        // device [total_tiles] split-K arrival counters, zero between runs
   uint16_t* hbuf = nullptr;       // device [max_M][N] fp16, MLP intermediate
   Launch over[3];
   // trellis
@@ -74,7 +84,7 @@ struct qg_plan {
 namespace {
 
 // ---- launch planning --------------------------------------------------------
-Launch choose(const qg_plan* h, int M) {
+Launch choose(const qg_plan* h, int M, bool dual = false) {
   Launch L = h->over[mclass(M)];
   const int G = h->G;
   if (h->format == QG_FMT_TRELLIS3) {
@@ -83,33 +93,48 @@ Launch choose(const qg_plan* h, int M) {
     if (L.S <= 0) L.S = 1;
     return L;
   }
+  // waves per workgroup split K; pick the most that keep every workgroup of the
+  // grid resident at once (no second round) and give each wave >= 2 groups
+  auto pick_nw = [&](int tilesets, int budget) {
+    int nw = 8;
+    while (nw > 1 && ((int64_t)tilesets * nw > budget || G / nw < 2)) nw /= 2;
+    return nw;
+  };
   if (M == 1) {
-    if (L.T <= 0) L.T = 1;
-    if (L.NW <= 0) L.NW = 8;
-    if (L.S <= 0) {
-      const int tilesets = (h->total_tiles + L.T - 1) / L.T;
-      int S = std::max(1, 1024 / std::max(1, tilesets));
-      S = std::min(S, std::max(1, G / L.NW));
-      S = std::min(S, 16);
-      L.S = S;
+    // one tile per workgroup; NW waves of NQ quads each split the K slice.  Prefer
+    // the most quads per wave that still gives >= 1500 waves, <= 1/8 dead quads
+    // (fused gate/up: at most 2 quads per wave for register room)
+    L.T = 1;
+    const int G4 = h->G4;
+    if (L.S <= 0) L.S = 1;
+    L.S = std::min(L.S, G4);
+    const int g4s = (G4 + L.S - 1) / L.S;
+    if (L.NW <= 0) {
+      const int nq_max = dual ? 2 : 5;
+      int best_nw = std::min(16, g4s), best_nq = (g4s + best_nw - 1) / best_nw;
+      for (int nq = nq_max; nq >= 1; --nq) {
+        const int nw = (g4s + nq - 1) / nq;
+        if (nw > 16) continue;
+        const int dead = nw * nq - g4s;
+        const int64_t waves = (int64_t)h->total_tiles * L.S * nw;
+        if (dead * 8 > std::max(g4s, 8) || waves < 1500) continue;
+        best_nq = nq;
+        best_nw = nw;
+        break;
+      }
+      L.NW = best_nw;
+      L.NQ = nq_round_up(best_nq);
+    } else {
+      L.NQ = nq_round_up((g4s + L.NW - 1) / L.NW);
     }
+    return L;
   } else {
     if (L.T <= 0) L.T = 2;
-    if (L.NW <= 0) L.NW = 4;
-    if (L.S <= 0) {
-      const int tilesets = (h->total_tiles + L.T - 1) / L.T;
-      int S = std::max(1, 512 / std::max(1, tilesets));
-      S = std::min(S, std::max(1, G / L.NW));
-      S = std::min(S, 8);
-      L.S = S;
-    }
+    const int tilesets = (h->total_tiles + L.T - 1) / L.T;
+    if (L.NW <= 0) L.NW = pick_nw(tilesets, 1800);
+    if (L.S <= 0) L.S = 1;
   }
   L.S = std::min(L.S, G);
-  if (M == 1) {
-    // the K slice of x plus its sums must fit the 64 KiB LDS window: 272 B per group
-    const int min_s = (G + 199) / 200;
-    L.S = std::max(L.S, std::min(min_s, G));
-  }
   return L;
 }
 
@@ -155,6 +180,7 @@ void free_plan(qg_plan* h) {
   }
   if (h->col_map) hipFree(h->col_map);
   if (h->partial) hipFree(h->partial);
+  if (h->counters) hipFree(h->counters);
   if (h->hbuf) hipFree(h->hbuf);
   if (h->tcodes) hipFree(h->tcodes);
   if (h->tscales) hipFree(h->tscales);
@@ -187,7 +213,7 @@ qg_status debug_trellis(const qg_plan*, uint16_t*, float*, hipStream_t) {
 
 // ---- uniform create -----------------------------------------------------------
 qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
-  const int N = d->N, K = d->K, G = K / QG_GROUP;
+  const int N = d->N, K = d->K, G = K / QG_GROUP, G4 = (G + 3) / 4;
   h->col_bits.resize(N);
   if (d->bits == 0) {
     if (!d->col_bits) return fail(QG_ERR_INVALID_ARG, "bits == 0 needs col_bits (host, N entries)");
@@ -233,16 +259,17 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   hipError_t e = hipMemcpyAsync(d_off, row_off.data(), N * sizeof(int64_t), hipMemcpyHostToDevice, st);
   for (auto& s : h->segs) {
     if (e != hipSuccess) break;
-    const size_t nslot = (size_t)s.tiles * G * 64;
-    if (hipMalloc(&s.codes, nslot * s.bits * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc(&s.scales, (size_t)s.tiles * G * 16 * sizeof(uint16_t)) != hipSuccess) {
+    const size_t nslot = (size_t)s.tiles * G4 * 64;
+    if (hipMalloc(&s.codes, nslot * s.bits * 4 * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&s.scales, nslot * sizeof(uint16_t)) != hipSuccess) {
       hipFree(d_off);
       return fail(QG_ERR_OOM, "device allocation for the weight layout failed");
     }
     const int threads = 256;
     const unsigned blocks = (unsigned)((nslot + threads - 1) / threads);
     k_repack_uniform<<<blocks, threads, 0, st>>>((const uint32_t*)d->codes, d_off, d->scales,
-                                                 h->col_map + 16 * s.tile0, s.bits, s.tiles, G, s.codes, s.scales);
+                                                 h->col_map + 16 * s.tile0, s.bits, s.tiles, G, G4, s.codes,
+                                                 s.scales);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -252,41 +279,77 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
 }
 
 // ---- dispatch ------------------------------------------------------------------
-template <int T>
-void launch_m1(const RunArgs& a, int NW, size_t lds, unsigned grid, bool dual, hipStream_t st) {
-  if (dual) k_gemv_m1<T, true><<<grid, NW * 64, lds, st>>>(a);
-  else k_gemv_m1<T, false><<<grid, NW * 64, lds, st>>>(a);
+// BF = the single code width of the handle (kernels compiled for it alone) or 0
+// (per-column widths: the kernel branches per segment).
+template <int NQ, int BF>
+void launch_q_b(const RunArgs& a, int NW, size_t lds, unsigned grid, bool dual, hipStream_t st) {
+  if constexpr (NQ <= 2) {
+    if (dual) {
+      k_gemv_q<NQ, true, BF><<<grid, NW * 64, lds, st>>>(a);
+      return;
+    }
+  }
+  k_gemv_q<NQ, false, BF><<<grid, NW * 64, lds, st>>>(a);
+}
+
+template <int NQ>
+void launch_q(const RunArgs& a, int NW, size_t lds, unsigned grid, bool dual, int bf, hipStream_t st) {
+  switch (bf) {
+    case 2: launch_q_b<NQ, 2>(a, NW, lds, grid, dual, st); break;
+    case 3: launch_q_b<NQ, 3>(a, NW, lds, grid, dual, st); break;
+    case 4: launch_q_b<NQ, 4>(a, NW, lds, grid, dual, st); break;
+    default: launch_q_b<NQ, 0>(a, NW, lds, grid, dual, st); break;
+  }
+}
+
+template <int T, int MT, int BF>
+void launch_mfma_b(const RunArgs& a, int NW, size_t lds, unsigned grid, bool dual, hipStream_t st) {
+  if constexpr (T <= 2) {
+    if (dual) {
+      k_gemm_mfma<T, MT, true, BF><<<grid, NW * 64, lds, st>>>(a);
+      return;
+    }
+  }
+  k_gemm_mfma<T, MT, false, BF><<<grid, NW * 64, lds, st>>>(a);
 }
 
 template <int T, int MT>
-void launch_mfma_t(const RunArgs& a, int NW, size_t lds, unsigned grid, bool dual, hipStream_t st) {
-  if (dual) k_gemm_mfma<T, MT, true><<<grid, NW * 64, lds, st>>>(a);
-  else k_gemm_mfma<T, MT, false><<<grid, NW * 64, lds, st>>>(a);
+void launch_mfma_t(const RunArgs& a, int NW, size_t lds, unsigned grid, bool dual, int bf, hipStream_t st) {
+  switch (bf) {
+    case 2: launch_mfma_b<T, MT, 2>(a, NW, lds, grid, dual, st); break;
+    case 3: launch_mfma_b<T, MT, 3>(a, NW, lds, grid, dual, st); break;
+    case 4: launch_mfma_b<T, MT, 4>(a, NW, lds, grid, dual, st); break;
+    default: launch_mfma_b<T, MT, 0>(a, NW, lds, grid, dual, st); break;
+  }
 }
 
 template <int MT>
-void launch_mfma(const RunArgs& a, int T, int NW, size_t lds, unsigned grid, bool dual, hipStream_t st) {
+void launch_mfma(const RunArgs& a, int T, int NW, size_t lds, unsigned grid, bool dual, int bf, hipStream_t st) {
   switch (T) {
-    case 1: launch_mfma_t<1, MT>(a, NW, lds, grid, dual, st); break;
-    case 2: launch_mfma_t<2, MT>(a, NW, lds, grid, dual, st); break;
-    default: launch_mfma_t<4, MT>(a, NW, lds, grid, dual, st); break;
+    case 1: launch_mfma_t<1, MT>(a, NW, lds, grid, dual, bf, st); break;
+    case 2: launch_mfma_t<2, MT>(a, NW, lds, grid, dual, bf, st); break;
+    default: launch_mfma_t<4, MT>(a, NW, lds, grid, dual, bf, st); break;
   }
 }
 
 // one GEMV/GEMM over a uniform handle (or the fused gate+up pair when h2 != NULL)
 qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, int M, uint16_t* y, int ldy,
                       hipStream_t st) {
-  Launch L = choose(h, M);
+  const bool dual = h2 != nullptr;
+  Launch L = choose(h, M, dual);
   int T = L.T;
-  if (M == 1) T = (T >= 2) ? 2 : 1;
+  if (M == 1) T = 1;
   else T = (T >= 4) ? 4 : (T >= 2 ? 2 : 1);
-  int NW = (L.NW >= 8) ? 8 : 4;
+  int NW = std::max(1, std::min(L.NW, M == 1 ? 16 : 8));
+  if (M > 1) NW = NW >= 8 ? 8 : (NW >= 4 ? 4 : (NW >= 2 ? 2 : 1));
   const int S = L.S;
+  const int bf = h->segs.size() == 1 ? h->segs[0].bits : 0;
+  if (dual && M > 1 && T > 2) T = 2;  // the fused gate/up MFMA pass is built for <= 2 tiles
   if (M > 1) {
     const int MT = M <= 16 ? 1 : 2;
-    while ((h2 ? 2 : 1) * NW * T * MT * 1024 > 65536) {
-      if (NW == 8) NW = 4;
-      else T /= 2;
+    while ((dual ? 2 : 1) * NW * T * MT * 1024 + 16 > 65536) {
+      if (T > 1) T /= 2;
+      else NW /= 2;
     }
   }
   RunArgs a{};
@@ -295,9 +358,11 @@ qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, in
   a.x = x;
   a.y = y;
   a.partial = h->partial;
+  a.counters = h->counters;
   a.M = M;
   a.K = h->K;
   a.G = h->G;
+  a.G4 = h->G4;
   a.ldy = ldy;
   a.NP = 16 * h->total_tiles;
   a.T = T;
@@ -311,30 +376,31 @@ qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, in
   if (S > 1 && partial_need(h, S, M) > h->partial_floats)
     return fail(QG_ERR_INVALID_ARG, "workspace too small for %d K-slices at M=%d", S, M);
   const unsigned grid = (unsigned)pre * (unsigned)S;
-  const bool dual = h2 != nullptr;
   if (M == 1) {
-    const int Gs = (h->G + S - 1) / S + 1;
-    const size_t lds = (size_t)Gs * 256 + (size_t)Gs * 16 + (size_t)2 * NW * T * 16 * sizeof(float);
-    if (T == 2) launch_m1<2>(a, NW, lds, grid, dual, st);
-    else launch_m1<1>(a, NW, lds, grid, dual, st);
+    const int nqs = (h->G4 + S - 1) / S;
+    const int NQ = L.NQ;
+    if (NQ <= 0 || (int64_t)NQ * NW < nqs)
+      return fail(QG_ERR_INVALID_ARG, "%d waves cannot cover %d quads per slice with the compiled quad counts", NW, nqs);
+    if (dual && NQ > 2) return fail(QG_ERR_INVALID_ARG, "fused gate/up needs at most 2 quads per wave");
+    const size_t lds = m1_lds_bytes(nqs, dual ? 2 : 1, NW);
+    if (lds > 65536) return fail(QG_ERR_INVALID_ARG, "K slice of %d quads does not fit LDS: use more splits", nqs);
+    switch (NQ) {
+      case 1: launch_q<1>(a, NW, lds, grid, dual, bf, st); break;
+      case 2: launch_q<2>(a, NW, lds, grid, dual, bf, st); break;
+      case 3: launch_q<3>(a, NW, lds, grid, dual, bf, st); break;
+      case 4: launch_q<4>(a, NW, lds, grid, dual, bf, st); break;
+      case 5: launch_q<5>(a, NW, lds, grid, dual, bf, st); break;
+      default: launch_q<5>(a, NW, lds, grid, dual, bf, st); break;
+    }
   } else {
     const int MT = M <= 16 ? 1 : 2;
-    const size_t lds = (size_t)(dual ? 2 : 1) * NW * T * MT * 4 * 64 * sizeof(float);
+    const size_t lds = (size_t)(dual ? 2 : 1) * NW * T * MT * 4 * 64 * sizeof(float) + 16;
     if (lds > 65536) return fail(QG_ERR_INVALID_ARG, "launch needs %zu B of LDS (max 65536): fewer tiles or waves", lds);
-    if (MT == 1) launch_mfma<1>(a, T, NW, lds, grid, dual, st);
-    else launch_mfma<2>(a, T, NW, lds, grid, dual, st);
+    if (MT == 1) launch_mfma<1>(a, T, NW, lds, grid, dual, bf, st);
+    else launch_mfma<2>(a, T, NW, lds, grid, dual, bf, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
-  if (S > 1) {
-    const int64_t n = (int64_t)M * a.NP;
-    const int threads = 256;
-    const unsigned blocks = (unsigned)((n + threads - 1) / threads);
-    if (dual) k_splitk_reduce<true><<<blocks, threads, 0, st>>>(h->partial, S, M, a.NP, h->col_map, y, ldy);
-    else k_splitk_reduce<false><<<blocks, threads, 0, st>>>(h->partial, S, M, a.NP, h->col_map, y, ldy);
-    e = hipGetLastError();
-    if (e != hipSuccess) return fail(QG_ERR_DEVICE, "reduce launch failed: %s", hipGetErrorString(e));
-  }
   if (getenv("QG_DEBUG_SYNC")) {
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel failed: %s", hipGetErrorString(e));
@@ -375,6 +441,7 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   h->K = d->K;
   h->N = d->N;
   h->G = d->K / QG_GROUP;
+  h->G4 = (h->G + 3) / 4;
   h->format = d->format;
   h->max_M = max_M;
   h->flags = d->flags;
@@ -382,6 +449,12 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   hipStream_t st = (hipStream_t)stream;
   s = d->format == QG_FMT_UNIFORM ? create_uniform(h, d, st) : create_trellis(h, d, st);
   if (s == QG_OK) s = ensure_workspace(h);
+  if (s == QG_OK) {
+    const int nc = std::max(1, h->total_tiles);
+    if (hipMalloc(&h->counters, nc * sizeof(int)) != hipSuccess) s = fail(QG_ERR_OOM, "counter allocation failed");
+    else if (hipMemsetAsync(h->counters, 0, nc * sizeof(int), st) != hipSuccess)
+      s = fail(QG_ERR_DEVICE, "counter initialisation failed");
+  }
   if (s == QG_OK && hipMalloc(&h->hbuf, (size_t)max_M * d->N * sizeof(uint16_t)) != hipSuccess)
     s = fail(QG_ERR_OOM, "staging allocation failed");
   if (s == QG_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(QG_ERR_DEVICE, "stream synchronisation failed");
@@ -410,7 +483,8 @@ qg_status qgemv_set_launch(qg_handle h, int32_t M, int32_t tiles, int32_t waves,
   g_err.clear();
   if (!h) return fail(QG_ERR_INVALID_ARG, "NULL handle");
   if (M < 1 || M > QG_MAX_M) return fail(QG_ERR_INVALID_ARG, "M = %d is not in [1, 32]", M);
-  if (waves > 0 && waves != 4 && waves != 8) return fail(QG_ERR_INVALID_ARG, "waves must be 4 or 8");
+  if (M == 1 ? (waves > 16) : (waves > 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8))
+    return fail(QG_ERR_INVALID_ARG, "waves must be 1..16 for M = 1, else 1, 2, 4 or 8");
   if (splits > 16) return fail(QG_ERR_INVALID_ARG, "splits must be <= 16");
   Launch& L = h->over[mclass(M)];
   L.T = tiles;
@@ -454,7 +528,8 @@ qg_status qgemv_debug_unpack(qg_handle h, int32_t* codes, void* stream) {
   for (const auto& s : h->segs) {
     SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0};
     const int64_t n = (int64_t)s.tiles * h->G * 64;
-    k_debug_uniform<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(sd, h->col_map, h->G, h->K, codes, nullptr, nullptr);
+    k_debug_uniform<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(sd, h->col_map, h->G, h->G4, h->K, codes, nullptr,
+                                                                 nullptr);
   }
   QG_HIP(hipGetLastError());
   return QG_OK;
@@ -468,7 +543,7 @@ qg_status qgemv_debug_dequant(qg_handle h, float* w, uint16_t* q16, void* stream
   for (const auto& s : h->segs) {
     SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0};
     const int64_t n = (int64_t)s.tiles * h->G * 64;
-    k_debug_uniform<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(sd, h->col_map, h->G, h->K, nullptr, w, q16);
+    k_debug_uniform<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(sd, h->col_map, h->G, h->G4, h->K, nullptr, w, q16);
   }
   QG_HIP(hipGetLastError());
   return QG_OK;

@@ -132,7 +132,7 @@ qg_status qgemv_weight_bytes(qg_handle h, int64_t* bytes);
 
 /* Override the launch geometry used for runs with M rows in the class of
  * `M` (M = 1, or any M in 2..16, or any M in 17..32): `tiles` 16-column tiles
- * per workgroup, `waves` waves per workgroup (4 or 8) splitting K, `splits`
+ * per workgroup, `waves` waves per workgroup (1, 2, 4 or 8) splitting K, `splits`
  * K-slices across workgroups (1..16, reduced in a fixed order).  Values <= 0
  * restore the built-in choice.  Used for launch-shape sweeps. */
 qg_status qgemv_set_launch(qg_handle h, int32_t M, int32_t tiles, int32_t waves, int32_t splits);

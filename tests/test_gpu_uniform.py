@@ -88,9 +88,9 @@ def test_mixed_width_parity(M):
 
 
 @pytest.mark.parametrize("M,tiles,waves,splits", [
-    (1, 1, 4, 1), (1, 2, 8, 1), (1, 1, 8, 3), (1, 2, 4, 5), (1, 1, 4, 10),
-    (8, 1, 4, 1), (8, 2, 8, 2), (8, 4, 4, 3), (8, 1, 8, 7),
-    (32, 1, 4, 1), (32, 2, 8, 4), (32, 4, 4, 2), (32, 4, 8, 1),
+    (1, 1, 4, 1), (1, 2, 2, 1), (1, 1, 1, 3), (1, 2, 4, 5), (1, 1, 4, 10), (1, 1, 2, 16), (1, 1, 8, 1), (1, 2, 8, 2),
+    (8, 1, 4, 1), (8, 2, 2, 2), (8, 4, 4, 3), (8, 1, 1, 7), (8, 2, 4, 10), (8, 1, 8, 1),
+    (32, 1, 4, 1), (32, 2, 2, 4), (32, 4, 4, 2), (32, 4, 1, 1), (32, 2, 4, 9), (32, 2, 8, 1),
 ])
 def test_launch_shapes(M, tiles, waves, splits):
     """Every launch geometry gives oracle-matching, repeatable results (ragged
@@ -131,4 +131,6 @@ def test_error_paths_on_device():
     with pytest.raises(Q.QGError):
         u.lin.run(xb)                                 # misaligned x
     with pytest.raises(Q.QGError):
-        u.lin.set_launch(1, 1, 6, 1)                  # waves must be 4 or 8
+        u.lin.set_launch(1, 1, 17, 1)                 # M = 1: at most 16 waves
+    with pytest.raises(Q.QGError):
+        u.lin.set_launch(8, 1, 6, 1)                  # M > 1: 1, 2, 4 or 8 waves
