@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--quick", action="store_true", help="skip the verify/MLP/CPU sections")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--only-layer", action="store_true", help="only the timed layer-set step (for profiling)")
+    p.add_argument("--profile-gate", type=int, default=0, metavar="REPS",
+                   help="profiling mode: REPS graph replays of the M=1 GEMV on the 5120x17408 shape over all "
+                        "weight copies, then a 256 MiB device copy (the counter calibration), then exit")
     return p.parse_args()
 
 
@@ -138,6 +141,29 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3  # s
 
+    if args.profile_gate:
+        # the dominant kernel alone, launched exactly as the per-shape timing below
+        # launches it, then a plain copy of known size for the HBM counter scale
+        out1 = ys[1][:, : shapes[4]["N"]]
+
+        def gate_all():
+            for r in range(R):
+                lins[r][4].run(xk[(1, 5120)], out=out1)
+        g = capture(gate_all)
+        time_graph(g, 2)
+        t = time_graph(g, args.profile_gate)
+        us = t / (args.profile_gate * R) * 1e6
+        n = 64 << 20
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "gemv M=1 5120x17408", "launches": args.profile_gate * R,
+                          "graph_us_per_launch": round(us, 3), "copy_bytes_each_way": 4 * n,
+                          "src_hash": src_hash()}), flush=True)
+        return
+
     # ---------------- the timed step: layer set at M = 1 ----------------
     def all_copies(M=1):
         def f():
@@ -226,7 +252,7 @@ def main():
             tj = json.load(f)
         if tj.get("src_hash") == src_hash():
             traffic = tj.get("bytes_per_launch")
-    result["roofline"] = {"bound": "hbm", "kernel": "qg::k_gemv_m1<1,false> (5120x17408, M=1)",
+    result["roofline"] = {"bound": "hbm", "kernel": "qg::k_gemv_q (M=1 GEMV, 5120x17408, 3-bit)",
                           "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                           "algorithmic_bytes_per_launch": gate_bytes, "avg_launch_us": gate_us,

@@ -101,23 +101,25 @@ Launch choose(const qg_plan* h, int M, bool dual = false) {
     return nw;
   };
   if (M == 1) {
-    // one tile per workgroup; NW waves of NQ quads each split the K slice.  Prefer
-    // the most quads per wave that still gives >= 1500 waves, <= 1/8 dead quads
-    // (fused gate/up: at most 2 quads per wave for register room)
+    // one tile per workgroup; NW waves of NQ quads each split the K slice.  Measured
+    // on the decode shapes: 2 quads per wave is fastest, then 3, then 1 (more quads
+    // per wave lengthen the serial load-to-use chain, fewer add per-wave fixed
+    // cost); take the first of that order that fits in 16 waves with <= 1/8 dead
+    // quads (fused gate/up: at most 2 quads per wave for register room)
     L.T = 1;
     const int G4 = h->G4;
     if (L.S <= 0) L.S = 1;
     L.S = std::min(L.S, G4);
     const int g4s = (G4 + L.S - 1) / L.S;
     if (L.NW <= 0) {
-      const int nq_max = dual ? 2 : 5;
+      static const int order[] = {2, 3, 1, 4, 5};
       int best_nw = std::min(16, g4s), best_nq = (g4s + best_nw - 1) / best_nw;
-      for (int nq = nq_max; nq >= 1; --nq) {
+      for (int nq : order) {
+        if (dual && nq > 2) continue;
         const int nw = (g4s + nq - 1) / nq;
         if (nw > 16) continue;
         const int dead = nw * nq - g4s;
-        const int64_t waves = (int64_t)h->total_tiles * L.S * nw;
-        if (dead * 8 > std::max(g4s, 8) || waves < 1500) continue;
+        if (dead * 8 > std::max(g4s, 8)) continue;
         best_nq = nq;
         best_nw = nw;
         break;
