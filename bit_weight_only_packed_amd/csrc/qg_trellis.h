@@ -1,0 +1,380 @@
+// qg_trellis.h -- bitshift-trellis weights (3 bits/weight, 65536-entry fp16
+// codebook) on gfx950: create-time re-layout, the in-register window decode,
+// the Walsh-Hadamard rotation of x, the M = 1 GEMV (v_dot2_f32_f16), the
+// M = 2..32 GEMM (v_mfma_f32_16x16x32_f16) and the checking kernel.
+//
+// Format (trellis family of "OrcaSAQ2-27B on AMD Radeon -- ROCm runtime", intro:
+// EXL3 trellis weights near 3 bits/weight): a 16x16 tile (16 output rows n x 16
+// input columns k) is a 768-bit stream, 48 uint16 words taken MSB first.
+// Weight i = 16*r + c of the tile takes the 16-bit window of the stream that
+// starts at bit 3*i, read cyclically (the windows of the last weights wrap to
+// the start of the tile's stream), as an unsigned index into the codebook;
+// w = codebook[state] * s[n][k/128].  Before the product x is rotated by the
+// normalised 128-point Walsh-Hadamard transform of each 128-group (natural
+// order, factor 2^-3.5).
+//
+// Device layout.  Row block rb = 16 rows; unit (rb, g) = the 8 tiles of group g
+// (16 rows x 128 k).  Lane l of a wave owns row n = l & 15 and quarter
+// kq = l >> 4 of the group: k = 128g + 32kq + j, j = 0..31, which is row n of
+// the two tiles A = 8g + 2kq (j < 16) and B = A + 1 (j >= 16).  The lane's three
+// words hold those two 48-bit rows back to back, MSB first:
+//   Z2 = A[3n] << 16 | A[3n+1],  Z1 = A[3n+2] << 16 | B[3n],  Z0 = B[3n+1] << 16 | B[3n+2]
+// at uint32 index (unit * 64 + l) * 3, so one wave-wide 12-byte-per-lane load
+// reads a unit's 768 contiguous bytes once.  The 15 bits of look-ahead that the
+// last windows of a row need are the first bits of the next row of the same
+// tile (row 0 after row 15), which the lane of row n + 1 mod 16 in the same
+// quarter holds: two cross-lane reads per unit.  Scales: fp16 [unit][16].
+//
+// Decode.  With a row as a 64-bit value R (row bits at 63..16, the next row's
+// first 16 bits at 15..0), 2 * state_c = (R >> (47 - 3c)) & 0x1FFFE: one funnel
+// shift (v_alignbit_b32) and one AND give the byte address of the codebook
+// entry in LDS, whose fp16 value is used as is (exact); the scale multiplies
+// each group's fp32 partial sum.
+#pragma once
+#include "qg_kernels.h"
+
+namespace qg {
+
+constexpr int TR_CB_BYTES = 65536 * 2;   // codebook in LDS
+
+// ---------------------------------------------------------------------------
+// create-time re-layout (one thread per unit and lane)
+// ---------------------------------------------------------------------------
+__global__ void k_repack_trellis(const uint16_t* __restrict__ tiles, const uint16_t* __restrict__ scales_in, int KT,
+                                 int G, int64_t units, uint32_t* __restrict__ dcodes, uint16_t* __restrict__ dscales) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= units * 64) return;
+  const int lane = (int)(gid & 63);
+  const int64_t u = gid >> 6;
+  const int rb = (int)(u / G), g = (int)(u % G);
+  const int n = lane & 15, kq = lane >> 4;
+  const uint16_t* A = tiles + ((int64_t)rb * KT + 8 * g + 2 * kq) * 48 + 3 * n;
+  const uint16_t* Bt = A + 48;
+  uint32_t* o = dcodes + gid * 3;
+  o[0] = ((uint32_t)A[0] << 16) | A[1];
+  o[1] = ((uint32_t)A[2] << 16) | Bt[0];
+  o[2] = ((uint32_t)Bt[1] << 16) | Bt[2];
+  if (kq == 0) dscales[u * 16 + n] = scales_in[((int64_t)rb * 16 + n) * G + g];
+}
+
+// ---------------------------------------------------------------------------
+// decode: codebook byte addresses of the lane's 32 weights (k = 32kq + j)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t tr_nbr_lane(int lane) { return (uint32_t)((lane & ~15) | ((lane + 1) & 15)); }
+
+// addr[j] = 2 * state of weight j; z = the lane's words, nz2 / nz1 = Z2 / Z1 of
+// the lane holding row n + 1 mod 16 of the same tiles
+__device__ __forceinline__ void tr_addrs(uint32_t z2, uint32_t z1, uint32_t z0, uint32_t nz2, uint32_t nz1,
+                                         uint32_t (&addr)[32]) {
+  // row A as (hi, lo) = (Z2, Z1.hi16 : next row's first 16 bits)
+  const uint32_t la = __builtin_amdgcn_perm(z1, nz2, 0x07060302u);  // bytes z1[3:2], nz2[3:2]
+  // row B as (hb, lb) = (Z1.lo16 : Z0.hi16, Z0.lo16 : next row's first 16 bits)
+  const uint32_t hb = __builtin_amdgcn_perm(z1, z0, 0x05040302u);   // bytes z1[1:0], z0[3:2]
+  const uint32_t lb = __builtin_amdgcn_perm(z0, nz1, 0x05040100u);  // bytes z0[1:0], nz1[1:0]
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int s = 47 - 3 * c;
+    uint32_t va, vb;
+    if (s >= 32) {
+      va = z2 >> (s - 32);
+      vb = hb >> (s - 32);
+    } else {
+      va = __builtin_amdgcn_alignbit(z2, la, s);
+      vb = __builtin_amdgcn_alignbit(hb, lb, s);
+    }
+    addr[c] = va & 0x1FFFEu;
+    addr[16 + c] = vb & 0x1FFFEu;
+  }
+}
+
+__device__ __forceinline__ _Float16 cb_at(const char* cbl, uint32_t a) {
+  return *reinterpret_cast<const _Float16*>(cbl + a);
+}
+
+// the lane's 32 codebook values as 16 fp16 pairs (weights 2p, 2p+1 in pair p)
+__device__ __forceinline__ void tr_gather(const char* cbl, const uint32_t (&addr)[32], uint32_t (&pr)[16]) {
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    h2_t v;
+    v.x = cb_at(cbl, addr[2 * p]);
+    v.y = cb_at(cbl, addr[2 * p + 1]);
+    pr[p] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rotation: x'[m][128g + j] = 2^-3.5 * sum_i (-1)^popcount(i & j) x[m][128g + i]
+// One wave per (row, group); lane l holds elements l and l + 64.  Butterflies in
+// fp32 (the sums of 128 fp16 values with signs are exact to fp32 rounding), one
+// rounding to fp16 at the end.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_fwht(const uint16_t* __restrict__ x, uint16_t* __restrict__ xr, int M,
+                                              int K) {
+  const int G = K / 128;
+  const int wv = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  if (wv >= M * G) return;
+  const int lane = threadIdx.x & 63;
+  const int m = wv / G, g = wv % G;
+  const uint16_t* p = x + (size_t)m * K + (size_t)g * 128;
+  float a = h2f(p[lane]), b = h2f(p[lane + 64]);
+  {
+    const float s = a + b, d = a - b;
+    a = s;
+    b = d;
+  }
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    const float pa = __shfl_xor(a, h), pb = __shfl_xor(b, h);
+    const bool upper = (lane & h) != 0;
+    a = upper ? pa - a : a + pa;
+    b = upper ? pb - b : b + pb;
+  }
+  const float f = 0.08838834764831845f;  // 2^-3.5
+  uint16_t* q = xr + (size_t)m * K + (size_t)g * 128;
+  q[lane] = f2h(a * f);
+  q[lane + 64] = f2h(b * f);
+}
+
+// ---------------------------------------------------------------------------
+// GEMV (MT = 0, M = 1) and GEMM (MT = 1: M <= 16, MT = 2: M <= 32).
+//
+// One workgroup per compute unit holds the codebook in LDS for the whole launch.
+// The RB * G units are split into W equal contiguous ranges in row-block-major
+// order, one per wave (stream-K): a wave walks its range with the next two
+// units' loads in flight (three register sets in rotation), accumulates while
+// the row block stays the same and leaves a partial sum per row block it
+// touches.  A row block's partials sit
+// in fixed slots (slot = wave - first wave of the row block); the wave that
+// completes a row block (device-scope arrival counter) adds the slots in slot
+// order and stores the fp16 result.  The slot order fixes every rounding, so
+// repeated runs are bit-identical.
+// ---------------------------------------------------------------------------
+struct TrArgs {
+  const uint32_t* codes;   // [U][64][3]
+  const uint16_t* scales;  // [U][16]
+  const uint16_t* cb;      // [65536] fp16
+  const uint16_t* x;       // [M][K] fp16, rotated
+  uint16_t* y;             // [M][N] fp16
+  float* partial;          // [RB][maxseg][M][16]
+  int* counters;           // [RB], zero between launches
+  int M, K, N, G, RB, maxseg, W;
+  int64_t U;
+};
+
+// first wave whose range holds unit x (ranges [w*U/W, (w+1)*U/W))
+__device__ __forceinline__ int tr_wave_of(int64_t x, int64_t U, int W) {
+  int w = (int)(x * W / U);
+  while (w + 1 < W && ((int64_t)(w + 1) * U) / W <= x) ++w;
+  while (w > 0 && ((int64_t)w * U) / W > x) --w;
+  return w;
+}
+
+template <int MT>
+struct TrUnit {
+  static constexpr int XR = MT == 0 ? 1 : MT;  // activation row blocks held
+  u3_t z;                                      // code words
+  uint32_t s;                                  // this lane's scale (fp16 in the low half)
+  uint4 xv[XR][4];                             // activations: 32 k of row (16*mt + (lane & 15)), or of row 0 (M = 1)
+};
+
+template <int MT>
+__device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT>& t, int64_t u, bool live, int lane) {
+  const int uu = live ? 1 : 0;
+  const int64_t uc = live ? u : 0;
+  const int g = (int)(uc % a.G);
+  const int kq = lane >> 4;
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes + uc * 192, uu * 768u);
+  t.z = __builtin_amdgcn_raw_buffer_load_b96(rc, (uint32_t)lane * 12u, 0, 0);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + uc * 16, uu * 32u);
+  t.s = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(lane & 14) * 2u, 0, 0);
+  if (lane & 1) t.s >>= 16;
+#pragma unroll
+  for (int mt = 0; mt < TrUnit<MT>::XR; ++mt) {
+    const int m = MT == 0 ? 0 : 16 * mt + (lane & 15);
+    const bool ok = live && m < a.M;
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(a.x + (size_t)(ok ? m : 0) * a.K + (size_t)g * 128 + 32 * kq, ok ? 64u : 0u);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u4_t q = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)v * 16u, 0, 0);
+      t.xv[mt][v] = make_uint4(q.x, q.y, q.z, q.w);
+    }
+  }
+}
+
+// A wave's partials reach device scope before it counts its arrival at the
+// row block's counter; the wave that arrives last re-arms the counter and then
+// sees every other wave's partials.
+__device__ __forceinline__ bool tr_arrive_last(int* counter, int nseg, int lane) {
+  __threadfence();  // release: this wave's partials
+  int old = 0;
+  if (lane == 0) old = atomicAdd(counter, 1);
+  old = __shfl(old, 0);
+  if (old != nseg - 1) return false;
+  if (lane == 0) *counter = 0;
+  __threadfence();  // acquire: the other waves' partials
+  return true;
+}
+
+template <int MT>
+__global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
+  // static (not dynamic) LDS: its address is a compile-time constant, so the
+  // gathers use the decoded byte address as is
+  __shared__ __align__(16) char smem[TR_CB_BYTES];
+  constexpr int XR = TrUnit<MT>::XR;
+  const int lane = threadIdx.x & 63;
+  const int NW = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * NW + wave;
+  const int64_t lo = (int64_t)gw * a.U / a.W, hi = (int64_t)(gw + 1) * a.U / a.W;
+  TrUnit<MT> c0, c1, c2;
+  tr_load<MT>(a, c0, lo, lo < hi, lane);
+  tr_load<MT>(a, c1, lo + 1, lo + 1 < hi, lane);
+  tr_load<MT>(a, c2, lo + 2, lo + 2 < hi, lane);
+  // codebook -> LDS (every wave stays to the barrier)
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.cb);
+    uint4* dst = reinterpret_cast<uint4*>(smem);
+    for (int i = threadIdx.x; i < TR_CB_BYTES / 16; i += blockDim.x) dst[i] = src[i];
+  }
+  __syncthreads();
+  if (lo >= hi) return;
+  const char* cbl = smem;
+  const uint32_t nbr = tr_nbr_lane(lane);
+  float acc1 = 0.0f;
+  f4_t acc[XR];
+#pragma unroll
+  for (int mt = 0; mt < XR; ++mt) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  int rb = (int)(lo / a.G);
+  // one unit: decode, contract, reload the same registers with unit u + 3, and
+  // flush at the end of a row block or of the range
+  auto step = [&](TrUnit<MT>& cu, int64_t u) {
+    const uint32_t z2 = cu.z.x, z1 = cu.z.y, z0 = cu.z.z;
+    const uint32_t nz2 = (uint32_t)__shfl((int)z2, (int)nbr), nz1 = (uint32_t)__shfl((int)z1, (int)nbr);
+    uint32_t addr[32];
+    tr_addrs(z2, z1, z0, nz2, nz1, addr);
+    uint32_t pr[16];
+    tr_gather(cbl, addr, pr);
+    const float s = h2f((uint16_t)(cu.s & 0xFFFFu));
+    if constexpr (MT == 0) {
+      float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        d0 = dot2(pr[4 * v + 0], cu.xv[0][v].x, d0);
+        d1 = dot2(pr[4 * v + 1], cu.xv[0][v].y, d1);
+        d0 = dot2(pr[4 * v + 2], cu.xv[0][v].z, d0);
+        d1 = dot2(pr[4 * v + 3], cu.xv[0][v].w, d1);
+      }
+      acc1 = __builtin_fmaf(s, d0 + d1, acc1);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < XR; ++mt) {
+        f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          cg = mfma16(__builtin_bit_cast(h8_t, cu.xv[mt][v]), as_h8(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]),
+                      cg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(s, cg[e], acc[mt][e]);
+      }
+    }
+    tr_load<MT>(a, cu, u + 3, u + 3 < hi, lane);
+    const bool last_unit = u + 1 == hi;
+    const int rb_next = (int)((u + 1) / a.G);
+    if (!last_unit && rb_next == rb) return;
+    const int w0 = tr_wave_of((int64_t)rb * a.G, a.U, a.W);
+    const int w1 = tr_wave_of((int64_t)rb * a.G + a.G - 1, a.U, a.W);
+    const int nseg = w1 - w0 + 1, seg = gw - w0;
+    const int n = lane & 15;
+    float* base = a.partial + ((size_t)rb * a.maxseg) * a.M * 16;
+    if constexpr (MT == 0) {
+      float v = acc1;
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (nseg == 1) {
+        if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(v);
+      } else {
+        if (lane < 16) base[(size_t)seg * 16 + n] = v;
+        if (tr_arrive_last(a.counters + rb, nseg, lane)) {
+          float t = 0.0f;
+          for (int k = 0; k < nseg; ++k) t += (k == seg) ? v : base[(size_t)k * 16 + n];
+          if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(t);
+        }
+      }
+      acc1 = 0.0f;
+    } else {
+      const int mq = lane >> 4;
+      if (nseg == 1) {
+#pragma unroll
+        for (int mt = 0; mt < XR; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = 16 * mt + 4 * mq + e;
+            if (m < a.M) a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(acc[mt][e]);
+          }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < XR; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = 16 * mt + 4 * mq + e;
+            if (m < a.M) base[((size_t)seg * a.M + m) * 16 + n] = acc[mt][e];
+          }
+        if (tr_arrive_last(a.counters + rb, nseg, lane)) {
+#pragma unroll
+          for (int mt = 0; mt < XR; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int m = 16 * mt + 4 * mq + e;
+              if (m >= a.M) continue;
+              float t = 0.0f;
+              for (int k = 0; k < nseg; ++k)
+                t += (k == seg) ? acc[mt][e] : base[((size_t)k * a.M + m) * 16 + n];
+              a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(t);
+            }
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < XR; ++mt) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    rb = rb_next;
+  };
+  for (int64_t u = lo; u < hi; u += 3) {
+    step(c0, u);
+    if (u + 1 >= hi) break;
+    step(c1, u + 1);
+    if (u + 2 >= hi) break;
+    step(c2, u + 2);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// checking kernel: states (and cb[state] * s in fp32) of every weight, through
+// the same decode as the run kernels.  One wave per unit.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_debug_trellis(const uint32_t* __restrict__ codes,
+                                                       const uint16_t* __restrict__ scales,
+                                                       const uint16_t* __restrict__ cb, int K, int G, int64_t U,
+                                                       uint16_t* states, float* w) {
+  const int64_t u = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (u >= U) return;  // whole waves leave together (blockDim is a multiple of 64)
+  const int lane = threadIdx.x & 63;
+  const int rb = (int)(u / G), g = (int)(u % G);
+  const uint32_t* zp = codes + (u * 64 + lane) * 3;
+  const uint32_t z2 = zp[0], z1 = zp[1], z0 = zp[2];
+  const uint32_t nbr = tr_nbr_lane(lane);
+  const uint32_t nz2 = (uint32_t)__shfl((int)z2, (int)nbr), nz1 = (uint32_t)__shfl((int)z1, (int)nbr);
+  uint32_t addr[32];
+  tr_addrs(z2, z1, z0, nz2, nz1, addr);
+  const int n = rb * 16 + (lane & 15);
+  const int kq = lane >> 4;
+  const float s = h2f(scales[u * 16 + (lane & 15)]);
+  for (int j = 0; j < 32; ++j) {
+    const size_t at = (size_t)n * K + (size_t)g * 128 + 32 * kq + j;
+    const uint32_t st = addr[j] >> 1;
+    if (states) states[at] = (uint16_t)st;
+    if (w) w[at] = h2f(cb[st]) * s;  // exact: fp16 x fp16 fits fp32
+  }
+}
+
+}  // namespace qg

@@ -13,6 +13,7 @@
 
 #include "../../include/qgemv.h"
 #include "qg_kernels.h"
+#include "qg_trellis.h"
 
 using namespace qg;
 
@@ -79,6 +80,9 @@ struct qg_plan {
   uint32_t* tcodes = nullptr;     // device layout of trellis tiles
   uint16_t* tscales = nullptr;    // [N/16 tiles][G][16]
   uint16_t* codebook = nullptr;   // device copy, 65536 fp16
+  uint16_t* xrot = nullptr;       // device [max_M][K] fp16, rotated activations
+  int64_t tr_units = 0;           // (N/16) * G
+  int tr_grid = 0, tr_nw = 0, tr_maxseg = 0;
 };
 
 namespace {
@@ -187,6 +191,7 @@ void free_plan(qg_plan* h) {
   if (h->tcodes) hipFree(h->tcodes);
   if (h->tscales) hipFree(h->tscales);
   if (h->codebook) hipFree(h->codebook);
+  if (h->xrot) hipFree(h->xrot);
   delete h;
 }
 
@@ -202,15 +207,98 @@ WSet wset_of(const qg_plan* h) {
 }
 
 
-// ---- trellis (filled in by the trellis kernels) ----------------------------------
-qg_status create_trellis(qg_plan*, const qg_weight_desc*, hipStream_t) {
-  return fail(QG_ERR_UNSUPPORTED, "trellis format not built yet");
+// ---- trellis ---------------------------------------------------------------------
+// stream-K plan: W = grid * NW waves share the U = (N/16) * G units; maxseg is
+// the largest number of waves any row block is split over (the device kernel
+// finds the same first and last wave of a row block with tr_wave_of)
+int tr_wave_of_host(int64_t x, int64_t U, int W) {
+  int w = (int)(x * W / U);
+  while (w + 1 < W && ((int64_t)(w + 1) * U) / W <= x) ++w;
+  while (w > 0 && ((int64_t)w * U) / W > x) --w;
+  return w;
 }
-qg_status run_trellis(const qg_plan*, const uint16_t*, int, uint16_t*, hipStream_t) {
-  return fail(QG_ERR_UNSUPPORTED, "trellis format not built yet");
+
+int tr_maxseg_of(int RB, int G, int64_t U, int W) {
+  int mx = 1;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int w0 = tr_wave_of_host((int64_t)rb * G, U, W);
+    const int w1 = tr_wave_of_host((int64_t)rb * G + G - 1, U, W);
+    mx = std::max(mx, w1 - w0 + 1);
+  }
+  return mx;
 }
-qg_status debug_trellis(const qg_plan*, uint16_t*, float*, hipStream_t) {
-  return fail(QG_ERR_UNSUPPORTED, "trellis format not built yet");
+
+qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
+  const int N = d->N, K = d->K, G = K / QG_GROUP, RB = N / 16;
+  int cus = 0;
+  QG_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device));
+  h->total_tiles = RB;
+  h->tr_units = (int64_t)RB * G;
+  h->weight_bytes = (int64_t)N * K * 3 / 8 + (int64_t)N * G * 2;
+  // one workgroup per compute unit, 8 waves, at least 2 units per wave
+  h->tr_nw = 8;
+  h->tr_grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (h->tr_units + 2 * h->tr_nw - 1) / (2 * h->tr_nw)));
+  const int W = h->tr_grid * h->tr_nw;
+  h->tr_maxseg = tr_maxseg_of(RB, G, h->tr_units, W);
+  const size_t ncode = (size_t)h->tr_units * 64 * 3;
+  QG_HIP(hipMalloc(&h->tcodes, ncode * sizeof(uint32_t)));
+  QG_HIP(hipMalloc(&h->tscales, (size_t)h->tr_units * 16 * sizeof(uint16_t)));
+  QG_HIP(hipMalloc(&h->codebook, 65536 * sizeof(uint16_t)));
+  if (!(d->flags & QG_FLAG_X_PREROTATED)) QG_HIP(hipMalloc(&h->xrot, (size_t)h->max_M * K * sizeof(uint16_t)));
+  const size_t nf = (size_t)RB * h->tr_maxseg * h->max_M * 16;
+  QG_HIP(hipMalloc(&h->partial, nf * sizeof(float)));
+  h->partial_floats = nf;
+  QG_HIP(hipMemcpyAsync(h->codebook, d->codebook, 65536 * sizeof(uint16_t), hipMemcpyDeviceToDevice, st));
+  const int64_t threads = h->tr_units * 64;
+  k_repack_trellis<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>((const uint16_t*)d->codes, d->scales, K / 16, G,
+                                                                      h->tr_units, h->tcodes, h->tscales);
+  QG_HIP(hipGetLastError());
+  QG_HIP(hipStreamSynchronize(st));
+  return QG_OK;
+}
+
+qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, hipStream_t st) {
+  const uint16_t* xr = x;
+  if (!(h->flags & QG_FLAG_X_PREROTATED)) {
+    const int waves = M * h->G;
+    k_fwht<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, h->xrot, M, h->K);
+    xr = h->xrot;
+  }
+  TrArgs a{};
+  a.codes = h->tcodes;
+  a.scales = h->tscales;
+  a.cb = h->codebook;
+  a.x = xr;
+  a.y = y;
+  a.partial = h->partial;
+  a.counters = h->counters;
+  a.M = M;
+  a.K = h->K;
+  a.N = h->N;
+  a.G = h->G;
+  a.RB = h->N / 16;
+  a.maxseg = h->tr_maxseg;
+  a.W = h->tr_grid * h->tr_nw;
+  a.U = h->tr_units;
+  const dim3 grid((unsigned)h->tr_grid), block((unsigned)(64 * h->tr_nw));
+  if (M == 1) k_trellis<0><<<grid, block, 0, st>>>(a);
+  else if (M <= 16) k_trellis<1><<<grid, block, 0, st>>>(a);
+  else k_trellis<2><<<grid, block, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  if (getenv("QG_DEBUG_SYNC")) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel failed: %s", hipGetErrorString(e));
+  }
+  return QG_OK;
+}
+
+qg_status debug_trellis(const qg_plan* h, uint16_t* states, float* w, hipStream_t st) {
+  const int64_t threads = h->tr_units * 64;
+  k_debug_trellis<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(h->tcodes, h->tscales, h->codebook, h->K, h->G,
+                                                                     h->tr_units, states, w);
+  QG_HIP(hipGetLastError());
+  return QG_OK;
 }
 
 // ---- uniform create -----------------------------------------------------------
@@ -450,7 +538,7 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   h->device = dev;
   hipStream_t st = (hipStream_t)stream;
   s = d->format == QG_FMT_UNIFORM ? create_uniform(h, d, st) : create_trellis(h, d, st);
-  if (s == QG_OK) s = ensure_workspace(h);
+  if (s == QG_OK && h->format == QG_FMT_UNIFORM) s = ensure_workspace(h);
   if (s == QG_OK) {
     const int nc = std::max(1, h->total_tiles);
     if (hipMalloc(&h->counters, nc * sizeof(int)) != hipSuccess) s = fail(QG_ERR_OOM, "counter allocation failed");
@@ -484,6 +572,7 @@ qg_status qgemv_weight_bytes(qg_handle h, int64_t* bytes) {
 qg_status qgemv_set_launch(qg_handle h, int32_t M, int32_t tiles, int32_t waves, int32_t splits) {
   g_err.clear();
   if (!h) return fail(QG_ERR_INVALID_ARG, "NULL handle");
+  if (h->format != QG_FMT_UNIFORM) return fail(QG_ERR_INVALID_ARG, "launch overrides apply to uniform-code handles");
   if (M < 1 || M > QG_MAX_M) return fail(QG_ERR_INVALID_ARG, "M = %d is not in [1, 32]", M);
   if (M == 1 ? (waves > 16) : (waves > 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8))
     return fail(QG_ERR_INVALID_ARG, "waves must be 1..16 for M = 1, else 1, 2, 4 or 8");

@@ -199,6 +199,21 @@ def gemv_trellis(x, words16, codebook, scales, N: int, K: int, prerotated: bool 
     return matmul(xr, w)
 
 
+def gemv_trellis_rows(x, words16, codebook, scales, N: int, K: int, rows, prerotated: bool = False) -> np.ndarray:
+    """Same as :func:`gemv_trellis` restricted to output rows ``rows`` (spot
+    checks of large shapes: only the 16-row tile rows holding them are
+    decoded).  Returns [M][len(rows)]."""
+    rows = np.asarray(rows)
+    xr = np.asarray(x, dtype=np.float64) if prerotated else rotate(x)
+    tiles = np.asarray(words16, dtype=np.uint16).reshape(N // 16, K // 16, 48)
+    blocks = np.unique(rows // 16)
+    st = trellis_states(tiles[blocks].reshape(-1), 16 * len(blocks), K)       # [16*nb][K]
+    pos = {int(b): i for i, b in enumerate(blocks)}
+    sel = np.array([16 * pos[int(n) // 16] + int(n) % 16 for n in rows])
+    s = np.asarray(scales).reshape(N, K // GROUP)[rows]
+    return matmul(xr, trellis_dequant(st[sel], codebook, s))
+
+
 def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 

@@ -1,0 +1,113 @@
+"""GPU parity of the bitshift-trellis path (3 bits/weight, 65536-entry fp16
+codebook, Walsh-Hadamard-rotated activations) against the CPU oracle, through
+the C ABI: bit-exact states and dequantised weights from the checking entry
+points, outputs within the normwise 2e-3 budget at M = 1 (vector-ALU GEMV)
+and M = 2..32 (matrix-core GEMM), pre-rotated input, bit-identical repeats and
+sampled columns of the 27B-class shapes."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle as O  # noqa: E402
+import qg_synth as S  # noqa: E402
+from _gpu import TOL, dev_f16, dev_u16, say, sha  # noqa: E402
+import bit_weight_only_packed_amd as Q  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_present():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def codebook():
+    cb = S.codebook(cfg_id=S.CFG_TRELLIS)
+    return cb, dev_f16(cb)
+
+
+class Trellis:
+    def __init__(self, N, K, cb, cfg_id=80, max_M=32, prerotated=False):
+        self.N, self.K = N, K
+        self.words = S.trellis_words(N, K, cfg_id=cfg_id)
+        self.scales = S.scales(N, K, cfg_id=cfg_id)
+        self.cb = cb[0]
+        self.dw = dev_u16(self.words)
+        self.ds = dev_f16(self.scales)
+        self.lin = Q.QLinear(self.dw, self.ds, K, N, trellis=True, codebook=cb[1], max_M=max_M,
+                             prerotated=prerotated)
+
+    def ref(self, x, prerotated=False):
+        return O.gemv_trellis(x, self.words, self.cb, self.scales, self.N, self.K, prerotated=prerotated)
+
+
+def _run(lin, x):
+    y = lin.run(dev_f16(x))
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (160, 1280)])
+def test_states_and_dequant_bit_exact(N, K, codebook):
+    say("trellis exact", N, K)
+    t = Trellis(N, K, codebook)
+    st = t.lin.debug_trellis().cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(st, O.trellis_states(t.words, N, K))
+    w, _ = t.lin.debug_dequant(with_q16=False)
+    ref = O.trellis_dequant(O.trellis_states(t.words, N, K), t.cb, t.scales)
+    np.testing.assert_array_equal(w.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 8, 16, 17, 32])
+@pytest.mark.parametrize("N,K", [(16, 128), (96, 640), (272, 1536), (512, 512)])
+def test_product_parity(M, N, K, codebook):
+    say("trellis product", M, N, K)
+    t = Trellis(N, K, codebook, cfg_id=81)
+    x = S.activations(M, K, cfg_id=81, tensor_id=200 + M)
+    y = _run(t.lin, x)
+    err = O.normwise_rel_err(y, t.ref(x))
+    say("trellis err", err)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_prerotated_input(M, codebook):
+    say("trellis prerotated", M)
+    N, K = 128, 1024
+    t = Trellis(N, K, codebook, cfg_id=82, prerotated=True)
+    xr = O.rotate(S.activations(M, K, cfg_id=82)).astype(np.float16)
+    y = _run(t.lin, xr)
+    err = O.normwise_rel_err(y, t.ref(xr, prerotated=True))
+    say("prerotated err", err)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_repeat_bit_identical(M, codebook):
+    say("trellis repeat", M)
+    t = Trellis(320, 2560, codebook, cfg_id=83)
+    x = dev_f16(S.activations(M, 2560, cfg_id=83))
+    h0 = sha(t.lin.run(x))
+    for _ in range(10):
+        assert sha(t.lin.run(x)) == h0
+
+
+@pytest.mark.parametrize("K,N", [(5120, 5120), (5120, 1024), (5120, 17408), (17408, 5120)])
+@pytest.mark.parametrize("M", [1, 8])
+def test_full_size_sampled_columns(K, N, M, codebook):
+    say("trellis full size", K, N, M)
+    t = Trellis(N, K, codebook, cfg_id=S.CFG_TRELLIS, max_M=8)
+    x = S.activations(M, K, cfg_id=S.CFG_TRELLIS, tensor_id=S.T_X + M)
+    y = _run(t.lin, x)
+    # whole 16-row tile rows: the first, the last and six random ones
+    blocks = np.unique(np.concatenate([[0, N // 16 - 1], np.random.default_rng(7).choice(N // 16, 6, replace=False)]))
+    rows = (16 * blocks[:, None] + np.arange(16)[None, :]).reshape(-1)
+    r = O.gemv_trellis_rows(x, t.words, t.cb, t.scales, N, K, rows)
+    err = O.normwise_rel_err(y[:, rows], r)
+    say("full size err", err)
+    assert err <= TOL, err
+    assert np.isfinite(y).all()

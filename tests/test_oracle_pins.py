@@ -427,3 +427,15 @@ def test_normwise_error_metric():
     r = np.array([[1.0, -4.0, 2.0]])
     y = np.array([[1.0, -4.002, 2.001]])
     assert abs(O.normwise_rel_err(y, r) - 0.002 / 4.0) < 1e-15
+
+
+def test_trellis_row_subset_is_a_restriction():
+    """The spot-check helper equals the full trellis product on the chosen rows."""
+    N, K = 64, 256
+    w = S.trellis_words(N, K, cfg_id=3)
+    cb = S.codebook(cfg_id=3)
+    sc = S.scales(N, K, cfg_id=3)
+    x = S.activations(2, K, cfg_id=3)
+    full = O.gemv_trellis(x, w, cb, sc, N, K)
+    rows = np.array([0, 5, 17, 40, 63])
+    np.testing.assert_allclose(O.gemv_trellis_rows(x, w, cb, sc, N, K, rows), full[:, rows], rtol=1e-12, atol=1e-12)
