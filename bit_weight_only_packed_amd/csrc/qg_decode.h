@@ -18,7 +18,7 @@
 //     B = 4: word i/4, offset 4*(i%4)         (4 pairs per word)
 //     B = 3: i < 15: word i/5, offset 3*(i%5) (5 pairs per word, bit 15/31 spare)
 //            i = 15: bit u of c30 is bit 15 of word u, bit u of c31 bit 31 of word u.
-//   Scales: fp16 [tile][4*G4][16].
+//   Scales: fp16 [tile][G4][16][4]: per quad, column, then group within the quad.
 //
 // Decode.  An fp16 whose bits are an integer v < 2048 has the value v * 2^-24
 // exactly (exponent field 0: subnormal m * 2^-24; exponent field 1:
@@ -27,9 +27,10 @@
 // (c_lo * 2^(p-24), c_hi * 2^(p-24)) -- exact, no conversion instruction.
 // gfx950's v_dot2_f32_f16 and v_mfma_f32_16x16x32_f16 consume such subnormal
 // fp16 operands exactly.  Codes at offsets beyond the exact range are first
-// shifted down.  The GEMV keeps one fp32 accumulator per offset ("class") and
-// rescales them per group; the MFMA path shifts every pair to offset 1 so a
-// whole operand shares one scale.
+// shifted down.  The M = 1 GEMVs scale each x by 2^-class of the code position
+// it meets (or, in the per-group-staged GEMV, keep one fp32 accumulator per
+// offset "class" and rescale them per group); the MFMA path shifts every pair to
+// offset 1 so a whole operand shares one scale.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,8 +45,10 @@ template <int B> struct Pair {
   // word holding pair i, its bit offset, and (GEMV) the shift applied before masking
   static constexpr int word(int i) { return B == 2 ? i / 8 : B == 4 ? i / 4 : (i < 15 ? i / 5 : 0); }
   static constexpr int off(int i) { return B == 2 ? 2 * (i % 8) : B == 4 ? 4 * (i % 4) : 3 * (i % 5); }
+  // (3-bit: word u is shifted by 9 - u, which also lines its spare bit 15 up at
+  // bit 6 + u, so pair 15 is assembled from the shifted words with no extra shift)
   static constexpr int gshift(int i) {
-    return B == 2 ? (i % 8 < 5 ? 0 : 10) : B == 4 ? (i % 4 < 2 ? 0 : 8) : (i % 5 < 3 ? 0 : 9);
+    return B == 2 ? (i % 8 < 5 ? 0 : 10) : B == 4 ? (i % 4 < 2 ? 0 : 8) : (i % 5 < 3 ? 0 : 9 - i / 5);
   }
   // GEMV class of pair i: bit offset after the shift (3-bit pair 15 is built at 6)
   static constexpr int cls(int i) { return (B == 3 && i == 15) ? 6 : off(i) - gshift(i); }
@@ -67,6 +70,13 @@ __device__ __forceinline__ void decode_classes(const uint32_t (&w)[B], uint32_t 
     // spare bits 15/31 of the three words -> (c30, c31) at offset 6
     r[15] = ((w[0] >> 9) & 0x00400040u) | ((w[1] >> 8) & 0x00800080u) | ((w[2] >> 7) & 0x01000100u);
   }
+}
+
+// fp16x2 bits of (2^-p, 2^-p), p = the class of pair i: x scaled by it meets the
+// pair's code at offset p, so every product lands at the common scale 2^-24
+template <int B> __device__ constexpr uint32_t class_scale_pair(int i) {
+  const uint32_t h = (uint32_t)(15 - Pair<B>::cls(i)) << 10;
+  return h | (h << 16);
 }
 
 // ---- MFMA decode: every pair at offset 1 (value 2*c*2^-24 = c*2^-23)
@@ -92,6 +102,11 @@ template <int B> __device__ constexpr uint32_t off1_offset_pair() {
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 
+// packed fp16 multiply (used once per activation element when x is staged)
+__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, as_h2(a) * as_h2(b));
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
 }
@@ -107,6 +122,14 @@ __device__ __forceinline__ f4_t mfma16(h8_t a, h8_t b, f4_t c) {
 
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// A pointer the compiler may not prove wave-uniform, made so (it is uniform in
+// fact): buffer resources built from it then live in scalar registers.
+template <typename T> __device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
 
 // Buffer resource over [base, base + bytes): raw loads outside the range return 0
 // and touch no memory, so a load can be issued unconditionally.

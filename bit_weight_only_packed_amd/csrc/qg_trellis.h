@@ -226,7 +226,10 @@ __global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
   const int NW = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * NW + wave;
-  const int64_t lo = (int64_t)gw * a.U / a.W, hi = (int64_t)(gw + 1) * a.U / a.W;
+  // W <= U: every wave below W has a non-empty range (the row blocks' arrival
+  // counts rely on it); waves past W only help load the codebook
+  const int64_t lo = gw < a.W ? (int64_t)gw * a.U / a.W : a.U;
+  const int64_t hi = gw < a.W ? (int64_t)(gw + 1) * a.U / a.W : a.U;
   TrUnit<MT> c0, c1, c2;
   tr_load<MT>(a, c0, lo, lo < hi, lane);
   tr_load<MT>(a, c1, lo + 1, lo + 1 < hi, lane);

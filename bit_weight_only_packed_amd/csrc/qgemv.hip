@@ -14,6 +14,7 @@
 #include "../../include/qgemv.h"
 #include "qg_kernels.h"
 #include "qg_trellis.h"
+#include "qg_stream.h"
 
 using namespace qg;
 
@@ -75,6 +76,8 @@ struct qg_plan {
   size_t partial_floats = 0;
   int* counters = nullptr;        // device [total_tiles] split-K arrival counters, zero between runs
   uint16_t* hbuf = nullptr;       // device [max_M][N] fp16, MLP intermediate
+  unsigned long long* acc64 = nullptr;  // device [2][16*total_tiles] M = 1 column words, zero between runs
+  int cus = 0;                    // compute units of the device
   Launch over[3];
   // trellis
   uint32_t* tcodes = nullptr;     // device layout of trellis tiles
@@ -188,6 +191,7 @@ void free_plan(qg_plan* h) {
   if (h->partial) hipFree(h->partial);
   if (h->counters) hipFree(h->counters);
   if (h->hbuf) hipFree(h->hbuf);
+  if (h->acc64) hipFree(h->acc64);
   if (h->tcodes) hipFree(h->tcodes);
   if (h->tscales) hipFree(h->tscales);
   if (h->codebook) hipFree(h->codebook);
@@ -238,7 +242,7 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   // one workgroup per compute unit, 8 waves, at least 2 units per wave
   h->tr_nw = 8;
   h->tr_grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (h->tr_units + 2 * h->tr_nw - 1) / (2 * h->tr_nw)));
-  const int W = h->tr_grid * h->tr_nw;
+  const int W = (int)std::min<int64_t>((int64_t)h->tr_grid * h->tr_nw, h->tr_units);
   h->tr_maxseg = tr_maxseg_of(RB, G, h->tr_units, W);
   const size_t ncode = (size_t)h->tr_units * 64 * 3;
   QG_HIP(hipMalloc(&h->tcodes, ncode * sizeof(uint32_t)));
@@ -278,7 +282,7 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
   a.G = h->G;
   a.RB = h->N / 16;
   a.maxseg = h->tr_maxseg;
-  a.W = h->tr_grid * h->tr_nw;
+  a.W = (int)std::min<int64_t>((int64_t)h->tr_grid * h->tr_nw, h->tr_units);  // every wave's range non-empty
   a.U = h->tr_units;
   const dim3 grid((unsigned)h->tr_grid), block((unsigned)(64 * h->tr_nw));
   if (M == 1) k_trellis<0><<<grid, block, 0, st>>>(a);
@@ -422,10 +426,90 @@ void launch_mfma(const RunArgs& a, int T, int NW, size_t lds, unsigned grid, boo
   }
 }
 
+// M = 1 stream-K GEMV.  Launch knobs (M = 1 overrides): NW waves per workgroup
+// (default 8), S workgroups per compute unit (default 2).
+constexpr size_t kLdsMax = 163840;  // LDS per workgroup on gfx950
+
+bool sk_fits(const qg_plan* h) { return h->G4 <= 63 && sk_lds_bytes(h->G4, (int)h->segs.size()) <= kLdsMax; }
+
+template <int BF, int ND>
+hipError_t sk_allow_lds() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_sk<BF, ND>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+}
+
+// let the stream-K GEMV take more than 64 KiB of dynamic LDS (wide x, several widths)
+hipError_t sk_allow_lds_all() {
+  hipError_t e = hipSuccess;
+  const hipError_t r[] = {sk_allow_lds<0, 1>(), sk_allow_lds<0, 2>(), sk_allow_lds<2, 1>(), sk_allow_lds<2, 2>(),
+                          sk_allow_lds<3, 1>(), sk_allow_lds<3, 2>(), sk_allow_lds<4, 1>(), sk_allow_lds<4, 2>()};
+  for (hipError_t x : r)
+    if (x != hipSuccess) e = x;
+  return e;
+}
+
+template <int BF>
+void launch_sk_b(const SkArgs& a, bool dual, unsigned grid, int NW, size_t lds, hipStream_t st) {
+  if (dual) k_gemv_sk<BF, 2><<<grid, NW * 64, lds, st>>>(a);
+  else k_gemv_sk<BF, 1><<<grid, NW * 64, lds, st>>>(a);
+}
+
+qg_status run_sk(const qg_plan* h, const qg_plan* h2, const uint16_t* x, uint16_t* y, hipStream_t st) {
+  const Launch& L = h->over[0];
+  // measured on the decode shapes: 4 waves per workgroup (8 for K >= 16384), and
+  // enough waves per tile for about 25 / 16 waves per SIMD over the whole chip
+  const int NW = std::max(L.NW > 0 ? std::min(L.NW, 8) : (h->G4 >= 32 ? 8 : 4), (h->G4 + SK_XR - 1) / SK_XR);
+  const int nch_min = (h->G4 + SK_UPW - 1) / SK_UPW;
+  const int nch_want = L.T > 0 ? L.T : (int)((25LL * h->cus / 4 + h->total_tiles - 1) / h->total_tiles);
+  const int nch = std::max(nch_min, std::min(nch_want, std::min(h->G4, 63)));
+  SkArgs a{};
+  a.w[0] = wset_of(h);
+  if (h2) a.w[1] = wset_of(h2);
+  a.x = x;
+  a.y = y;
+  a.acc = h->acc64;
+  a.K = h->K;
+  a.N = h->N;
+  a.G = h->G;
+  a.G4 = h->G4;
+  a.total_tiles = h->total_tiles;
+  a.U = (int64_t)h->total_tiles * h->G4;
+  a.nch = nch;  // waves per tile
+  const unsigned grid = (unsigned)(((int64_t)h->total_tiles * a.nch + NW - 1) / NW);
+  const size_t lds = sk_lds_bytes(h->G4, (int)h->segs.size());
+  const int bf = h->segs.size() == 1 ? h->segs[0].bits : 0;
+  switch (bf) {
+    case 2: launch_sk_b<2>(a, h2 != nullptr, grid, NW, lds, st); break;
+    case 3: launch_sk_b<3>(a, h2 != nullptr, grid, NW, lds, st); break;
+    case 4: launch_sk_b<4>(a, h2 != nullptr, grid, NW, lds, st); break;
+    default: launch_sk_b<0>(a, h2 != nullptr, grid, NW, lds, st); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  if (getenv("QG_DEBUG_SYNC")) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel failed: %s", hipGetErrorString(e));
+  }
+  return QG_OK;
+}
+
+// M = 1 kernel choice, measured on the decode shapes: the per-tile-run kernel
+// (run_sk) everywhere except wide, short-K matrices (>= 512 tiles, K <= 8192),
+// where the per-group kernel (k_gemv_q) is faster.  QG_M1_KERNEL=pergroup|runs
+// forces one.
+bool use_sk(const qg_plan* h) {
+  if (!sk_fits(h)) return false;
+  const char* f = getenv("QG_M1_KERNEL");
+  if (f && !strcmp(f, "pergroup")) return false;
+  if (f && !strcmp(f, "runs")) return true;
+  return !(h->total_tiles >= 512 && h->G4 <= 16);
+}
+
 // one GEMV/GEMM over a uniform handle (or the fused gate+up pair when h2 != NULL)
 qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, int M, uint16_t* y, int ldy,
                       hipStream_t st) {
   const bool dual = h2 != nullptr;
+  if (M == 1 && use_sk(h)) return run_sk(h, h2, x, y, st);
   Launch L = choose(h, M, dual);
   int T = L.T;
   if (M == 1) T = 1;
@@ -536,6 +620,10 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   h->max_M = max_M;
   h->flags = d->flags;
   h->device = dev;
+  if (hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || h->cus < 1) {
+    delete h;
+    return fail(QG_ERR_DEVICE, "cannot query the compute-unit count");
+  }
   hipStream_t st = (hipStream_t)stream;
   s = d->format == QG_FMT_UNIFORM ? create_uniform(h, d, st) : create_trellis(h, d, st);
   if (s == QG_OK && h->format == QG_FMT_UNIFORM) s = ensure_workspace(h);
@@ -547,6 +635,15 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   }
   if (s == QG_OK && hipMalloc(&h->hbuf, (size_t)max_M * d->N * sizeof(uint16_t)) != hipSuccess)
     s = fail(QG_ERR_OOM, "staging allocation failed");
+  if (s == QG_OK && h->format == QG_FMT_UNIFORM && sk_allow_lds_all() != hipSuccess)
+    s = fail(QG_ERR_DEVICE, "cannot raise the LDS limit of the M = 1 kernels");
+  if (s == QG_OK && h->format == QG_FMT_UNIFORM) {
+    const size_t nw = (size_t)2 * 16 * h->total_tiles;
+    if (hipMalloc(&h->acc64, nw * sizeof(unsigned long long)) != hipSuccess)
+      s = fail(QG_ERR_OOM, "column-word allocation failed");
+    else if (hipMemsetAsync(h->acc64, 0, nw * sizeof(unsigned long long), st) != hipSuccess)
+      s = fail(QG_ERR_DEVICE, "column-word initialisation failed");
+  }
   if (s == QG_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(QG_ERR_DEVICE, "stream synchronisation failed");
   if (s != QG_OK) {
     free_plan(h);
