@@ -294,6 +294,42 @@ def main():
         log("mlp", mres)
         del mlps
 
+    # ---------------- trellis-coded weights (27B-class shapes, M = 1 and 8) ----------------
+    if not args.quick:
+        cbk = df16(S.codebook(cfg_id=S.CFG_TRELLIS))
+        tres = {}
+        for name, i in distinct.items():
+            sh = shapes[i]
+            N, K = sh["N"], sh["K"]
+            tw = S.trellis_words(N, K, cfg_id=S.CFG_TRELLIS, tensor_id=S.T_TRELLIS + 10 * i)
+            ts = S.scales(N, K, cfg_id=S.CFG_TRELLIS, tensor_id=S.T_SCALE + 10 * i)
+            dtw = torch.from_numpy(np.ascontiguousarray(tw).view(np.int16).copy()).to(dev)
+            dts = df16(ts)
+            wbt = tw.nbytes + ts.nbytes
+            Rt = int(np.ceil((1 << 30) / wbt))
+            tl = [Q.QLinear(dtw, dts, K, N, trellis=True, codebook=cbk, max_M=8) for _ in range(Rt)]
+            del dtw
+            row = {"K": K, "N": N, "weight_bytes": wbt, "codebook_bytes": 131072, "copies": Rt}
+            for M in (1, 8):
+                xt = xk[(M, K)]
+                out = ys[M][:, :N] if N == 17408 else ys[M].view(-1)[: M * N].view(M, N)
+
+                def f():
+                    for t in tl:
+                        t.run(xt, out=out)
+                g = capture(f)
+                time_graph(g, 2)
+                us = time_graph(g, 10) / (10 * Rt) * 1e6
+                row[f"us_M{M}"] = round(us, 3)
+                row[f"GBs_M{M}"] = round(wbt / us / 1e3, 1)
+            row["ratio_M8_M1"] = round(row["us_M8"] / row["us_M1"], 3)
+            tres[name] = row
+            log("trellis", name, row)
+            for t in tl:
+                t.close()
+            del tl
+        result["trellis"] = tres
+
     # ---------------- CPU oracle on a bounded sample ----------------
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline()

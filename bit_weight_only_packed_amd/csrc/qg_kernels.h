@@ -142,19 +142,31 @@ __global__ void k_repack_uniform(const uint32_t* __restrict__ canon, const int64
 // tile set) adds the S partials in slice order 0..S-1 and stores the result,
 // then re-arms the counter.  No floating-point atomics, so the order of
 // arrival never changes a bit of the output.
+//
+// The partials are written and read only with agent-scope atomic accesses,
+// which go to the device coherence point past the per-XCD L2 caches by
+// themselves: so no cache write-back or invalidation (a device-wide fence,
+// which writes back a whole L2) is needed.  Every thread waits until its own
+// partial stores have completed, the workgroup synchronises, one thread counts
+// the arrival, and only a workgroup that has seen every other slice arrive
+// reads the partials.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_partial(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ bool splitk_last(int* counter, int S, int* flag) {
-  __threadfence();  // release: this workgroup's partials reach device scope
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int last = (atomicAdd(counter, 1) == S - 1);
-    if (last) *counter = 0;
+    const bool last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = last;
   }
   __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __threadfence();  // acquire: the other slices' partials
-  return last;
+  return *flag != 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -328,14 +340,14 @@ __global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
   if (S > 1) {
     if (mine) {
 #pragma unroll
-      for (int d = 0; d < ND; ++d) a.partial[(size_t)(d * S + s) * a.NP + pc] = v[d];
+      for (int d = 0; d < ND; ++d) st_partial(a.partial + (size_t)(d * S + s) * a.NP + pc, v[d]);
     }
     if (!splitk_last(a.counters + tsg, S, flag)) return;
     if (mine) {
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         float acc = 0.0f;
-        for (int k = 0; k < S; ++k) acc += a.partial[(size_t)(d * S + k) * a.NP + pc];
+        for (int k = 0; k < S; ++k) acc += ld_partial(a.partial + (size_t)(d * S + k) * a.NP + pc);
         v[d] = acc;
       }
     }
@@ -539,7 +551,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(RunArgs a) {
       const int pc = 16 * (sg.tile0 + tl0 + t) + (ln & 15);
 #pragma unroll
       for (int d = 0; d < ND; ++d)
-        a.partial[((size_t)(d * S + s) * a.M + row) * a.NP + pc] = red[(size_t)(d * NW) * PER * 64 + idx];
+        st_partial(a.partial + ((size_t)(d * S + s) * a.M + row) * a.NP + pc, red[(size_t)(d * NW) * PER * 64 + idx]);
     }
     if (!splitk_last(a.counters + tsg, S, flag)) return;
   }
@@ -556,7 +568,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(RunArgs a) {
     for (int d = 0; d < ND; ++d) {
       if (S > 1) {
         float acc = 0.0f;
-        for (int k = 0; k < S; ++k) acc += a.partial[((size_t)(d * S + k) * a.M + row) * a.NP + pc];
+        for (int k = 0; k < S; ++k) acc += ld_partial(a.partial + ((size_t)(d * S + k) * a.M + row) * a.NP + pc);
         v[d] = acc;
       } else {
         v[d] = red[(size_t)(d * NW) * PER * 64 + idx];

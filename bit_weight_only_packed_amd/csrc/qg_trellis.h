@@ -202,17 +202,17 @@ __device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT>& t, int64_t 
   }
 }
 
-// A wave's partials reach device scope before it counts its arrival at the
-// row block's counter; the wave that arrives last re-arms the counter and then
-// sees every other wave's partials.
+// A wave's partials (agent-scope atomic stores, which bypass the per-XCD L2)
+// have completed before it counts its arrival at the row block's counter; the
+// wave that arrives last re-arms the counter and reads the other partials with
+// agent-scope atomic loads.  No device-wide fence (an L2 write-back) is needed.
 __device__ __forceinline__ bool tr_arrive_last(int* counter, int nseg, int lane) {
-  __threadfence();  // release: this wave's partials
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
   int old = 0;
-  if (lane == 0) old = atomicAdd(counter, 1);
+  if (lane == 0) old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
   if (old != nseg - 1) return false;
-  if (lane == 0) *counter = 0;
-  __threadfence();  // acquire: the other waves' partials
+  if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
@@ -297,10 +297,10 @@ __global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
       if (nseg == 1) {
         if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(v);
       } else {
-        if (lane < 16) base[(size_t)seg * 16 + n] = v;
+        if (lane < 16) st_partial(base + (size_t)seg * 16 + n, v);
         if (tr_arrive_last(a.counters + rb, nseg, lane)) {
           float t = 0.0f;
-          for (int k = 0; k < nseg; ++k) t += (k == seg) ? v : base[(size_t)k * 16 + n];
+          for (int k = 0; k < nseg; ++k) t += (k == seg) ? v : ld_partial(base + (size_t)k * 16 + n);
           if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(t);
         }
       }
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int m = 16 * mt + 4 * mq + e;
-            if (m < a.M) base[((size_t)seg * a.M + m) * 16 + n] = acc[mt][e];
+            if (m < a.M) st_partial(base + ((size_t)seg * a.M + m) * 16 + n, acc[mt][e]);
           }
         if (tr_arrive_last(a.counters + rb, nseg, lane)) {
 #pragma unroll
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
               if (m >= a.M) continue;
               float t = 0.0f;
               for (int k = 0; k < nseg; ++k)
-                t += (k == seg) ? acc[mt][e] : base[((size_t)k * a.M + m) * 16 + n];
+                t += (k == seg) ? acc[mt][e] : ld_partial(base + ((size_t)k * a.M + m) * 16 + n);
               a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(t);
             }
         }

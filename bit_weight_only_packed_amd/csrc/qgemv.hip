@@ -15,6 +15,7 @@
 #include "qg_kernels.h"
 #include "qg_trellis.h"
 #include "qg_stream.h"
+#include "qg_gemm.h"
 
 using namespace qg;
 
@@ -91,6 +92,26 @@ struct qg_plan {
 namespace {
 
 // ---- launch planning --------------------------------------------------------
+// verify GEMM: the per-wave-K-split kernel (k_gemm_mfma), measured faster on
+// the decode shapes; QG_GEMM=v2 selects the shared-x kernel (k_gemm_v2)
+bool gemm_v2_on() {
+  const char* f = getenv("QG_GEMM");
+  return f && !strcmp(f, "v2");
+}
+
+// Launch shapes of the per-wave-K-split GEMM measured best on MI355X (sweeps
+// over tiles per wave T, waves per workgroup NW and K slices S) for the
+// 27B-class layer shapes; other shapes use the generic rule in choose().
+struct TunedLaunch {
+  int N, K, mcls, T, NW, S;
+};
+constexpr TunedLaunch kTuned[] = {
+    {5120, 5120, 1, 2, 4, 1},  {5120, 5120, 2, 2, 4, 1},   // q, o
+    {1024, 5120, 1, 1, 4, 1},  {1024, 5120, 2, 2, 8, 5},   // k, v
+    {17408, 5120, 1, 2, 2, 1}, {17408, 5120, 2, 4, 4, 1},  // gate, up
+    {5120, 17408, 1, 2, 8, 1}, {5120, 17408, 2, 4, 4, 3},  // down
+};
+
 Launch choose(const qg_plan* h, int M, bool dual = false) {
   Launch L = h->over[mclass(M)];
   const int G = h->G;
@@ -137,7 +158,36 @@ Launch choose(const qg_plan* h, int M, bool dual = false) {
       L.NQ = nq_round_up((g4s + L.NW - 1) / L.NW);
     }
     return L;
+  } else if (gemm_v2_on()) {
+    // verify GEMM: K slices of at most QMAX quads; T tiles per wave and NW
+    // waves per workgroup as wide as keeps >= 2 workgroups per compute unit
+    const int qmax = M <= 16 ? 4 : 2;
+    const int smin = (h->G4 + qmax - 1) / qmax;
+    L.S = std::min(std::max(L.S, smin), h->G4);
+    const int want = std::max(1, h->cus);
+    auto wgs = [&](int T, int NW) {
+      int n = 0;
+      for (const auto& sg : h->segs) n += (sg.tiles + T * NW - 1) / (T * NW);
+      return (int64_t)n * L.S;
+    };
+    if (L.T <= 0) {
+      L.T = 2;
+      if (wgs(2, 8) < want) L.T = 1;
+    }
+    L.T = L.T >= 4 ? 4 : (L.T >= 2 ? 2 : 1);
+    L.T = std::min(L.T, M <= 16 ? (dual ? 1 : 2) : (dual ? 2 : 4));  // compiled tile counts
+    if (L.NW <= 0) L.NW = 8;
+    L.NW = L.NW >= 8 ? 8 : 4;  // the x staging takes at least 4 waves
+    return L;
   } else {
+    if (L.T <= 0 && L.NW <= 0 && L.S <= 0 && !dual) {
+      for (const TunedLaunch& t : kTuned)
+        if (t.N == h->N && t.K == h->K && t.mcls == mclass(M)) {
+          L.T = t.T;
+          L.NW = t.NW;
+          L.S = t.S;
+        }
+    }
     if (L.T <= 0) L.T = 2;
     const int tilesets = (h->total_tiles + L.T - 1) / L.T;
     if (L.NW <= 0) L.NW = pick_nw(tilesets, 1800);
@@ -505,11 +555,79 @@ bool use_sk(const qg_plan* h) {
   return !(h->total_tiles >= 512 && h->G4 <= 16);
 }
 
+template <int T, int MT, int QMAX, bool DUAL>
+void launch_v2_b(const GmArgs& a, int bf, unsigned grid, size_t lds, hipStream_t st) {
+  switch (bf) {
+    case 2: k_gemm_v2<T, MT, QMAX, DUAL, 2><<<grid, a.NW * 64, lds, st>>>(a); break;
+    case 3: k_gemm_v2<T, MT, QMAX, DUAL, 3><<<grid, a.NW * 64, lds, st>>>(a); break;
+    case 4: k_gemm_v2<T, MT, QMAX, DUAL, 4><<<grid, a.NW * 64, lds, st>>>(a); break;
+    default: k_gemm_v2<T, MT, QMAX, DUAL, 0><<<grid, a.NW * 64, lds, st>>>(a); break;
+  }
+}
+
+// compiled tile counts per wave: (MT, QMAX) = (1, 4): T <= 2, fused pair T = 1;
+// (2, 2): T <= 4, fused pair T <= 2 (register room for all of a slice's codes)
+constexpr int v2_tmax(int MT, bool dual) { return MT == 1 ? (dual ? 1 : 2) : (dual ? 2 : 4); }
+
+template <int MT, int QMAX>
+void launch_v2(const GmArgs& a, int T, bool dual, int bf, unsigned grid, size_t lds, hipStream_t st) {
+  if (dual) {
+    if (T == 1 || v2_tmax(MT, true) < 2) launch_v2_b<1, MT, QMAX, true>(a, bf, grid, lds, st);
+    else if constexpr (v2_tmax(MT, true) >= 2) launch_v2_b<2, MT, QMAX, true>(a, bf, grid, lds, st);
+  } else {
+    if (T == 1) launch_v2_b<1, MT, QMAX, false>(a, bf, grid, lds, st);
+    else if (T == 2 || v2_tmax(MT, false) < 4) launch_v2_b<2, MT, QMAX, false>(a, bf, grid, lds, st);
+    else if constexpr (v2_tmax(MT, false) >= 4) launch_v2_b<4, MT, QMAX, false>(a, bf, grid, lds, st);
+  }
+}
+
+qg_status run_gemm_v2(const qg_plan* h, const qg_plan* h2, const uint16_t* x, int M, uint16_t* y, int ldy,
+                      hipStream_t st) {
+  const bool dual = h2 != nullptr;
+  const Launch L = choose(h, M, dual);
+  GmArgs a{};
+  a.w[0] = wset_of(h);
+  if (h2) a.w[1] = wset_of(h2);
+  a.x = x;
+  a.y = y;
+  a.partial = h->partial;
+  a.counters = h->counters;
+  a.M = M;
+  a.K = h->K;
+  a.G = h->G;
+  a.G4 = h->G4;
+  a.ldy = ldy;
+  a.NP = 16 * h->total_tiles;
+  a.S = L.S;
+  a.NW = L.NW;
+  int pre = 0;
+  for (int i = 0; i < (int)h->segs.size(); ++i) {
+    a.ts_prefix[i] = pre;
+    pre += (h->segs[i].tiles + L.T * L.NW - 1) / (L.T * L.NW);
+  }
+  for (int i = (int)h->segs.size(); i <= MAX_SEG; ++i) a.ts_prefix[i] = pre;
+  if (L.S > 1 && partial_need(h, L.S, M) > h->partial_floats)
+    return fail(QG_ERR_INVALID_ARG, "workspace too small for %d K-slices at M=%d", L.S, M);
+  if (pre > h->total_tiles) return fail(QG_ERR_INVALID_ARG, "more tile sets than counters");
+  const unsigned grid = (unsigned)pre * (unsigned)L.S;
+  const int bf = h->segs.size() == 1 ? h->segs[0].bits : 0;
+  if (M <= 16) launch_v2<1, 4>(a, L.T, dual, bf, grid, gm_lds_bytes(1, 4), st);
+  else launch_v2<2, 2>(a, L.T, dual, bf, grid, gm_lds_bytes(2, 2), st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  if (getenv("QG_DEBUG_SYNC")) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel failed: %s", hipGetErrorString(e));
+  }
+  return QG_OK;
+}
+
 // one GEMV/GEMM over a uniform handle (or the fused gate+up pair when h2 != NULL)
 qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, int M, uint16_t* y, int ldy,
                       hipStream_t st) {
   const bool dual = h2 != nullptr;
   if (M == 1 && use_sk(h)) return run_sk(h, h2, x, y, st);
+  if (M > 1 && gemm_v2_on()) return run_gemm_v2(h, h2, x, M, y, ldy, st);
   Launch L = choose(h, M, dual);
   int T = L.T;
   if (M == 1) T = 1;
