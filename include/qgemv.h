@@ -131,10 +131,18 @@ const char* qg_last_error(void);
 qg_status qgemv_weight_bytes(qg_handle h, int64_t* bytes);
 
 /* Override the launch geometry used for runs with M rows in the class of
- * `M` (M = 1, or any M in 2..16, or any M in 17..32): `tiles` 16-column tiles
- * per workgroup, `waves` waves per workgroup (1, 2, 4 or 8) splitting K, `splits`
- * K-slices across workgroups (1..16, reduced in a fixed order).  Values <= 0
- * restore the built-in choice.  Used for launch-shape sweeps. */
+ * `M` (M = 1, or any M in 2..16, or any M in 17..32); for sweeps of launch
+ * shapes.  Values <= 0 restore the built-in choice.  Meaning per kernel:
+ *   M = 1, per-tile-run GEMV (the default except for >= 512 tiles with
+ *     K <= 8192): `tiles` = waves per 16-column tile (each takes a run of at most
+ *     8 quads of 512 k), `waves` = waves per workgroup (1..8), `splits` unused.
+ *   M = 1, per-group GEMV: `tiles` 16-column tiles per workgroup (1), `waves`
+ *     waves per workgroup splitting K (1..16), `splits` K slices across
+ *     workgroups (1..16, reduced in a fixed order).
+ *   M > 1: `tiles` tiles per wave (1, 2 or 4), `waves` waves per workgroup
+ *     (1, 2, 4 or 8), `splits` K slices across workgroups (1..16).
+ * Uniform-code handles only; a shape the compiled kernels cannot take fails
+ * with QG_ERR_INVALID_ARG when it is run. */
 qg_status qgemv_set_launch(qg_handle h, int32_t M, int32_t tiles, int32_t waves, int32_t splits);
 
 /* ---- checking entry points (same device decode functions as the run kernels) ---- */
