@@ -5,9 +5,9 @@
 // B KiB of codes, read by B wave-wide 16-byte-per-lane loads, and 128 B of
 // scales.  Each tile's G4 quads are cut into `nch` near-equal runs of at most
 // SK_UPW consecutive quads, one run per wave; a wave walks its run in
-// straight-line code with the next two units' loads in flight (three register
-// sets in rotation), so every wait the compiler places is exact, and hands its
-// partial of the tile on once, at the end.
+// straight-line code with the next SK_PD - 1 units' loads in flight (SK_PD
+// register sets in rotation), so every wait the compiler places is exact, and
+// hands its partial of the tile on once, at the end.
 //
 // Activations.  Each workgroup stages x once in LDS, every element already
 // multiplied by 2^-class of the code position it meets (class_scale_pair), so a
@@ -36,6 +36,7 @@ namespace qg {
 
 constexpr int SK_FRAC = 28;  // fraction bits of the fixed-point column words
 constexpr int SK_UPW = 8;    // at most this many quads per wave
+constexpr int SK_PD = 3;     // units whose loads are in flight while one is computed
 
 struct SkArgs {
   WSet w[2];                   // w[1]: up matrix of the fused gate/up pass
@@ -94,14 +95,14 @@ __device__ __forceinline__ float sk_value(unsigned long long total) {
   return (float)((double)((long long)total >> 6) * (1.0 / (double)(1ll << SK_FRAC)));
 }
 
-// The three register sets of a wave's load pipeline over one width segment.
+// The SK_PD register sets of a wave's load pipeline over one width segment.
 template <int B, int ND>
 struct SkPipe {
   SkPtrs<ND> ptr;
-  SkUnit<B, ND> c0, c1, c2;
+  SkUnit<B, ND> c[SK_PD];
 };
 
-// Issue the loads of the first three units of [u0, u1) (segment-local); a
+// Issue the loads of the first SK_PD units of [u0, u1) (segment-local); a
 // wave with an empty range issues loads that read nothing.
 template <int B, int ND>
 __device__ __forceinline__ void sk_prime(SkPipe<B, ND>& pp, const SegDev (&sd)[2], int u0, int u1, int lane) {
@@ -110,9 +111,8 @@ __device__ __forceinline__ void sk_prime(SkPipe<B, ND>& pp, const SegDev (&sd)[2
     pp.ptr.codes[d] = uniform_ptr(sd[d].codes);
     pp.ptr.scales[d] = uniform_ptr(sd[d].scales);
   }
-  sk_load<B, ND>(pp.ptr, pp.c0, u0, u0 < u1, lane);
-  sk_load<B, ND>(pp.ptr, pp.c1, u0 + 1, u0 + 1 < u1, lane);
-  sk_load<B, ND>(pp.ptr, pp.c2, u0 + 2, u0 + 2 < u1, lane);
+#pragma unroll
+  for (int i = 0; i < SK_PD; ++i) sk_load<B, ND>(pp.ptr, pp.c[i], u0 + i, u0 + i < u1, lane);
 }
 
 // Walk the primed units [u0, u1) (segment-local, all of one tile, at most
@@ -158,14 +158,11 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, SkPipe<B, ND>& pp, int u
         acc[d] = __builtin_fmaf(s, e0 + e1, acc[d]);
       }
     }
-    if (u + 3 - u0 < SK_UPW) sk_load<B, ND>(pp.ptr, cu, u + 3, u + 3 < u1, lane);
+    if (u + SK_PD - u0 < SK_UPW) sk_load<B, ND>(pp.ptr, cu, u + SK_PD, u + SK_PD < u1, lane);
   };
 #pragma unroll
-  for (int k = 0; k < SK_UPW; k += 3) {
-    if (u0 + k < u1) step(pp.c0, u0 + k);
-    if (k + 1 < SK_UPW && u0 + k + 1 < u1) step(pp.c1, u0 + k + 1);
-    if (k + 2 < SK_UPW && u0 + k + 2 < u1) step(pp.c2, u0 + k + 2);
-  }
+  for (int k = 0; k < SK_UPW; ++k)
+    if (u0 + k < u1) step(pp.c[k % SK_PD], u0 + k);
   // ---- hand this wave's partial of the tile on
   const int tg = tg0 + tile;  // tile index over all segments
   float v[ND];

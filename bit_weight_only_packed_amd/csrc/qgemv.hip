@@ -112,7 +112,7 @@ constexpr TunedLaunch kTuned[] = {
     {5120, 17408, 1, 2, 8, 1}, {5120, 17408, 2, 4, 4, 3},  // down
 };
 
-Launch choose(const qg_plan* h, int M, bool dual = false) {
+Launch choose(const qg_plan* h, int M, bool dual = false, int force_v2 = -1) {
   Launch L = h->over[mclass(M)];
   const int G = h->G;
   if (h->format == QG_FMT_TRELLIS3) {
@@ -158,7 +158,7 @@ Launch choose(const qg_plan* h, int M, bool dual = false) {
       L.NQ = nq_round_up((g4s + L.NW - 1) / L.NW);
     }
     return L;
-  } else if (gemm_v2_on()) {
+  } else if (force_v2 < 0 ? gemm_v2_on() : force_v2 != 0) {
     // verify GEMM: K slices of at most QMAX quads; T tiles per wave and NW
     // waves per workgroup as wide as keeps >= 2 workgroups per compute unit
     const int qmax = M <= 16 ? 4 : 2;
@@ -207,7 +207,11 @@ qg_status ensure_workspace(qg_plan* h) {
     const int Mc = c == 0 ? 1 : (c == 1 ? 16 : 32);
     if (Mc > h->max_M && c > 0 && (c == 1 ? 2 : 17) > h->max_M) continue;
     const int Mm = std::min(Mc, h->max_M);
-    need = std::max(need, partial_need(h, choose(h, Mm).S, Mm));
+    // either verify GEMM may be selected at run time: size for both
+    for (int v2 = 0; v2 < 2; ++v2) {
+      need = std::max(need, partial_need(h, choose(h, Mm, false, v2).S, Mm));
+      need = std::max(need, partial_need(h, choose(h, Mm, true, v2).S, Mm));
+    }
   }
   if (need > h->partial_floats) {
     if (h->partial) hipFree(h->partial);
