@@ -262,9 +262,7 @@ __global__ __launch_bounds__(512) void k_gemm_v2(GmArgs a) {
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
           if (S > 1) {
-            float t2 = 0.0f;
-            for (int k = 0; k < S; ++k) t2 += ld_partial(a.partial + ((size_t)(d * S + k) * a.M + m) * a.NP + pc);
-            v[d] = t2;
+            v[d] = sum_partials(a.partial + ((size_t)(d * S) * a.M + m) * a.NP + pc, (size_t)a.M * a.NP, S);
           } else {
             v[d] = acc[d][t][mt][e] * 16777216.0f;
           }

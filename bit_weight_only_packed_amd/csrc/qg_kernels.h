@@ -157,6 +157,25 @@ __device__ __forceinline__ void st_partial(float* p, float v) {
 __device__ __forceinline__ float ld_partial(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// sum_{k < n} (k == own ? own_v : p[k * stride]) in the order k = 0, 1, ...: the
+// loads go out eight at a time (one round trip per eight partials, not one
+// each); own < 0 means every partial comes from memory
+__device__ __forceinline__ float sum_partials(const float* p, size_t stride, int n, int own = -1, float own_v = 0.0f) {
+  float t = 0.0f;
+  for (int k0 = 0; k0 < n; k0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + i;
+      v[i] = (k < n && k != own) ? ld_partial(p + (size_t)k * stride) : own_v;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (k0 + i < n) t += v[i];
+  }
+  return t;
+}
 __device__ __forceinline__ bool splitk_last(int* counter, int S, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
@@ -347,7 +366,7 @@ __global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         float acc = 0.0f;
-        for (int k = 0; k < S; ++k) acc += ld_partial(a.partial + (size_t)(d * S + k) * a.NP + pc);
+        acc = sum_partials(a.partial + (size_t)(d * S) * a.NP + pc, (size_t)a.NP, S);
         v[d] = acc;
       }
     }
@@ -568,7 +587,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(RunArgs a) {
     for (int d = 0; d < ND; ++d) {
       if (S > 1) {
         float acc = 0.0f;
-        for (int k = 0; k < S; ++k) acc += ld_partial(a.partial + ((size_t)(d * S + k) * a.M + row) * a.NP + pc);
+        acc = sum_partials(a.partial + ((size_t)(d * S) * a.M + row) * a.NP + pc, (size_t)a.M * a.NP, S);
         v[d] = acc;
       } else {
         v[d] = red[(size_t)(d * NW) * PER * 64 + idx];

@@ -23,7 +23,7 @@
 // reads a unit's 768 contiguous bytes once.  The 15 bits of look-ahead that the
 // last windows of a row need are the first bits of the next row of the same
 // tile (row 0 after row 15), which the lane of row n + 1 mod 16 in the same
-// quarter holds: two cross-lane reads per unit.  Scales: fp16 [unit][16].
+// quarter holds: two DPP row rotations per unit.  Scales: fp16 [unit][16].
 //
 // Decode.  With a row as a 64-bit value R (row bits at 63..16, the next row's
 // first 16 bits at 15..0), 2 * state_c = (R >> (47 - 3c)) & 0x1FFFE: one funnel
@@ -60,7 +60,11 @@ __global__ void k_repack_trellis(const uint16_t* __restrict__ tiles, const uint1
 // ---------------------------------------------------------------------------
 // decode: codebook byte addresses of the lane's 32 weights (k = 32kq + j)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t tr_nbr_lane(int lane) { return (uint32_t)((lane & ~15) | ((lane + 1) & 15)); }
+// the value of lane (l & ~15) | ((l + 1) & 15): a DPP rotate of each 16-lane row
+// (row_ror by 15 moves every lane's value one lane down, the first to the last)
+__device__ __forceinline__ uint32_t tr_from_next_row_lane(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x12F, 0xF, 0xF, false);
+}
 
 // addr[j] = 2 * state of weight j; z = the lane's words, nz2 / nz1 = Z2 / Z1 of
 // the lane holding row n + 1 mod 16 of the same tiles
@@ -140,8 +144,8 @@ __global__ __launch_bounds__(256) void k_fwht(const uint16_t* __restrict__ x, ui
 //
 // One workgroup per compute unit holds the codebook in LDS for the whole launch.
 // The RB * G units are split into W equal contiguous ranges in row-block-major
-// order, one per wave (stream-K): a wave walks its range with the next two
-// units' loads in flight (three register sets in rotation), accumulates while
+// order, one per wave (stream-K): a wave walks its range with the next units'
+// loads in flight (PD register sets in rotation), accumulates while
 // the row block stays the same and leaves a partial sum per row block it
 // touches.  A row block's partials sit
 // in fixed slots (slot = wave - first wave of the row block); the wave that
@@ -172,16 +176,16 @@ __device__ __forceinline__ int tr_wave_of(int64_t x, int64_t U, int W) {
 template <int MT>
 struct TrUnit {
   static constexpr int XR = MT == 0 ? 1 : MT;  // activation row blocks held
+  static constexpr int loads = 2 + 4 * XR;     // load instructions per unit
   u3_t z;                                      // code words
   uint32_t s;                                  // this lane's scale (fp16 in the low half)
   uint4 xv[XR][4];                             // activations: 32 k of row (16*mt + (lane & 15)), or of row 0 (M = 1)
 };
 
 template <int MT>
-__device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT>& t, int64_t u, bool live, int lane) {
+__device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT>& t, int64_t u, int g, bool live, int lane) {
   const int uu = live ? 1 : 0;
   const int64_t uc = live ? u : 0;
-  const int g = (int)(uc % a.G);
   const int kq = lane >> 4;
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes + uc * 192, uu * 768u);
   t.z = __builtin_amdgcn_raw_buffer_load_b96(rc, (uint32_t)lane * 12u, 0, 0);
@@ -216,8 +220,16 @@ __device__ __forceinline__ bool tr_arrive_last(int* counter, int nseg, int lane)
   return true;
 }
 
+// NWMAX: waves per workgroup the kernel is built for (16 keeps four waves on
+// each SIMD; the 32-row variant needs the registers of eight); PD: units whose
+// loads are in flight while one is computed.
+template <int MT> struct TrShape {
+  static constexpr int NWMAX = MT == 2 ? 8 : 16;
+  static constexpr int PD = MT == 2 ? 3 : 2;
+};
+
 template <int MT>
-__global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
+__global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
   // static (not dynamic) LDS: its address is a compile-time constant, so the
   // gathers use the decoded byte address as is
   __shared__ __align__(16) char smem[TR_CB_BYTES];
@@ -230,30 +242,41 @@ __global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
   // counts rely on it); waves past W only help load the codebook
   const int64_t lo = gw < a.W ? (int64_t)gw * a.U / a.W : a.U;
   const int64_t hi = gw < a.W ? (int64_t)(gw + 1) * a.U / a.W : a.U;
-  TrUnit<MT> c0, c1, c2;
-  tr_load<MT>(a, c0, lo, lo < hi, lane);
-  tr_load<MT>(a, c1, lo + 1, lo + 1 < hi, lane);
-  tr_load<MT>(a, c2, lo + 2, lo + 2 < hi, lane);
-  // codebook -> LDS (every wave stays to the barrier)
+  constexpr int PD = TrShape<MT>::PD;
+  // codebook -> LDS straight from memory (buffer loads to LDS, 1 KiB per wave
+  // instruction), then this wave's first units: waiting for the codebook does
+  // not wait for those
   {
-    const uint4* src = reinterpret_cast<const uint4*>(a.cb);
-    uint4* dst = reinterpret_cast<uint4*>(smem);
-    for (int i = threadIdx.x; i < TR_CB_BYTES / 16; i += blockDim.x) dst[i] = src[i];
+    const __amdgpu_buffer_rsrc_t rcb = make_rsrc(uniform_ptr(a.cb), TR_CB_BYTES);
+    const int NWv = blockDim.x >> 6;
+    for (int ci = wave; ci < TR_CB_BYTES / 1024; ci += NWv)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rcb, (__attribute__((address_space(3))) void*)(smem + (size_t)ci * 1024),
+                                               16, (uint32_t)(ci * 1024 + lane * 16), 0, 0, 0);
   }
-  __syncthreads();
+  TrUnit<MT> c[PD];
+#pragma unroll
+  for (int i = 0; i < PD; ++i) tr_load<MT>(a, c[i], lo + i, (int)((lo + i) % a.G), lo + i < hi, lane);
+  {
+    constexpr int n = PD * TrUnit<MT>::loads;  // loads issued after the codebook's
+    static_assert(n < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  }
+  lds_barrier();  // every wave's share of the codebook has landed
   if (lo >= hi) return;
   const char* cbl = smem;
-  const uint32_t nbr = tr_nbr_lane(lane);
   float acc1 = 0.0f;
   f4_t acc[XR];
 #pragma unroll
   for (int mt = 0; mt < XR; ++mt) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  int rb = (int)(lo / a.G);
+  // row block and group of the unit being computed, group of the next unit to
+  // load (kept as counters: no division per unit)
+  int rb = (int)(lo / a.G), g = (int)(lo - (int64_t)rb * a.G);
+  int gpf = (int)((lo + PD) % a.G);
   // one unit: decode, contract, reload the same registers with unit u + 3, and
   // flush at the end of a row block or of the range
   auto step = [&](TrUnit<MT>& cu, int64_t u) {
     const uint32_t z2 = cu.z.x, z1 = cu.z.y, z0 = cu.z.z;
-    const uint32_t nz2 = (uint32_t)__shfl((int)z2, (int)nbr), nz1 = (uint32_t)__shfl((int)z1, (int)nbr);
+    const uint32_t nz2 = tr_from_next_row_lane(z2), nz1 = tr_from_next_row_lane(z1);
     uint32_t addr[32];
     tr_addrs(z2, z1, z0, nz2, nz1, addr);
     uint32_t pr[16];
@@ -281,9 +304,11 @@ __global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
         for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(s, cg[e], acc[mt][e]);
       }
     }
-    tr_load<MT>(a, cu, u + 3, u + 3 < hi, lane);
+    tr_load<MT>(a, cu, u + PD, gpf, u + PD < hi, lane);
+    gpf = gpf + 1 == a.G ? 0 : gpf + 1;
     const bool last_unit = u + 1 == hi;
-    const int rb_next = (int)((u + 1) / a.G);
+    g = g + 1 == a.G ? 0 : g + 1;
+    const int rb_next = g == 0 ? rb + 1 : rb;
     if (!last_unit && rb_next == rb) return;
     const int w0 = tr_wave_of((int64_t)rb * a.G, a.U, a.W);
     const int w1 = tr_wave_of((int64_t)rb * a.G + a.G - 1, a.U, a.W);
@@ -299,8 +324,7 @@ __global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
       } else {
         if (lane < 16) st_partial(base + (size_t)seg * 16 + n, v);
         if (tr_arrive_last(a.counters + rb, nseg, lane)) {
-          float t = 0.0f;
-          for (int k = 0; k < nseg; ++k) t += (k == seg) ? v : ld_partial(base + (size_t)k * 16 + n);
+          const float t = sum_partials(base + n, 16, nseg, seg, v);
           if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(t);
         }
       }
@@ -330,9 +354,7 @@ __global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
             for (int e = 0; e < 4; ++e) {
               const int m = 16 * mt + 4 * mq + e;
               if (m >= a.M) continue;
-              float t = 0.0f;
-              for (int k = 0; k < nseg; ++k)
-                t += (k == seg) ? acc[mt][e] : ld_partial(base + ((size_t)k * a.M + m) * 16 + n);
+              const float t = sum_partials(base + (size_t)m * 16 + n, (size_t)a.M * 16, nseg, seg, acc[mt][e]);
               a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(t);
             }
         }
@@ -342,12 +364,12 @@ __global__ __launch_bounds__(512) void k_trellis(TrArgs a) {
     }
     rb = rb_next;
   };
-  for (int64_t u = lo; u < hi; u += 3) {
-    step(c0, u);
-    if (u + 1 >= hi) break;
-    step(c1, u + 1);
-    if (u + 2 >= hi) break;
-    step(c2, u + 2);
+  for (int64_t u = lo; u < hi; u += PD) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) {
+      if (u + i >= hi) break;
+      step(c[i], u + i);
+    }
   }
 }
 
@@ -365,8 +387,7 @@ __global__ __launch_bounds__(256) void k_debug_trellis(const uint32_t* __restric
   const int rb = (int)(u / G), g = (int)(u % G);
   const uint32_t* zp = codes + (u * 64 + lane) * 3;
   const uint32_t z2 = zp[0], z1 = zp[1], z0 = zp[2];
-  const uint32_t nbr = tr_nbr_lane(lane);
-  const uint32_t nz2 = (uint32_t)__shfl((int)z2, (int)nbr), nz1 = (uint32_t)__shfl((int)z1, (int)nbr);
+  const uint32_t nz2 = tr_from_next_row_lane(z2), nz1 = tr_from_next_row_lane(z1);
   uint32_t addr[32];
   tr_addrs(z2, z1, z0, nz2, nz1, addr);
   const int n = rb * 16 + (lane & 15);

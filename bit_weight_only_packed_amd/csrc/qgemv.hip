@@ -86,7 +86,7 @@ struct qg_plan {
   uint16_t* codebook = nullptr;   // device copy, 65536 fp16
   uint16_t* xrot = nullptr;       // device [max_M][K] fp16, rotated activations
   int64_t tr_units = 0;           // (N/16) * G
-  int tr_grid = 0, tr_nw = 0, tr_maxseg = 0;
+  int tr_grid = 0, tr_maxseg = 0;
 };
 
 namespace {
@@ -293,11 +293,15 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   h->total_tiles = RB;
   h->tr_units = (int64_t)RB * G;
   h->weight_bytes = (int64_t)N * K * 3 / 8 + (int64_t)N * G * 2;
-  // one workgroup per compute unit, 8 waves, at least 2 units per wave
-  h->tr_nw = 8;
-  h->tr_grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (h->tr_units + 2 * h->tr_nw - 1) / (2 * h->tr_nw)));
-  const int W = (int)std::min<int64_t>((int64_t)h->tr_grid * h->tr_nw, h->tr_units);
-  h->tr_maxseg = tr_maxseg_of(RB, G, h->tr_units, W);
+  // one workgroup per compute unit (the codebook fills its LDS) of 16 waves (8
+  // for more than 16 rows); the codebook gathers bound the kernel, so small
+  // matrices still spread over as many compute units as they have 16 units for
+  h->tr_grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (h->tr_units + 15) / 16));
+  h->tr_maxseg = 1;
+  for (int nw : {8, 16}) {
+    const int W = (int)std::min<int64_t>((int64_t)h->tr_grid * nw, h->tr_units);
+    h->tr_maxseg = std::max(h->tr_maxseg, tr_maxseg_of(RB, G, h->tr_units, W));
+  }
   const size_t ncode = (size_t)h->tr_units * 64 * 3;
   QG_HIP(hipMalloc(&h->tcodes, ncode * sizeof(uint32_t)));
   QG_HIP(hipMalloc(&h->tscales, (size_t)h->tr_units * 16 * sizeof(uint16_t)));
@@ -336,9 +340,10 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
   a.G = h->G;
   a.RB = h->N / 16;
   a.maxseg = h->tr_maxseg;
-  a.W = (int)std::min<int64_t>((int64_t)h->tr_grid * h->tr_nw, h->tr_units);  // every wave's range non-empty
+  const int nw = M > 16 ? TrShape<2>::NWMAX : TrShape<0>::NWMAX;
+  a.W = (int)std::min<int64_t>((int64_t)h->tr_grid * nw, h->tr_units);  // every wave's range non-empty
   a.U = h->tr_units;
-  const dim3 grid((unsigned)h->tr_grid), block((unsigned)(64 * h->tr_nw));
+  const dim3 grid((unsigned)h->tr_grid), block((unsigned)(64 * nw));
   if (M == 1) k_trellis<0><<<grid, block, 0, st>>>(a);
   else if (M <= 16) k_trellis<1><<<grid, block, 0, st>>>(a);
   else k_trellis<2><<<grid, block, 0, st>>>(a);
