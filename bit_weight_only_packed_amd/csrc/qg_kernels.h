@@ -4,9 +4,11 @@
 //
 // Arithmetic (uniform b-bit codes, offset o = (2^b - 1)/2, group g of 128 k):
 //   y[m][n] = sum_g s[n][g] * sum_{k in g} x[m][k] * (c[n][k] - o)
-// The GEMV forms sum x*c per group from the exact subnormal code values, adds
-// the offset term as -o * s * sum_{k in g} x[k] (activation sums precomputed
-// once per workgroup) and applies the scale per group, all in fp32.  The MFMA
+// The GEMV stages x once per workgroup, each element times 2^-class of the code
+// position it meets, so one dot2 chain over the exact subnormal code values
+// gives 2^-24 * sum x*c whatever the class; the chain starts from the offset
+// term -o * 2^-24 * (sum of the lane's 32 x, staged beside x) and the scale is
+// applied per group, all in fp32.  The MFMA
 // path feeds codes at scale 2^-23 and starts every group's accumulation from
 // the offset product x * (-o * 2^-23), so each group's MFMA chain yields
 // 2^-23 * sum x*(c - o) directly; the scale is applied per group in fp32.
@@ -204,7 +206,7 @@ __host__ __device__ constexpr size_t m1_lds_bytes(int nqs, int ND, int NW) {
 
 template <int B, int NQ, int ND>
 __device__ __forceinline__ void gemv_q_body(const RunArgs& a, const SegDev (&sd)[2], int tile, int q_beg, int q_end,
-                                            char* smem, float (&R)[2], float (&Ro)[2]) {
+                                            char* smem, float (&R)[2]) {
   using P = Pair<B>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -239,9 +241,19 @@ __device__ __forceinline__ void gemv_q_body(const RunArgs& a, const SegDev (&sd)
 #pragma unroll
     for (int u = 0; u < NQ; ++u) buffer_quad<B>(rs, (uint32_t)lane, u, cw[d][u]);
   }
-  // ---- prologue stores: x, 32-element quarter sums, scales
+  // ---- prologue stores: x (each element times 2^-class of the code position
+  // it meets, so one dot2 chain serves every class), 32-element quarter sums
+  // (of x itself), scales
   {
     const uint32_t ones = 0x3C003C00u;  // fp16 (1, 1)
+    const int pos = tid & 3;            // uint4 position within a quarter (blockDim % 4 == 0)
+    uint32_t f[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t f0 = class_scale_pair<B>(e), f1 = class_scale_pair<B>(4 + e);
+      const uint32_t f2 = class_scale_pair<B>(8 + e), f3 = class_scale_pair<B>(12 + e);
+      f[e] = pos == 0 ? f0 : pos == 1 ? f1 : pos == 2 ? f2 : f3;
+    }
     auto stage = [&](const uint4& v, int i) {
       float ps = dot2(v.x, ones, 0.0f);
       ps = dot2(v.y, ones, ps);
@@ -250,7 +262,7 @@ __device__ __forceinline__ void gemv_q_body(const RunArgs& a, const SegDev (&sd)
       ps += dpp_xor1(ps);
       ps += dpp_xor2(ps);
       if (i < nx) {
-        xl[i] = v;
+        xl[i] = make_uint4(pk_mul_f16(v.x, f[0]), pk_mul_f16(v.y, f[1]), pk_mul_f16(v.z, f[2]), pk_mul_f16(v.w, f[3]));
         if ((i & 3) == 0) xs[i >> 2] = ps;
       }
     };
@@ -284,30 +296,24 @@ __device__ __forceinline__ void gemv_q_body(const RunArgs& a, const SegDev (&sd)
         xp[4 * v + 0] = u4.x; xp[4 * v + 1] = u4.y; xp[4 * v + 2] = u4.z; xp[4 * v + 3] = u4.w;
       }
       const float xsum = xs[gl * 4 + q];
+      const float ko = -0.5f * (float)((1 << B) - 1) * 5.9604644775390625e-08f;  // -o * 2^-24
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         uint32_t g3[B];
         quad_group<B>(cw[d][u], gi, g3);
         uint32_t r[16];
         decode_classes<B>(g3, r);
-        float acc[9];
+        // 2^-24 * sum x * (c - o) over the lane's 32 weights
+        float e0 = xsum * ko, e1 = 0.0f;
 #pragma unroll
-        for (int p = 0; p < 9; ++p) acc[p] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[P::cls(i)] = dot2(r[i], xp[i], acc[P::cls(i)]);
-        // sum x*c * 2^-24 = sum_p acc_p * 2^-p
-        float sxc = acc[0];
-#pragma unroll
-        for (int p = 1; p < 9; ++p) {
-          bool used = false;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) used |= (P::cls(i) == p);
-          if (used) sxc = __builtin_fmaf(acc[p], 1.0f / (float)(1 << p), sxc);
+        for (int i = 0; i < 16; i += 2) {
+          e0 = dot2(r[i], xp[i], e0);
+          e1 = dot2(r[i + 1], xp[i + 1], e1);
         }
+        const float sxc = e0 + e1;
         // scales staged as [quad][16][4]
         const float s = h2f(sl[d * nsw * 2 + ((gl >> 2) * 16 + j) * 4 + (gl & 3)]);
         R[d] = __builtin_fmaf(s, sxc, R[d]);
-        Ro[d] = __builtin_fmaf(s, xsum, Ro[d]);
       }
     }
   }
@@ -331,18 +337,17 @@ __global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
   sd[1] = DUAL ? (BF == 0 ? pick(a.w[1], si) : a.w[1].seg[0]) : sd[0];
   const int tile = BF == 0 ? tsg - a.ts_prefix[si] : tsg;
   const int q_beg = (int)((int64_t)s * G4 / S), q_end = (int)((int64_t)(s + 1) * G4 / S);
-  float R[2] = {0.0f, 0.0f}, Ro[2] = {0.0f, 0.0f};
+  float R[2] = {0.0f, 0.0f};
   const int bits = sd[0].bits;
-  if (BF == 2 || (BF == 0 && bits == 2)) gemv_q_body<2, NQ, ND>(a, sd, tile, q_beg, q_end, smem, R, Ro);
-  else if (BF == 3 || (BF == 0 && bits == 3)) gemv_q_body<3, NQ, ND>(a, sd, tile, q_beg, q_end, smem, R, Ro);
-  else gemv_q_body<4, NQ, ND>(a, sd, tile, q_beg, q_end, smem, R, Ro);
+  if (BF == 2 || (BF == 0 && bits == 2)) gemv_q_body<2, NQ, ND>(a, sd, tile, q_beg, q_end, smem, R);
+  else if (BF == 3 || (BF == 0 && bits == 3)) gemv_q_body<3, NQ, ND>(a, sd, tile, q_beg, q_end, smem, R);
+  else gemv_q_body<4, NQ, ND>(a, sd, tile, q_beg, q_end, smem, R);
   const int nqs = q_end - q_beg;
   float* red = reinterpret_cast<float*>(smem + (size_t)nqs * 1088 + (size_t)ND * nqs * 128);
   int* flag = reinterpret_cast<int*>(red + 2 * NW * 16);
-  const float o = 0.5f * (float)((1 << bits) - 1);
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
-    float v = __builtin_fmaf(R[d], 16777216.0f, -o * Ro[d]);
+    float v = R[d] * 16777216.0f;  // 2^24
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     if (lane < 16) red[(d * NW + wave) * 16 + lane] = v;
