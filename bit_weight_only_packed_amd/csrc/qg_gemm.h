@@ -27,11 +27,6 @@
 
 namespace qg {
 
-template <int N> __device__ __forceinline__ float dpp_row_ror(float v) {
-  return __builtin_bit_cast(float,
-                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF, false));
-}
-
 struct GmArgs {
   WSet w[2];                 // w[1]: up matrix of the fused gate/up pass
   const uint16_t* x;         // [M][K] fp16

@@ -76,6 +76,11 @@ __device__ __forceinline__ float dpp_xor1(float v) {
 __device__ __forceinline__ float dpp_xor2(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
 }
+// value of lane (l & ~15) | ((l + N) & 15): rotation within each row of 16 lanes
+template <int N> __device__ __forceinline__ float dpp_row_ror(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF, false));
+}
 
 // scale of group g, column j of tile t (scales layout [tile][G4][16][4])
 __device__ __forceinline__ size_t scale_index(int t, int G4, int g, int j) {
@@ -178,6 +183,26 @@ __device__ __forceinline__ float sum_partials(const float* p, size_t stride, int
   }
   return t;
 }
+// Fixed-point accumulation words (the order-independent alternative to the
+// partials above): each contributor adds (round(v * 2^28) << 6) + 1 (v clamped
+// to +-2^23) to a 64-bit word with one integer atomic.  Integer addition is
+// exact and commutative, so the total does not depend on the order of arrival,
+// and the low 6 bits count the arrivals (at most 63 contributors per word).
+constexpr int FX_FRAC = 28;  // fraction bits
+
+__device__ __forceinline__ unsigned long long fx_word(float v) {
+  const float vc = fminf(fmaxf(v, -8388608.0f), 8388608.0f);  // +-2^23
+  return ((unsigned long long)__double2ll_rn((double)vc * (double)(1ll << FX_FRAC)) << 6) + 1ull;
+}
+
+__device__ __forceinline__ unsigned long long fx_add(unsigned long long* w, unsigned long long v) {
+  return __hip_atomic_fetch_add(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float fx_value(unsigned long long total) {
+  return (float)((double)((long long)total >> 6) * (1.0 / (double)(1ll << FX_FRAC)));
+}
+
 __device__ __forceinline__ bool splitk_last(int* counter, int S, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();

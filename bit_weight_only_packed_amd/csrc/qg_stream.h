@@ -34,7 +34,6 @@
 
 namespace qg {
 
-constexpr int SK_FRAC = 28;  // fraction bits of the fixed-point column words
 constexpr int SK_UPW = 8;    // at most this many quads per wave
 constexpr int SK_PD = 3;     // units whose loads are in flight while one is computed
 
@@ -79,20 +78,6 @@ __device__ __forceinline__ void sk_load(const SkPtrs<ND>& p, SkUnit<B, ND>& c, i
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes[d] + (size_t)uc * (B * 256), live ? B * 1024u : 0u);
     buffer_quad<B>(rc, (uint32_t)lane, 0, c.cw[d]);
   }
-}
-
-// fixed-point increment of a column word for partial v (and one arrival)
-__device__ __forceinline__ unsigned long long sk_word(float v) {
-  const float vc = fminf(fmaxf(v, -8388608.0f), 8388608.0f);  // +-2^23
-  return ((unsigned long long)__double2ll_rn((double)vc * (double)(1ll << SK_FRAC)) << 6) + 1ull;
-}
-
-__device__ __forceinline__ unsigned long long sk_atomic_add(unsigned long long* w, unsigned long long v) {
-  return __hip_atomic_fetch_add(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float sk_value(unsigned long long total) {
-  return (float)((double)((long long)total >> 6) * (1.0 / (double)(1ll << SK_FRAC)));
 }
 
 // The SK_PD register sets of a wave's load pipeline over one width segment.
@@ -183,23 +168,23 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, SkPipe<B, ND>& pp, int u
     return;
   }
   unsigned long long* wg = a.acc + pc;
-  const unsigned long long ag = sk_word(v[0]);
+  const unsigned long long ag = fx_word(v[0]);
   if constexpr (ND == 2) {
     unsigned long long* wu = a.acc + 16 * (size_t)a.total_tiles + pc;
-    const unsigned long long ou = sk_atomic_add(wu, sk_word(v[1]));
+    const unsigned long long ou = fx_add(wu, fx_word(v[1]));
     __builtin_amdgcn_s_waitcnt(0);  // the up word holds this wave's part before gate counts it
     __asm__ volatile("" ::"v"(ou));
-    const unsigned long long og = sk_atomic_add(wg, ag);
+    const unsigned long long og = fx_add(wg, ag);
     if ((int)(og & 63ull) == nch - 1) {
-      const unsigned long long tu = sk_atomic_add(wu, 0ull);
-      a.y[n] = f2h(silu_mul(sk_value(og + ag), sk_value(tu)));
+      const unsigned long long tu = fx_add(wu, 0ull);
+      a.y[n] = f2h(silu_mul(fx_value(og + ag), fx_value(tu)));
       __hip_atomic_store(wg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(wu, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
-    const unsigned long long og = sk_atomic_add(wg, ag);
+    const unsigned long long og = fx_add(wg, ag);
     if ((int)(og & 63ull) == nch - 1) {
-      a.y[n] = f2h(sk_value(og + ag));
+      a.y[n] = f2h(fx_value(og + ag));
       __hip_atomic_store(wg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

@@ -16,6 +16,7 @@
 #include "qg_trellis.h"
 #include "qg_stream.h"
 #include "qg_gemm.h"
+#include "qg_xs.h"
 
 using namespace qg;
 
@@ -77,7 +78,7 @@ struct qg_plan {
   size_t partial_floats = 0;
   int* counters = nullptr;        // device [total_tiles] split-K arrival counters, zero between runs
   uint16_t* hbuf = nullptr;       // device [max_M][N] fp16, MLP intermediate
-  unsigned long long* acc64 = nullptr;  // device [2][16*total_tiles] M = 1 column words, zero between runs
+  unsigned long long* acc64 = nullptr;  // device [2][max_M][16*total_tiles] fixed-point output words, zero between runs
   int cus = 0;                    // compute units of the device
   Launch over[3];
   // trellis
@@ -92,12 +93,18 @@ struct qg_plan {
 namespace {
 
 // ---- launch planning --------------------------------------------------------
-// verify GEMM: the per-wave-K-split kernel (k_gemm_mfma), measured faster on
-// the decode shapes; QG_GEMM=v2 selects the shared-x kernel (k_gemm_v2)
-bool gemm_v2_on() {
+// verify GEMM kernels: the per-wave-K-split kernel (k_gemm_mfma), the shared-x
+// kernel (k_gemm_v2) and the x-in-LDS streaming kernel (k_gemm_xs).
+// QG_GEMM=mfma (or v1)|v2|xs forces one.
+enum { GEMM_MFMA = 0, GEMM_V2 = 1, GEMM_XS = 2 };
+int gemm_forced() {
   const char* f = getenv("QG_GEMM");
-  return f && !strcmp(f, "v2");
+  if (f && (!strcmp(f, "mfma") || !strcmp(f, "v1"))) return GEMM_MFMA;
+  if (f && !strcmp(f, "v2")) return GEMM_V2;
+  if (f && !strcmp(f, "xs")) return GEMM_XS;
+  return -1;
 }
+bool gemm_v2_on() { return gemm_forced() == GEMM_V2; }
 
 // Launch shapes of the per-wave-K-split GEMM measured best on MI355X (sweeps
 // over tiles per wave T, waves per workgroup NW and K slices S) for the
@@ -197,6 +204,104 @@ Launch choose(const qg_plan* h, int M, bool dual = false, int force_v2 = -1) {
   return L;
 }
 
+constexpr size_t kLdsMax = 163840;  // LDS per workgroup on gfx950
+constexpr int kXsNQ = 8;            // longest K slice of the x-in-LDS GEMM, in quads
+// slice lengths the x-in-LDS GEMM is compiled for (the smallest >= the longest slice runs)
+constexpr int kXsNQs[] = {4, 5, 8};
+
+// Plan of the x-in-LDS GEMM (k_gemm_xs): K slices S (as few as let the slice of
+// x fit LDS), T tiles per group (2; 1 gate + 1 up tile in the fused pass) and
+// GPW tile groups per workgroup, one per wave, at most 8 (about one workgroup
+// per LDS slot of the chip).  Overrides for M > 1 (qgemv_set_launch): tiles (or
+// waves) = tile groups per workgroup, splits = K slices (at least as many as
+// the LDS needs).
+struct XsPlan {
+  int MT = 1, T = 2, S = 1, nq = 1, NQ = 4, GPW = 1, NW = 1;
+  bool fx = false;  // K slices meet in fixed-point words (else fp32 partials)
+  size_t lds = 0;
+  unsigned grid = 0;
+  int wg_prefix[MAX_SEG + 1] = {};
+  int tg_prefix[MAX_SEG + 1] = {};
+};
+
+int xs_nq_compiled(int nq) {
+  for (int v : kXsNQs)
+    if (v >= nq) return v;
+  return 0;
+}
+
+// Launch shapes of the x-in-LDS GEMM measured best on MI355X (sweeps over tile
+// groups per workgroup GPW and K slices S) for the 27B-class layer shapes; the
+// generic rule in xs_plan covers other shapes.
+struct XsTuned {
+  int N, K, mcls, GPW, S;
+};
+constexpr XsTuned kXsTuned[] = {
+    {5120, 5120, 1, 4, 6},  {5120, 5120, 2, 4, 6},    // q, o
+    {1024, 5120, 1, 2, 10}, {1024, 5120, 2, 4, 10},   // k, v
+    {17408, 5120, 1, 4, 3}, {17408, 5120, 2, 8, 3},   // gate, up
+    {5120, 17408, 1, 4, 6}, {5120, 17408, 2, 8, 9},   // down
+};
+
+// Verify GEMM kind: the x-in-LDS kernel, except where the per-wave-K-split
+// kernel measured faster (k/v at more than 16 rows); QG_GEMM forces one.
+int gemm_kind(const qg_plan* h, int M) {
+  const int f = gemm_forced();
+  if (f >= 0) return f;
+  if (h->N == 1024 && h->K == 5120 && M > 16) return GEMM_MFMA;
+  return GEMM_XS;
+}
+
+XsPlan xs_plan(const qg_plan* h, int M, bool dual) {
+  XsPlan p;
+  Launch L = h->over[mclass(M)];
+  if (L.T <= 0 && L.NW <= 0 && L.S <= 0 && !dual)
+    for (const XsTuned& t : kXsTuned)
+      if (t.N == h->N && t.K == h->K && t.mcls == mclass(M)) {
+        L.T = t.GPW;
+        L.S = t.S;
+      }
+  p.MT = M <= 16 ? 1 : 2;
+  p.T = dual ? 1 : 2;
+  const size_t col_cap = 4096;  // room for the run's column map
+  // fewest K slices whose x slice fits LDS (at the compiled slice length)
+  p.S = std::max(1, std::min(h->G4, L.S > 0 ? L.S : 1));
+  for (;; ++p.S) {
+    p.nq = (h->G4 + p.S - 1) / p.S;
+    p.NQ = xs_nq_compiled(p.nq);
+    if (p.NQ > 0 && xs_x_bytes(M, p.NQ) + xs_sum_bytes(p.MT, p.NQ) + col_cap <= kLdsMax) break;
+    if (p.S >= h->G4) break;
+  }
+  int tg = 0;
+  for (const auto& sg : h->segs) tg += (sg.tiles + p.T - 1) / p.T;
+  const size_t lds0 = xs_x_bytes(M, p.NQ) + xs_sum_bytes(p.MT, p.NQ) + 1024;
+  const int per_cu = std::max(1, (int)(kLdsMax / lds0));
+  const int64_t want = (int64_t)std::max(1, h->cus) * per_cu;  // workgroups that fit at once
+  if (L.T > 0) p.GPW = L.T;
+  else if (L.NW > 0) p.GPW = L.NW;
+  else p.GPW = (int)std::max<int64_t>(1, ((int64_t)tg * p.S + want - 1) / want);
+  p.GPW = std::max(1, std::min(p.GPW, 8));  // one tile group per wave
+  p.NW = p.GPW;
+  int wgs = 0, tgs = 0;
+  for (int i = 0; i < (int)h->segs.size(); ++i) {
+    const int ng = (h->segs[i].tiles + p.T - 1) / p.T;
+    p.wg_prefix[i] = wgs;
+    p.tg_prefix[i] = tgs;
+    wgs += (ng + p.GPW - 1) / p.GPW;
+    tgs += ng;
+  }
+  for (int i = (int)h->segs.size(); i <= MAX_SEG; ++i) {
+    p.wg_prefix[i] = wgs;
+    p.tg_prefix[i] = tgs;
+  }
+  p.grid = (unsigned)wgs * (unsigned)p.S;
+  p.lds = xs_lds_bytes(M, p.MT, p.NQ, p.GPW, p.T);
+  // fixed-point words while the atomics stay few (measured: they win at 8 rows
+  // on every decode shape, the partials at 32 rows on the widest); <= 63 slices
+  p.fx = p.S > 1 && p.S <= 63 && (int64_t)M * 16 * h->total_tiles * p.S <= (int64_t)1 << 20;
+  return p;
+}
+
 size_t partial_need(const qg_plan* h, int S, int M) {
   return S <= 1 ? 0 : (size_t)2 * S * M * (size_t)(16 * h->total_tiles);
 }
@@ -207,10 +312,14 @@ qg_status ensure_workspace(qg_plan* h) {
     const int Mc = c == 0 ? 1 : (c == 1 ? 16 : 32);
     if (Mc > h->max_M && c > 0 && (c == 1 ? 2 : 17) > h->max_M) continue;
     const int Mm = std::min(Mc, h->max_M);
-    // either verify GEMM may be selected at run time: size for both
+    // any verify GEMM may be selected at run time: size for all
     for (int v2 = 0; v2 < 2; ++v2) {
       need = std::max(need, partial_need(h, choose(h, Mm, false, v2).S, Mm));
       need = std::max(need, partial_need(h, choose(h, Mm, true, v2).S, Mm));
+    }
+    for (int Mx = 2; Mx <= Mm; ++Mx) {
+      need = std::max(need, partial_need(h, xs_plan(h, Mx, false).S, Mx));
+      need = std::max(need, partial_need(h, xs_plan(h, Mx, true).S, Mx));
     }
   }
   if (need > h->partial_floats) {
@@ -487,8 +596,6 @@ void launch_mfma(const RunArgs& a, int T, int NW, size_t lds, unsigned grid, boo
 
 // M = 1 stream-K GEMV.  Launch knobs (M = 1 overrides): NW waves per workgroup
 // (default 8), S workgroups per compute unit (default 2).
-constexpr size_t kLdsMax = 163840;  // LDS per workgroup on gfx950
-
 bool sk_fits(const qg_plan* h) { return h->G4 <= 63 && sk_lds_bytes(h->G4, (int)h->segs.size()) <= kLdsMax; }
 
 template <int BF, int ND>
@@ -631,11 +738,110 @@ qg_status run_gemm_v2(const qg_plan* h, const qg_plan* h2, const uint16_t* x, in
   return QG_OK;
 }
 
+template <int T, int MT, bool DUAL, int BF>
+hipError_t xs_allow_lds() {
+  hipError_t e = hipSuccess;
+  const hipError_t r[] = {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_xs<T, MT, DUAL, BF, 4>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_xs<T, MT, DUAL, BF, 5>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_xs<T, MT, DUAL, BF, 8>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax)};
+  for (hipError_t x : r)
+    if (x != hipSuccess) e = x;
+  return e;
+}
+
+template <int BF>
+hipError_t xs_allow_lds_b() {
+  hipError_t e = hipSuccess;
+  const hipError_t r[] = {xs_allow_lds<2, 1, false, BF>(), xs_allow_lds<2, 2, false, BF>(),
+                          xs_allow_lds<1, 1, true, BF>(), xs_allow_lds<1, 2, true, BF>()};
+  for (hipError_t x : r)
+    if (x != hipSuccess) e = x;
+  return e;
+}
+
+// let the x-in-LDS GEMM take up to the whole LDS of a compute unit
+hipError_t xs_allow_lds_all() {
+  hipError_t e = hipSuccess;
+  const hipError_t r[] = {xs_allow_lds_b<0>(), xs_allow_lds_b<2>(), xs_allow_lds_b<3>(), xs_allow_lds_b<4>()};
+  for (hipError_t x : r)
+    if (x != hipSuccess) e = x;
+  return e;
+}
+
+template <int MT, bool DUAL, int NQ>
+void launch_xs_q(const XsArgs& a, const XsPlan& p, int bf, hipStream_t st) {
+  constexpr int T = DUAL ? 1 : 2;
+  switch (bf) {
+    case 2: k_gemm_xs<T, MT, DUAL, 2, NQ><<<p.grid, p.NW * 64, p.lds, st>>>(a); break;
+    case 3: k_gemm_xs<T, MT, DUAL, 3, NQ><<<p.grid, p.NW * 64, p.lds, st>>>(a); break;
+    case 4: k_gemm_xs<T, MT, DUAL, 4, NQ><<<p.grid, p.NW * 64, p.lds, st>>>(a); break;
+    default: k_gemm_xs<T, MT, DUAL, 0, NQ><<<p.grid, p.NW * 64, p.lds, st>>>(a); break;
+  }
+}
+
+template <int MT, bool DUAL>
+void launch_xs_b(const XsArgs& a, const XsPlan& p, int bf, hipStream_t st) {
+  if (p.NQ == 4) launch_xs_q<MT, DUAL, 4>(a, p, bf, st);
+  else if (p.NQ == 5) launch_xs_q<MT, DUAL, 5>(a, p, bf, st);
+  else launch_xs_q<MT, DUAL, 8>(a, p, bf, st);
+}
+
+qg_status run_gemm_xs(const qg_plan* h, const qg_plan* h2, const uint16_t* x, int M, uint16_t* y, int ldy,
+                      hipStream_t st) {
+  const bool dual = h2 != nullptr;
+  const XsPlan p = xs_plan(h, M, dual);
+  if (p.NQ == 0 || p.lds > kLdsMax)
+    return fail(QG_ERR_INVALID_ARG, "x slice of %d quads at M=%d does not fit LDS", p.nq, M);
+  if (p.S > 1 && partial_need(h, p.S, M) > h->partial_floats)
+    return fail(QG_ERR_INVALID_ARG, "workspace too small for %d K-slices at M=%d", p.S, M);
+  if (p.tg_prefix[MAX_SEG] > std::max(1, h->total_tiles)) return fail(QG_ERR_INVALID_ARG, "more tile groups than counters");
+  XsArgs a{};
+  a.w[0] = wset_of(h);
+  if (h2) a.w[1] = wset_of(h2);
+  a.x = x;
+  a.y = y;
+  a.partial = h->partial;
+  a.counters = h->counters;
+  a.acc = p.fx ? h->acc64 : nullptr;
+  a.M = M;
+  a.K = h->K;
+  a.G = h->G;
+  a.G4 = h->G4;
+  a.ldy = ldy;
+  a.NP = 16 * h->total_tiles;
+  a.S = p.S;
+  a.GPW = p.GPW;
+  for (int i = 0; i <= MAX_SEG; ++i) {
+    a.wg_prefix[i] = p.wg_prefix[i];
+    a.tg_prefix[i] = p.tg_prefix[i];
+  }
+  const int bf = h->segs.size() == 1 ? h->segs[0].bits : 0;
+  if (p.MT == 1) {
+    if (dual) launch_xs_b<1, true>(a, p, bf, st);
+    else launch_xs_b<1, false>(a, p, bf, st);
+  } else {
+    if (dual) launch_xs_b<2, true>(a, p, bf, st);
+    else launch_xs_b<2, false>(a, p, bf, st);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  if (getenv("QG_DEBUG_SYNC")) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel failed: %s", hipGetErrorString(e));
+  }
+  return QG_OK;
+}
+
 // one GEMV/GEMM over a uniform handle (or the fused gate+up pair when h2 != NULL)
 qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, int M, uint16_t* y, int ldy,
                       hipStream_t st) {
   const bool dual = h2 != nullptr;
   if (M == 1 && use_sk(h)) return run_sk(h, h2, x, y, st);
+  if (M > 1 && gemm_kind(h, M) == GEMM_XS) return run_gemm_xs(h, h2, x, M, y, ldy, st);
   if (M > 1 && gemm_v2_on()) return run_gemm_v2(h, h2, x, M, y, ldy, st);
   Launch L = choose(h, M, dual);
   int T = L.T;
@@ -764,8 +970,12 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
     s = fail(QG_ERR_OOM, "staging allocation failed");
   if (s == QG_OK && h->format == QG_FMT_UNIFORM && sk_allow_lds_all() != hipSuccess)
     s = fail(QG_ERR_DEVICE, "cannot raise the LDS limit of the M = 1 kernels");
+  if (s == QG_OK && h->format == QG_FMT_UNIFORM && xs_allow_lds_all() != hipSuccess)
+    s = fail(QG_ERR_DEVICE, "cannot raise the LDS limit of the verify GEMM");
   if (s == QG_OK && h->format == QG_FMT_UNIFORM) {
-    const size_t nw = (size_t)2 * 16 * h->total_tiles;
+    // fixed-point output words [2][max_M][16 * total_tiles]: the M = 1 GEMV uses
+    // the first 2 * 16 * total_tiles, the x-in-LDS GEMM rows 0 .. M - 1
+    const size_t nw = (size_t)2 * h->max_M * 16 * h->total_tiles;
     if (hipMalloc(&h->acc64, nw * sizeof(unsigned long long)) != hipSuccess)
       s = fail(QG_ERR_OOM, "column-word allocation failed");
     else if (hipMemsetAsync(h->acc64, 0, nw * sizeof(unsigned long long), st) != hipSuccess)

@@ -1,8 +1,9 @@
 """Every kernel variant the dispatcher can pick, forced through its switch on
 shapes small enough for a full oracle comparison: the two M = 1 GEMVs (per-group
-and per-tile-run) and the two verify GEMMs (per-wave K split and shared-x), on
-one and several code widths, single matrices and the fused gate/up pass, each
-checked against the oracle and for bit-identical repeats."""
+and per-tile-run) and the three verify GEMMs (per-wave K split, shared-x and
+x-in-LDS streaming), on one and several code widths, single matrices and the
+fused gate/up pass, each checked against the oracle and for bit-identical
+repeats."""
 from __future__ import annotations
 
 import numpy as np
@@ -13,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 import oracle as O  # noqa: E402
 import qg_synth as S  # noqa: E402
-from _gpu import TOL, Uniform, dev_f16, say, sha  # noqa: E402
+from _gpu import TOL, Uniform, dev_f16, dev_words, run_np, say, sha  # noqa: E402
 import bit_weight_only_packed_amd as Q  # noqa: E402
 
 
@@ -56,7 +57,7 @@ def test_m1_kernels_mixed_widths(kernel, monkeypatch):
     _check(u.lin, x, u.ref(x))
 
 
-@pytest.mark.parametrize("gemm", ["v1", "v2"])
+@pytest.mark.parametrize("gemm", ["v1", "v2", "xs"])
 @pytest.mark.parametrize("M", [2, 8, 16, 17, 32])
 @pytest.mark.parametrize("N,K,bits", [(48, 384, 3), (272, 1280, 2), (528, 2560, 4)])
 def test_gemm_kernels(gemm, M, N, K, bits, monkeypatch):
@@ -67,7 +68,7 @@ def test_gemm_kernels(gemm, M, N, K, bits, monkeypatch):
     _check(u.lin, x, u.ref(x))
 
 
-@pytest.mark.parametrize("gemm", ["v1", "v2"])
+@pytest.mark.parametrize("gemm", ["v1", "v2", "xs"])
 @pytest.mark.parametrize("M,tiles,waves,splits", [(8, 1, 4, 1), (8, 2, 8, 3), (32, 1, 8, 5), (32, 4, 4, 2),
                                                   (32, 2, 8, 1), (17, 2, 4, 4)])
 def test_gemm_launch_shapes(gemm, M, tiles, waves, splits, monkeypatch):
@@ -80,7 +81,7 @@ def test_gemm_launch_shapes(gemm, M, tiles, waves, splits, monkeypatch):
     _check(u.lin, x, u.ref(x))
 
 
-@pytest.mark.parametrize("kernel,gemm", [("pergroup", "v1"), ("runs", "v2")])
+@pytest.mark.parametrize("kernel,gemm", [("pergroup", "v1"), ("runs", "v2"), ("runs", "xs")])
 @pytest.mark.parametrize("M", [1, 8, 32])
 def test_fused_mlp_variants(kernel, gemm, M, monkeypatch):
     monkeypatch.setenv("QG_M1_KERNEL", kernel)
@@ -101,3 +102,39 @@ def test_fused_mlp_variants(kernel, gemm, M, monkeypatch):
     err = O.normwise_rel_err(o1.cpu().numpy().astype(np.float64), O.mlp(x, g.w(), up.w(), d.w()))
     say("mlp err", err)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("M", [3, 16, 32])
+def test_gemm_xs_mixed_widths(M, monkeypatch):
+    """x-in-LDS GEMM over three width segments (its workgroups never span two)."""
+    monkeypatch.setenv("QG_GEMM", "xs")
+    N, K = 464, 4608
+    cb = S.column_bits(N, 0.2, 4, cfg_id=95)
+    cb[3::13] = 2
+    say("gemm xs mixed", M)
+    u = Uniform(N, K, col_bits=cb, cfg_id=95)
+    x = S.activations(M, K, cfg_id=95, tensor_id=300 + M)
+    _check(u.lin, x, u.ref(x))
+
+
+@pytest.mark.parametrize("M", [8, 32])
+@pytest.mark.parametrize("N,K", [(5120, 5120), (1024, 5120), (17408, 5120), (5120, 17408)])
+def test_gemm_xs_decode_shapes(M, N, K, monkeypatch):
+    """x-in-LDS GEMM at the full 27B-class layer shapes, in its own launch
+    choice, on sampled output columns the oracle computes one by one."""
+    monkeypatch.setenv("QG_GEMM", "xs")
+    say("gemm xs full", M, N, K)
+    w = S.uniform_code_words(N, K, 3, cfg_id=96)
+    sc = S.scales(N, K, cfg_id=96)
+    lin = Q.QLinear(dev_words(w), dev_f16(sc), K, N, bits=3, max_M=32)
+    x = S.activations(M, K, cfg_id=96, tensor_id=300 + M)
+    y1 = run_np(lin, x)
+    y2 = run_np(lin, x)
+    assert np.array_equal(y1, y2)
+    rng = np.random.default_rng([96, N])
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N), rng.choice(N, size=64, replace=False)]))
+    r = O.gemv_uniform_rows(x, w, sc, N, K, 3, rows)
+    err = O.normwise_rel_err(y1[:, rows], r)
+    say("err", err)
+    assert err <= TOL, err
+    lin.close()
