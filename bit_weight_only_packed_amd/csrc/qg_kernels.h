@@ -76,7 +76,7 @@ __device__ __forceinline__ float dpp_xor1(float v) {
 __device__ __forceinline__ float dpp_xor2(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
 }
-// value of lane (l & ~15) | ((l + N) & 15): rotation within each row of 16 lanes
+// value of lane (l & ~15) | ((l - N) & 15): rotation right within each row of 16 lanes
 template <int N> __device__ __forceinline__ float dpp_row_ror(float v) {
   return __builtin_bit_cast(float,
                             __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF, false));

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(512) void k_gemv_sk(SkArgs a) {
     SkPipe<BF, ND> pp;
     sk_prime<BF, ND>(pp, sd, v0, v1, lane);
     sk_x_store<BF>(xr, a.G4, reinterpret_cast<uint4*>(smem), const_cast<float*>(xsl), true);
-    __syncthreads();
+    lds_barrier();  // orders the staged x only (a full barrier would wait for the primed code loads)
     sk_run<BF, ND, true>(a, pp, v0, v1, sd[0].tile0, reinterpret_cast<const uint4*>(smem), xsl, lane);
   } else {
     for (int si = 0; si < nseg; ++si) {
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(512) void k_gemv_sk(SkArgs a) {
       else if (s0.bits == 3) sk_x_store<3>(xr, a.G4, xl, xs, si == 0);
       else sk_x_store<4>(xr, a.G4, xl, xs, si == 0);
     }
-    __syncthreads();
+    lds_barrier();
     for (int si = 0; si < nseg; ++si) {
       SegDev sd[2];
       sd[0] = pick(a.w[0], si);
