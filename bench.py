@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--profile-gate", type=int, default=0, metavar="REPS",
                    help="profiling mode: REPS graph replays of the M=1 GEMV on the 5120x17408 shape over all "
                         "weight copies, then a 256 MiB device copy (the counter calibration), then exit")
+    p.add_argument("--profile-rows", type=int, default=1, choices=(1, 8, 16, 32), metavar="M",
+                   help="rows of the profiled gate/up product (1 = the GEMV, more = the verify GEMM)")
     return p.parse_args()
 
 
@@ -144,11 +146,12 @@ def main():
     if args.profile_gate:
         # the dominant kernel alone, launched exactly as the per-shape timing below
         # launches it, then a plain copy of known size for the HBM counter scale
-        out1 = ys[1][:, : shapes[4]["N"]]
+        Mp = args.profile_rows
+        out1 = ys[Mp][:, : shapes[4]["N"]]
 
         def gate_all():
             for r in range(R):
-                lins[r][4].run(xk[(1, 5120)], out=out1)
+                lins[r][4].run(xk[(Mp, 5120)], out=out1)
         g = capture(gate_all)
         time_graph(g, 2)
         t = time_graph(g, args.profile_gate)
@@ -159,7 +162,8 @@ def main():
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"profile": "gemv M=1 5120x17408", "launches": args.profile_gate * R,
+        print(json.dumps({"profile": f"{'gemv' if Mp == 1 else 'verify gemm'} M={Mp} 5120x17408",
+                          "launches": args.profile_gate * R,
                           "graph_us_per_launch": round(us, 3), "copy_bytes_each_way": 4 * n,
                           "src_hash": src_hash()}), flush=True)
         return
