@@ -140,7 +140,9 @@ __global__ __launch_bounds__(256) void k_fwht(const uint16_t* __restrict__ x, ui
 }
 
 // ---------------------------------------------------------------------------
-// GEMV (MT = 0, M = 1) and GEMM (MT = 1: M <= 16, MT = 2: M <= 32).
+// GEMV (MT = 0, M = 1) and GEMM (MT = 1: M <= 16, MT = 2: M <= 32); the GEMM
+// form is selected only with QG_TRELLIS=stream (the banded kernel below is
+// the default for more than one row).
 //
 // One workgroup per compute unit holds the codebook in LDS for the whole launch.
 // The RB * G units are split into W equal contiguous ranges in row-block-major
@@ -370,6 +372,196 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
       if (u + i >= hi) break;
       step(c[i], u + i);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Banded GEMM for 2..32 rows.  In the stream-K kernel above every unit loads
+// its own 16 rows of x, one row per lane: 64 different cache lines per load
+// instruction, which the address pipeline takes one by one.  Here a workgroup
+// owns a band of NW row blocks (one per wave) and a K slice of groups, and its
+// waves walk the slice's groups in step: the x fragment of each group (MR rows
+// x 128 k) is copied once per workgroup into LDS beside the codebook (dword
+// buffer-to-LDS copies, each wave its share of the rows, XB slots in rotation,
+// PD groups ahead), and every wave reads its A fragments from there.  A wave
+// keeps one row block's sums over the whole slice; K slices meet as in the
+// stream-K kernel (fixed slots, arrival counter, sums in slot order).
+// ---------------------------------------------------------------------------
+template <int MT> struct TbShape {
+  static constexpr int NW = MT == 2 ? 8 : 16;  // waves = row blocks per workgroup
+  static constexpr int PD = MT == 2 ? 2 : 3;   // groups whose copies and code loads are in flight
+  static constexpr int XB = PD + 1;            // x slots
+  static constexpr int MR = 16 * MT;           // rows of an x slot
+  static constexpr int XRD = MR / NW;          // 256-byte row copies per wave per group
+  static constexpr int SLOT = MR * 256;        // bytes per x slot
+};
+
+struct TbArgs {
+  const uint32_t* codes;   // [U][64][3]
+  const uint16_t* scales;  // [U][16]
+  const uint16_t* cb;      // [65536] fp16
+  const uint16_t* x;       // [M][K] fp16, rotated
+  uint16_t* y;             // [M][N] fp16
+  float* partial;          // [RB][maxseg][M][16] (S > 1)
+  int* counters;           // [RB], zero between launches
+  int M, K, N, G, RB, maxseg, S;
+};
+
+// 4 bytes per lane from a buffer into LDS at lds + 4 * lane (lds wave-uniform),
+// as assembly so the compiler does not make LDS reads wait for it (the kernel
+// orders it with explicit waits and barriers); no register receives data.
+__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t voff) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const __attribute__((address_space(3))) char*)(lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+
+template <int N> __device__ __forceinline__ void tb_vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+struct TbUnit {
+  u3_t z;      // code words
+  uint32_t s;  // this lane's scale (fp16 in the low half)
+};
+
+template <int MT>
+__global__ __launch_bounds__(64 * TbShape<MT>::NW) void k_trellis_band(TbArgs a) {
+  using TS = TbShape<MT>;
+  constexpr int PD = TS::PD, XB = TS::XB, MR = TS::MR, XRD = TS::XRD, NW = TS::NW, SLOT = TS::SLOT;
+  // static LDS: the codebook at address 0 (the gathers use the decoded byte
+  // address as is), then the x slots
+  __shared__ __align__(16) char smem[TR_CB_BYTES + XB * SLOT];
+  char* const xl = smem + TR_CB_BYTES;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = a.S;
+  const int s = blockIdx.x % S, band = blockIdx.x / S;
+  const int rb = band * NW + wave;
+  const bool mine = rb < a.RB;
+  const int g0 = (int)((int64_t)s * a.G / S), g1 = (int)((int64_t)(s + 1) * a.G / S), ng = g1 - g0;
+  // codebook -> LDS (1 KiB per wave instruction)
+  {
+    const __amdgpu_buffer_rsrc_t rcb = make_rsrc(uniform_ptr(a.cb), TR_CB_BYTES);
+    for (int ci = wave; ci < TR_CB_BYTES / 1024; ci += NW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rcb, (__attribute__((address_space(3))) void*)(smem + (size_t)ci * 1024),
+                                               16, (uint32_t)(ci * 1024 + lane * 16), 0, 0, 0);
+  }
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(a.x), (uint32_t)a.M * a.K * 2u);
+  // step i's x fragment (group g0 + i) into slot sl: rows m = XRD * wave + r, the
+  // 16-byte chunk p of a row at position p ^ (m & 15); rows past M and steps past
+  // the slice read zeros
+  auto copy_x = [&](int i, int sl) {
+    const int g = g0 + i;
+#pragma unroll
+    for (int r = 0; r < XRD; ++r) {
+      const int m = XRD * wave + r;
+      const int pc = (lane >> 2) ^ (m & 15);
+      const uint32_t voff =
+          (m < a.M && i < ng) ? (uint32_t)(((size_t)m * a.K + (size_t)g * 128 + pc * 8 + (lane & 3) * 2) * 2) : 0xFFFFFFF0u;
+      lds_copy4(rx, xl + (size_t)sl * SLOT + (size_t)m * 256, voff);
+    }
+  };
+  auto load_unit = [&](TbUnit& t, int i) {
+    const bool live = mine && i < ng;
+    const int64_t u = live ? (int64_t)rb * a.G + g0 + i : 0;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(uniform_ptr(a.codes) + u * 192, live ? 768u : 0u);
+    t.z = __builtin_amdgcn_raw_buffer_load_b96(rc, (uint32_t)lane * 12u, 0, 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(a.scales) + u * 16, live ? 32u : 0u);
+    t.s = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(lane & 14) * 2u, 0, 0);
+  };
+  TbUnit c[PD];
+#pragma unroll
+  for (int i = 0; i < PD; ++i) {
+    copy_x(i, i);
+    load_unit(c[i], i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const char* cbl = smem;
+  const int kq = lane >> 4, m16 = lane & 15;
+  int xa[MT][4];  // this lane's A-fragment offsets within a slot
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * mt + m16;
+      xa[mt][v] = row * 256 + (((4 * kq + v) ^ (row & 15)) * 16);
+    }
+  f4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  int sl = 0;  // slot of the step being computed
+  // one step: wait for this wave's copies of the step's x, meet the other waves
+  // (the fragment is then whole, and the slot the next copy overwrites is
+  // free), compute the unit, then issue the copies and loads PD steps ahead.
+  // Every step issues the same loads (past the slice through empty ranges), so
+  // the wait count is the same in every step.
+  auto step = [&](TbUnit& cu, int i) {
+    tb_vm_wait<2 + (PD - 1) * (XRD + 2)>();
+    lds_barrier();
+    if (mine && i < ng) {
+      const uint32_t z2 = cu.z.x, z1 = cu.z.y, z0 = cu.z.z;
+      const uint32_t nz2 = tr_from_next_row_lane(z2), nz1 = tr_from_next_row_lane(z1);
+      uint32_t addr[32];
+      tr_addrs(z2, z1, z0, nz2, nz1, addr);
+      uint32_t pr[16];
+      tr_gather(cbl, addr, pr);
+      const float sc = h2f((uint16_t)((lane & 1) ? (cu.s >> 16) : (cu.s & 0xFFFFu)));
+      const char* xs = xl + (size_t)sl * SLOT;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          cg = mfma16(*reinterpret_cast<const h8_t*>(xs + xa[mt][v]), as_h8(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]),
+                      cg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(sc, cg[e], acc[mt][e]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int sl_next = sl == 0 ? XB - 1 : sl - 1;  // (i + PD) % XB = (i - 1) % XB
+    copy_x(i + PD, sl_next);
+    load_unit(cu, i + PD);
+    __builtin_amdgcn_sched_barrier(0);
+    sl = sl + 1 == XB ? 0 : sl + 1;
+  };
+  for (int u = 0; u < ng; u += PD) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) step(c[i], u + i);
+  }
+  if (!mine) return;
+  // ---- results of this row block over the slice
+  const int n = lane & 15, mq = lane >> 4;
+  if (S == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * mt + 4 * mq + e;
+        if (m < a.M) a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(acc[mt][e]);
+      }
+    return;
+  }
+  float* base = a.partial + ((size_t)rb * a.maxseg) * a.M * 16;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * mt + 4 * mq + e;
+      if (m < a.M) st_partial(base + ((size_t)s * a.M + m) * 16 + n, acc[mt][e]);
+    }
+  if (tr_arrive_last(a.counters + rb, S, lane)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * mt + 4 * mq + e;
+        if (m >= a.M) continue;
+        const float t = sum_partials(base + (size_t)m * 16 + n, (size_t)a.M * 16, S, s, acc[mt][e]);
+        a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(t);
+      }
   }
 }
 

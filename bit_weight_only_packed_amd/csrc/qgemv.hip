@@ -395,6 +395,19 @@ int tr_maxseg_of(int RB, int G, int64_t U, int W) {
   return mx;
 }
 
+// Banded trellis GEMM: K slices so that the bands x slices workgroups (one per
+// compute unit: the codebook fills its LDS) cover the chip in one round.
+int tb_slices(const qg_plan* h, int nw) {
+  const int RB = h->N / 16, bands = (RB + nw - 1) / nw;
+  return std::max(1, std::min(h->G, std::max(1, h->cus) / bands));
+}
+
+bool trellis_banded_on(int M) {
+  const char* f = getenv("QG_TRELLIS");
+  if (f && !strcmp(f, "stream")) return false;
+  return M > 1;
+}
+
 qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   const int N = d->N, K = d->K, G = K / QG_GROUP, RB = N / 16;
   int cus = 0;
@@ -411,6 +424,7 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
     const int W = (int)std::min<int64_t>((int64_t)h->tr_grid * nw, h->tr_units);
     h->tr_maxseg = std::max(h->tr_maxseg, tr_maxseg_of(RB, G, h->tr_units, W));
   }
+  h->tr_maxseg = std::max({h->tr_maxseg, tb_slices(h, TbShape<1>::NW), tb_slices(h, TbShape<2>::NW)});
   const size_t ncode = (size_t)h->tr_units * 64 * 3;
   QG_HIP(hipMalloc(&h->tcodes, ncode * sizeof(uint32_t)));
   QG_HIP(hipMalloc(&h->tscales, (size_t)h->tr_units * 16 * sizeof(uint16_t)));
@@ -434,6 +448,36 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
     const int waves = M * h->G;
     k_fwht<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, h->xrot, M, h->K);
     xr = h->xrot;
+  }
+  if (trellis_banded_on(M)) {
+    const bool m32 = M > 16;
+    const int nw = m32 ? TbShape<2>::NW : TbShape<1>::NW;
+    TbArgs b{};
+    b.codes = h->tcodes;
+    b.scales = h->tscales;
+    b.cb = h->codebook;
+    b.x = xr;
+    b.y = y;
+    b.partial = h->partial;
+    b.counters = h->counters;
+    b.M = M;
+    b.K = h->K;
+    b.N = h->N;
+    b.G = h->G;
+    b.RB = h->N / 16;
+    b.maxseg = h->tr_maxseg;
+    b.S = tb_slices(h, nw);
+    if (b.S > h->tr_maxseg) return fail(QG_ERR_INVALID_ARG, "%d K slices exceed the workspace's %d", b.S, h->tr_maxseg);
+    const unsigned grid = (unsigned)(((b.RB + nw - 1) / nw) * b.S);
+    if (m32) k_trellis_band<2><<<grid, 64 * nw, 0, st>>>(b);
+    else k_trellis_band<1><<<grid, 64 * nw, 0, st>>>(b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    if (getenv("QG_DEBUG_SYNC")) {
+      e = hipStreamSynchronize(st);
+      if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel failed: %s", hipGetErrorString(e));
+    }
+    return QG_OK;
   }
   TrArgs a{};
   a.codes = h->tcodes;

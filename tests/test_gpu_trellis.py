@@ -2,8 +2,8 @@
 codebook, Walsh-Hadamard-rotated activations) against the CPU oracle, through
 the C ABI: bit-exact states and dequantised weights from the checking entry
 points, outputs within the normwise 2e-3 budget at M = 1 (vector-ALU GEMV)
-and M = 2..32 (matrix-core GEMM), pre-rotated input, bit-identical repeats and
-sampled columns of the 27B-class shapes."""
+and M = 2..32 (matrix-core GEMMs: banded, the default, and stream-K), pre-rotated
+input, bit-identical repeats and sampled columns of the 27B-class shapes."""
 from __future__ import annotations
 
 import numpy as np
@@ -111,3 +111,24 @@ def test_full_size_sampled_columns(K, N, M, codebook):
     say("full size err", err)
     assert err <= TOL, err
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("kernel", ["stream", "banded"])
+@pytest.mark.parametrize("M", [2, 8, 17, 32])
+@pytest.mark.parametrize("N,K", [(48, 384), (400, 2560)])
+def test_gemm_kernels_both(kernel, M, N, K, codebook, monkeypatch):
+    """Both trellis GEMMs, forced: the stream-K kernel (every unit loads its own
+    rows of x) and the banded one (x fragments shared through LDS, K slices)."""
+    if kernel == "stream":
+        monkeypatch.setenv("QG_TRELLIS", "stream")
+    else:
+        monkeypatch.delenv("QG_TRELLIS", raising=False)
+    say("trellis gemm", kernel, M, N, K)
+    t = Trellis(N, K, codebook, cfg_id=86)
+    x = S.activations(M, K, cfg_id=86, tensor_id=500 + M)
+    y1 = _run(t.lin, x)
+    y2 = _run(t.lin, x)
+    assert np.array_equal(y1, y2)
+    err = O.normwise_rel_err(y1, t.ref(x))
+    say("err", err)
+    assert err <= TOL, err
