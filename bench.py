@@ -245,6 +245,47 @@ def main():
     result["layer_set_ratio_M8_M1"] = round(layer_us[8] / layer_us[1], 3)
     log("layer set us", result["layer_set_us"])
 
+    # ---------------- the same layer set with sibling projections fused ----------------
+    # q|k|v and gate|up read the same input: each pair of siblings runs as one
+    # launch over its rows stacked (N = 7168 and 34816) -- the same weights, bytes
+    # and outputs in 4 launches instead of 7
+    if not args.quick:
+        groups = [(0, 1, 2), (3,), (4, 5), (6,)]
+        cw = [(S.uniform_code_words(sh["N"], sh["K"], 3, cfg_id=S.CFG_DECODE, tensor_id=S.T_CODES + 10 * i),
+               S.scales(sh["N"], sh["K"], cfg_id=S.CFG_DECODE, tensor_id=S.T_SCALE + 10 * i))
+              for i, sh in enumerate(shapes)]
+        fmats = []
+        for grp in groups:
+            w = np.concatenate([cw[i][0].reshape(shapes[i]["N"], -1) for i in grp], axis=0)
+            sc = np.concatenate([cw[i][1] for i in grp], axis=0)
+            fmats.append((dw(w), df16(sc), sum(shapes[i]["N"] for i in grp), shapes[grp[0]]["K"]))
+        del cw
+        flins = [[Q.QLinear(w, sc, K, N, bits=3, max_M=32) for (w, sc, N, K) in fmats] for _ in range(R)]
+        del fmats
+        fys = {M: [torch.empty((M, N), dtype=torch.float16, device=dev) for N in (7168, 5120, 34816, 5120)]
+               for M in (1, 8, 16, 32)}
+        fks = (5120, 5120, 5120, 17408)
+        fused_us = {}
+        for M in (1, 8, 16, 32):
+            def fstep(M=M):
+                for r in range(R):
+                    for j in range(4):
+                        flins[r][j].run(xk[(M, fks[j])], out=fys[M][j])
+            g = capture(fstep)
+            time_graph(g, 1)
+            fused_us[M] = time_graph(g, max(1, reps_t // 2)) / (max(1, reps_t // 2) * R) * 1e6
+        result["layer_set_fused"] = {
+            "launches": 4, "note": "q|k|v and gate|up as one launch each over stacked rows",
+            **{f"us_M{M}": round(v, 3) for M, v in fused_us.items()},
+            "GBs_M1": round(per_copy / fused_us[1] / 1e3, 1),
+            "pct_8TBs_M1": round(100 * per_copy / fused_us[1] / 1e3 / HBM_PEAK_GBS, 2),
+            "ratio_M32_M1": round(fused_us[32] / fused_us[1], 3)}
+        log("fused layer set", result["layer_set_fused"])
+        for row in flins:
+            for l in row:
+                l.close()
+        del flins
+
     # ---------------- roofline entry: M=1 GEMV on the gate/up shape ----------------
     gate_us = per_shape["gateup"]["us_M1"]
     gate_bytes = per_shape["gateup"]["weight_bytes"]

@@ -241,6 +241,8 @@ constexpr XsTuned kXsTuned[] = {
     {1024, 5120, 1, 2, 10}, {1024, 5120, 2, 4, 10},   // k, v
     {17408, 5120, 1, 4, 3}, {17408, 5120, 2, 8, 3},   // gate, up
     {5120, 17408, 1, 4, 6}, {5120, 17408, 2, 8, 9},   // down
+    {7168, 5120, 1, 4, 4},  {7168, 5120, 2, 4, 4},    // q | k | v stacked
+    {34816, 5120, 1, 4, 3}, {34816, 5120, 2, 8, 3},   // gate | up stacked
 };
 
 // Verify GEMM kind: the x-in-LDS kernel, except where the per-wave-K-split
