@@ -45,13 +45,12 @@ struct SkArgs {
   int K, N, G, G4, total_tiles;
   int nch;                     // waves per tile
   int64_t U;                   // total_tiles * G4
+  int wg_prefix[MAX_SEG + 1];  // several widths: workgroups before each width segment
 };
 
-// LDS: per width segment a scaled copy of x (4 * G4 * 64 uint32 = 4*G4 groups of
-// 128 fp16), then the quarter sums (4 * G4 * 4 floats)
-__host__ __device__ constexpr size_t sk_lds_bytes(int G4, int nseg) {
-  return (size_t)nseg * G4 * 1024 + (size_t)G4 * 64;
-}
+// LDS: a copy of x scaled for the workgroup's width (4 * G4 * 64 uint32 =
+// 4*G4 groups of 128 fp16), then the quarter sums (4 * G4 * 4 floats)
+__host__ __device__ constexpr size_t sk_lds_bytes(int G4) { return (size_t)G4 * 1024 + (size_t)G4 * 64; }
 
 template <int B, int ND>
 struct SkUnit {
@@ -247,66 +246,51 @@ __device__ __forceinline__ void sk_seg_range(const SegDev& sd, int G4, int64_t l
 }
 
 // BF: the single code width of the matrices, or 0 (several width segments)
+// one workgroup's runs over a segment of width B: x loads, then the first
+// units' loads, then x staged (scaled for width B), then the runs
+template <int B, int ND, bool ONE>
+__device__ __forceinline__ void sk_body(const SkArgs& a, const SegDev (&sd)[2], int64_t lo, int64_t hi, char* smem,
+                                        int lane) {
+  const float* xsl = reinterpret_cast<const float*>(smem + (size_t)a.G4 * 1024);
+  uint4 xr[SK_XR];
+  sk_x_load(a.x, a.G, a.G4, xr);
+  int v0, v1;
+  sk_seg_range(sd[0], a.G4, lo, hi, v0, v1);
+  SkPipe<B, ND> pp;
+  sk_prime<B, ND>(pp, sd, v0, v1, lane);
+  sk_x_store<B>(xr, a.G4, reinterpret_cast<uint4*>(smem), const_cast<float*>(xsl), true);
+  lds_barrier();  // orders the staged x only (a full barrier would wait for the primed code loads)
+  sk_run<B, ND, ONE>(a, pp, v0, v1, sd[0].tile0, reinterpret_cast<const uint4*>(smem), xsl, lane);
+}
+
+// BF: the single code width of the matrices, or 0 (several width segments:
+// every workgroup then belongs to one segment, so it stages x for one width)
 template <int BF, int ND>
 __global__ __launch_bounds__(512) void k_gemv_sk(SkArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63;
   const int NW = blockDim.x >> 6;
-  const int gw = blockIdx.x * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // wave gw takes run gw % nch of tile gw / nch (global units [lo, hi)); waves
-  // past the last tile only help stage x
-  const int tgw = gw / a.nch, ch = gw - tgw * a.nch;
-  const bool live = tgw < a.total_tiles;
-  const int64_t lo = live ? (int64_t)tgw * a.G4 + ch * a.G4 / a.nch : a.U;
-  const int64_t hi = live ? (int64_t)tgw * a.G4 + (ch + 1) * a.G4 / a.nch : a.U;
-  const int nseg = a.w[0].nseg;
-  const float* xsl = reinterpret_cast<const float*>(smem + (size_t)nseg * a.G4 * 1024);
-  uint4 xr[SK_XR];
-  sk_x_load(a.x, a.G, a.G4, xr);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int si = 0;
+  if (BF == 0)
+    while (si + 1 < a.w[0].nseg && (int)blockIdx.x >= a.wg_prefix[si + 1]) ++si;
+  SegDev sd[2];
+  sd[0] = BF == 0 ? pick(a.w[0], si) : a.w[0].seg[0];
+  sd[1] = ND == 2 ? (BF == 0 ? pick(a.w[1], si) : a.w[1].seg[0]) : sd[0];
+  // wave gw (of the segment) takes run gw % nch of the segment's tile gw / nch
+  // (global units [lo, hi)); waves past the segment's last tile only help stage x
+  const int gw = ((int)blockIdx.x - (BF == 0 ? a.wg_prefix[si] : 0)) * NW + wave;
+  const int tl = gw / a.nch, ch = gw - tl * a.nch;
+  const bool live = tl < sd[0].tiles;
+  const int64_t t0 = (int64_t)(sd[0].tile0 + tl) * a.G4;
+  const int64_t lo = live ? t0 + ch * a.G4 / a.nch : a.U;
+  const int64_t hi = live ? t0 + (ch + 1) * a.G4 / a.nch : a.U;
   if constexpr (BF != 0) {
-    // one width: the first units' loads go out right behind the x loads
-    SegDev sd[2];
-    sd[0] = a.w[0].seg[0];
-    sd[1] = ND == 2 ? a.w[1].seg[0] : sd[0];
-    int v0, v1;
-    sk_seg_range(sd[0], a.G4, lo, hi, v0, v1);
-    SkPipe<BF, ND> pp;
-    sk_prime<BF, ND>(pp, sd, v0, v1, lane);
-    sk_x_store<BF>(xr, a.G4, reinterpret_cast<uint4*>(smem), const_cast<float*>(xsl), true);
-    lds_barrier();  // orders the staged x only (a full barrier would wait for the primed code loads)
-    sk_run<BF, ND, true>(a, pp, v0, v1, sd[0].tile0, reinterpret_cast<const uint4*>(smem), xsl, lane);
+    sk_body<BF, ND, true>(a, sd, lo, hi, smem, lane);
   } else {
-    for (int si = 0; si < nseg; ++si) {
-      const SegDev s0 = pick(a.w[0], si);
-      uint4* xl = reinterpret_cast<uint4*>(smem + (size_t)si * a.G4 * 1024);
-      float* xs = const_cast<float*>(xsl);
-      if (s0.bits == 2) sk_x_store<2>(xr, a.G4, xl, xs, si == 0);
-      else if (s0.bits == 3) sk_x_store<3>(xr, a.G4, xl, xs, si == 0);
-      else sk_x_store<4>(xr, a.G4, xl, xs, si == 0);
-    }
-    lds_barrier();
-    for (int si = 0; si < nseg; ++si) {
-      SegDev sd[2];
-      sd[0] = pick(a.w[0], si);
-      sd[1] = ND == 2 ? pick(a.w[1], si) : sd[0];
-      int v0, v1;
-      sk_seg_range(sd[0], a.G4, lo, hi, v0, v1);
-      if (v0 >= v1) continue;
-      const uint4* xl = reinterpret_cast<const uint4*>(smem + (size_t)si * a.G4 * 1024);
-      if (sd[0].bits == 2) {
-        SkPipe<2, ND> pp;
-        sk_prime<2, ND>(pp, sd, v0, v1, lane);
-        sk_run<2, ND, false>(a, pp, v0, v1, sd[0].tile0, xl, xsl, lane);
-      } else if (sd[0].bits == 3) {
-        SkPipe<3, ND> pp;
-        sk_prime<3, ND>(pp, sd, v0, v1, lane);
-        sk_run<3, ND, false>(a, pp, v0, v1, sd[0].tile0, xl, xsl, lane);
-      } else {
-        SkPipe<4, ND> pp;
-        sk_prime<4, ND>(pp, sd, v0, v1, lane);
-        sk_run<4, ND, false>(a, pp, v0, v1, sd[0].tile0, xl, xsl, lane);
-      }
-    }
+    if (sd[0].bits == 2) sk_body<2, ND, false>(a, sd, lo, hi, smem, lane);
+    else if (sd[0].bits == 3) sk_body<3, ND, false>(a, sd, lo, hi, smem, lane);
+    else sk_body<4, ND, false>(a, sd, lo, hi, smem, lane);
   }
 }
 

@@ -642,7 +642,7 @@ void launch_mfma(const RunArgs& a, int T, int NW, size_t lds, unsigned grid, boo
 
 // M = 1 stream-K GEMV.  Launch knobs (M = 1 overrides): NW waves per workgroup
 // (default 8), S workgroups per compute unit (default 2).
-bool sk_fits(const qg_plan* h) { return h->G4 <= 63 && sk_lds_bytes(h->G4, (int)h->segs.size()) <= kLdsMax; }
+bool sk_fits(const qg_plan* h) { return h->G4 <= 63 && sk_lds_bytes(h->G4) <= kLdsMax; }
 
 template <int BF, int ND>
 hipError_t sk_allow_lds() {
@@ -687,8 +687,15 @@ qg_status run_sk(const qg_plan* h, const qg_plan* h2, const uint16_t* x, uint16_
   a.total_tiles = h->total_tiles;
   a.U = (int64_t)h->total_tiles * h->G4;
   a.nch = nch;  // waves per tile
-  const unsigned grid = (unsigned)(((int64_t)h->total_tiles * a.nch + NW - 1) / NW);
-  const size_t lds = sk_lds_bytes(h->G4, (int)h->segs.size());
+  // one segment per workgroup: each segment's waves are rounded up to whole workgroups
+  int wgs = 0;
+  for (int i = 0; i < (int)h->segs.size(); ++i) {
+    a.wg_prefix[i] = wgs;
+    wgs += (int)(((int64_t)h->segs[i].tiles * nch + NW - 1) / NW);
+  }
+  for (int i = (int)h->segs.size(); i <= MAX_SEG; ++i) a.wg_prefix[i] = wgs;
+  const unsigned grid = (unsigned)wgs;
+  const size_t lds = sk_lds_bytes(h->G4);
   const int bf = h->segs.size() == 1 ? h->segs[0].bits : 0;
   switch (bf) {
     case 2: launch_sk_b<2>(a, h2 != nullptr, grid, NW, lds, st); break;
