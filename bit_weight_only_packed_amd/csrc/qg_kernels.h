@@ -50,6 +50,8 @@ struct RunArgs {
   int* counters;           // one arrival counter per tile set (all zero between runs)
   int M, K, G, G4, ldy, NP;
   int T, S;                // tiles per workgroup, K slices across workgroups
+  int pair;                // M = 1 gate/up pass with one matrix per workgroup (w[0], w[1])
+  unsigned long long* xw;  // pair pass, one K slice: per padded column hand-over word, zero between runs
   int ts_prefix[MAX_SEG + 1];  // prefix sums of tile-sets per segment
 };
 
@@ -352,14 +354,24 @@ __global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.S, G4 = a.G4;
-  const int s = blockIdx.x % S, tsg = blockIdx.x / S;
+  // paired gate/up pass (DUAL false, a.pair set): the two matrices are taken as
+  // extra K slices, slice index dm * S + s for matrix dm; the last arrival of a
+  // tile set sums each matrix's slices and applies SiLU(g) * u
+  const int P = (!DUAL && a.pair) ? 2 : 1;
+  const int SP = S * P;
+  const int sx = blockIdx.x % SP, tsg = blockIdx.x / SP;
+  const int dm = sx / S, s = sx - dm * S;
   // single-width handles have one segment: no data-dependent argument loads
   int si = 0;
   if (BF == 0)
     while (si + 1 < a.w[0].nseg && tsg >= a.ts_prefix[si + 1]) ++si;
   SegDev sd[2];
-  sd[0] = BF == 0 ? pick(a.w[0], si) : a.w[0].seg[0];
-  sd[1] = DUAL ? (BF == 0 ? pick(a.w[1], si) : a.w[1].seg[0]) : sd[0];
+  {
+    const SegDev s0 = BF == 0 ? pick(a.w[0], si) : a.w[0].seg[0];
+    const SegDev s1 = BF == 0 ? pick(a.w[1], si) : a.w[1].seg[0];
+    sd[0] = (P == 2 && dm == 1) ? s1 : s0;
+    sd[1] = DUAL ? s1 : sd[0];
+  }
   const int tile = BF == 0 ? tsg - a.ts_prefix[si] : tsg;
   const int q_beg = (int)((int64_t)s * G4 / S), q_end = (int)((int64_t)(s + 1) * G4 / S);
   float R[2] = {0.0f, 0.0f};
@@ -386,24 +398,47 @@ __global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
     for (int d = 0; d < ND; ++d)
       for (int w = 0; w < NW; ++w) v[d] += red[(d * NW + w) * 16 + tid];
   }
-  if (S > 1) {
+  if (P == 2 && S == 1) {
+    // one K slice: the two workgroups of a tile meet in a per-column word.
+    // Each swaps in (matrix + 1) << 32 | its fp32 bits; the one that gets a
+    // non-zero word back holds both values, writes SiLU(g) * u and re-arms the
+    // word.  One round trip per workgroup, and the result does not depend on
+    // which matrix arrives first.
     if (mine) {
-#pragma unroll
-      for (int d = 0; d < ND; ++d) st_partial(a.partial + (size_t)(d * S + s) * a.NP + pc, v[d]);
+      const unsigned long long w = ((unsigned long long)(dm + 1) << 32) | __float_as_uint(v[0]);
+      const unsigned long long o = __hip_atomic_exchange(a.xw + pc, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (o != 0ull) {
+        const float other = __uint_as_float((uint32_t)o);
+        const float g = dm == 0 ? v[0] : other, u = dm == 0 ? other : v[0];
+        __hip_atomic_store(a.xw + pc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int n = a.w[0].col_map[pc];
+        if (n >= 0) a.y[n] = f2h(silu_mul(g, u));
+      }
     }
-    if (!splitk_last(a.counters + tsg, S, flag)) return;
+    return;
+  }
+  if (SP > 1) {
+    // partials [matrix][slice][NP]; the arriving workgroup adds its own value
+    // in its slot of the fixed order instead of reading it back
     if (mine) {
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        float acc = 0.0f;
-        acc = sum_partials(a.partial + (size_t)(d * S) * a.NP + pc, (size_t)a.NP, S);
-        v[d] = acc;
+      for (int d = 0; d < ND; ++d) st_partial(a.partial + (size_t)((d + dm) * S + s) * a.NP + pc, v[d]);
+    }
+    if (!splitk_last(a.counters + tsg, SP, flag)) return;
+    if (mine) {
+      const float own = v[0];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        if (d == 1 && ND == 1 && P == 1) break;
+        const bool is_own = P == 1 || d == dm;
+        v[d] = sum_partials(a.partial + (size_t)(d * S) * a.NP + pc, (size_t)a.NP, S, is_own ? s : -1,
+                            P == 1 ? v[d] : own);
       }
     }
   }
   if (mine) {
     const int n = a.w[0].col_map[pc];
-    if (n >= 0) a.y[n] = f2h(DUAL ? silu_mul(v[0], v[1]) : v[0]);
+    if (n >= 0) a.y[n] = f2h((DUAL || P == 2) ? silu_mul(v[0], v[1]) : v[0]);
   }
 }
 

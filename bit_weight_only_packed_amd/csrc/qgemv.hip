@@ -308,12 +308,22 @@ size_t partial_need(const qg_plan* h, int S, int M) {
   return S <= 1 ? 0 : (size_t)2 * S * M * (size_t)(16 * h->total_tiles);
 }
 
+// M = 1 fused gate/up pass with one matrix per workgroup (partials of both
+// matrices, even with one K slice); QG_M1_PAIR=0 keeps both matrices in each
+// workgroup
+bool m1_pair_on() {
+  const char* f = getenv("QG_M1_PAIR");
+  return !(f && !strcmp(f, "0"));
+}
+size_t pair_need(const qg_plan* h, int S) { return (size_t)2 * std::max(S, 1) * (size_t)(16 * h->total_tiles); }
+
 qg_status ensure_workspace(qg_plan* h) {
   size_t need = 0;
   for (int c = 0; c < 3; ++c) {
     const int Mc = c == 0 ? 1 : (c == 1 ? 16 : 32);
     if (Mc > h->max_M && c > 0 && (c == 1 ? 2 : 17) > h->max_M) continue;
     const int Mm = std::min(Mc, h->max_M);
+    if (c == 0) need = std::max(need, pair_need(h, choose(h, 1, true).S));
     // any verify GEMM may be selected at run time: size for all
     for (int v2 = 0; v2 < 2; ++v2) {
       need = std::max(need, partial_need(h, choose(h, Mm, false, v2).S, Mm));
@@ -927,6 +937,10 @@ qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, in
   a.NP = 16 * h->total_tiles;
   a.T = T;
   a.S = S;
+  const bool pair = M == 1 && dual && m1_pair_on();
+  a.pair = pair ? 1 : 0;
+  a.xw = h->acc64;
+  if (pair && S == 1 && !h->acc64) return fail(QG_ERR_INVALID_ARG, "no hand-over words for the paired gate/up pass");
   int pre = 0;
   for (int i = 0; i < (int)h->segs.size(); ++i) {
     a.ts_prefix[i] = pre;
@@ -935,22 +949,25 @@ qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, in
   for (int i = (int)h->segs.size(); i <= MAX_SEG; ++i) a.ts_prefix[i] = pre;
   if (S > 1 && partial_need(h, S, M) > h->partial_floats)
     return fail(QG_ERR_INVALID_ARG, "workspace too small for %d K-slices at M=%d", S, M);
-  const unsigned grid = (unsigned)pre * (unsigned)S;
+  if (pair && pair_need(h, S) > h->partial_floats)
+    return fail(QG_ERR_INVALID_ARG, "workspace too small for the paired gate/up pass");
+  const unsigned grid = (unsigned)pre * (unsigned)S * (pair ? 2u : 1u);
   if (M == 1) {
     const int nqs = (h->G4 + S - 1) / S;
     const int NQ = L.NQ;
     if (NQ <= 0 || (int64_t)NQ * NW < nqs)
       return fail(QG_ERR_INVALID_ARG, "%d waves cannot cover %d quads per slice with the compiled quad counts", NW, nqs);
-    if (dual && NQ > 2) return fail(QG_ERR_INVALID_ARG, "fused gate/up needs at most 2 quads per wave");
-    const size_t lds = m1_lds_bytes(nqs, dual ? 2 : 1, NW);
+    if (dual && !pair && NQ > 2) return fail(QG_ERR_INVALID_ARG, "fused gate/up needs at most 2 quads per wave");
+    const bool kd = dual && !pair;  // both matrices in each workgroup
+    const size_t lds = m1_lds_bytes(nqs, kd ? 2 : 1, NW);
     if (lds > 65536) return fail(QG_ERR_INVALID_ARG, "K slice of %d quads does not fit LDS: use more splits", nqs);
     switch (NQ) {
-      case 1: launch_q<1>(a, NW, lds, grid, dual, bf, st); break;
-      case 2: launch_q<2>(a, NW, lds, grid, dual, bf, st); break;
-      case 3: launch_q<3>(a, NW, lds, grid, dual, bf, st); break;
-      case 4: launch_q<4>(a, NW, lds, grid, dual, bf, st); break;
-      case 5: launch_q<5>(a, NW, lds, grid, dual, bf, st); break;
-      default: launch_q<5>(a, NW, lds, grid, dual, bf, st); break;
+      case 1: launch_q<1>(a, NW, lds, grid, kd, bf, st); break;
+      case 2: launch_q<2>(a, NW, lds, grid, kd, bf, st); break;
+      case 3: launch_q<3>(a, NW, lds, grid, kd, bf, st); break;
+      case 4: launch_q<4>(a, NW, lds, grid, kd, bf, st); break;
+      case 5: launch_q<5>(a, NW, lds, grid, kd, bf, st); break;
+      default: launch_q<5>(a, NW, lds, grid, kd, bf, st); break;
     }
   } else {
     const int MT = M <= 16 ? 1 : 2;
@@ -1027,7 +1044,8 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
     s = fail(QG_ERR_DEVICE, "cannot raise the LDS limit of the verify GEMM");
   if (s == QG_OK && h->format == QG_FMT_UNIFORM) {
     // fixed-point output words [2][max_M][16 * total_tiles]: the M = 1 GEMV uses
-    // the first 2 * 16 * total_tiles, the x-in-LDS GEMM rows 0 .. M - 1
+    // the first 2 * 16 * total_tiles (the paired gate/up pass the first
+    // 16 * total_tiles as hand-over words), the x-in-LDS GEMM rows 0 .. M - 1
     const size_t nw = (size_t)2 * h->max_M * 16 * h->total_tiles;
     if (hipMalloc(&h->acc64, nw * sizeof(unsigned long long)) != hipSuccess)
       s = fail(QG_ERR_OOM, "column-word allocation failed");

@@ -104,6 +104,38 @@ def test_fused_mlp_variants(kernel, gemm, M, monkeypatch):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("mixed", [False, True])
+@pytest.mark.parametrize("splits", [0, 2, 3])
+def test_m1_gate_up_pair_matches_dual(mixed, splits, monkeypatch):
+    """M = 1 per-group gate/up pass: one matrix per workgroup (paired arrival)
+    gives the same bits as both matrices in one workgroup, with and without
+    K slices, and matches the oracle."""
+    monkeypatch.setenv("QG_M1_KERNEL", "pergroup")
+    H, I = 2048, 1408
+    cb_gu = S.column_bits(I, 0.2, 4, cfg_id=96, tensor_id=S.T_MASK) if mixed else None
+    kw = dict(col_bits=cb_gu) if mixed else dict(bits=3)
+    g = Uniform(I, H, cfg_id=96, tid=0, **kw)
+    up = Uniform(I, H, cfg_id=96, tid=1, **kw)
+    d = Uniform(H, I, bits=4, cfg_id=96, tid=2)
+    if splits:
+        g.lin.set_launch(1, 1, 0, splits)
+    say("mlp pair", mixed, splits)
+    x = S.activations(1, H, cfg_id=96, tensor_id=401)
+    xd = dev_f16(x)
+    outs = {}
+    for pair in ("0", "1"):
+        monkeypatch.setenv("QG_M1_PAIR", pair)
+        o1 = Q.mlp(g.lin, up.lin, d.lin, xd)
+        o2 = Q.mlp(g.lin, up.lin, d.lin, xd)
+        torch.cuda.synchronize()
+        assert sha(o1) == sha(o2)
+        outs[pair] = o1
+    assert sha(outs["0"]) == sha(outs["1"])
+    err = O.normwise_rel_err(outs["1"].cpu().numpy().astype(np.float64), O.mlp(x, g.w(), up.w(), d.w()))
+    say("mlp pair err", err)
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("M", [3, 16, 32])
 def test_gemm_xs_mixed_widths(M, monkeypatch):
     """x-in-LDS GEMM over three width segments (its workgroups never span two)."""
