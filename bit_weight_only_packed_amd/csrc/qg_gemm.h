@@ -245,7 +245,7 @@ __global__ __launch_bounds__(512) void k_gemm_v2(GmArgs a) {
   for (int t = 0; t < T; ++t) {
     if (tl0 + t >= sd[0].tiles) continue;
     const int pc = 16 * (sd[0].tile0 + tl0 + t) + j;
-    const int n = a.w[0].col_map[pc];
+    const int n = BF != 0 ? pc : a.w[0].col_map[pc];  // one width: no padding, identity
     if (n < 0) continue;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)

@@ -374,6 +374,11 @@ __global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
   }
   const int tile = BF == 0 ? tsg - a.ts_prefix[si] : tsg;
   const int q_beg = (int)((int64_t)s * G4 / S), q_end = (int)((int64_t)(s + 1) * G4 / S);
+  const int pc = 16 * (sd[0].tile0 + tile) + (tid & 15);
+  // output column: the padded column itself for one width (no padding then);
+  // with several widths looked up here, so the lookup is not on the tail
+  int n_out = pc;
+  if (BF == 0) n_out = tid < 16 ? a.w[0].col_map[pc] : -1;
   float R[2] = {0.0f, 0.0f};
   const int bits = sd[0].bits;
   if (BF == 2 || (BF == 0 && bits == 2)) gemv_q_body<2, NQ, ND>(a, sd, tile, q_beg, q_end, smem, R);
@@ -391,7 +396,6 @@ __global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
   }
   __syncthreads();
   const bool mine = tid < 16;
-  const int pc = 16 * (sd[0].tile0 + tile) + (tid & 15);
   float v[2] = {0.0f, 0.0f};
   if (mine) {
 #pragma unroll
@@ -411,8 +415,7 @@ __global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
         const float other = __uint_as_float((uint32_t)o);
         const float g = dm == 0 ? v[0] : other, u = dm == 0 ? other : v[0];
         __hip_atomic_store(a.xw + pc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int n = a.w[0].col_map[pc];
-        if (n >= 0) a.y[n] = f2h(silu_mul(g, u));
+        if (n_out >= 0) a.y[n_out] = f2h(silu_mul(g, u));
       }
     }
     return;
@@ -436,10 +439,7 @@ __global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
       }
     }
   }
-  if (mine) {
-    const int n = a.w[0].col_map[pc];
-    if (n >= 0) a.y[n] = f2h((DUAL || P == 2) ? silu_mul(v[0], v[1]) : v[0]);
-  }
+  if (mine && n_out >= 0) a.y[n_out] = f2h((DUAL || P == 2) ? silu_mul(v[0], v[1]) : v[0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(RunArgs a) {
         v[d] = red[(size_t)(d * NW) * PER * 64 + idx];
       }
     }
-    const int n = a.w[0].col_map[pc];
+    const int n = BF != 0 ? pc : a.w[0].col_map[pc];  // one width: no padding, identity
     if (n >= 0) a.y[(size_t)row * a.ldy + n] = f2h(DUAL ? silu_mul(v[0], v[1]) : v[0]);
   }
 }
