@@ -259,7 +259,10 @@ __device__ __forceinline__ void gemv_q_body(const RunArgs& a, const SegDev (&sd)
   __builtin_amdgcn_sched_barrier(0);  // keep the prologue loads ahead of the code loads
   // ---- code loads: NQ quads per wave, buffer range = the wave's real quads
   const int qw0 = q_beg + wave * NQ;
-  const int nvalid = max(0, min(NQ, q_end - qw0));
+  // wave-uniform, and kept in a scalar register: the compiler computes the clamp
+  // with a vector instruction, and a descriptor built from a vector register
+  // is taken as divergent (each load wrapped in a per-lane descriptor loop)
+  const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(NQ, q_end - qw0)));
   uint32_t cw[ND][NQ][4 * B];
 #pragma unroll
   for (int d = 0; d < ND; ++d) {

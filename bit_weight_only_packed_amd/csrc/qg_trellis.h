@@ -153,7 +153,10 @@ __global__ __launch_bounds__(256) void k_fwht(const uint16_t* __restrict__ x, ui
 // in fixed slots (slot = wave - first wave of the row block); the wave that
 // completes a row block (device-scope arrival counter) adds the slots in slot
 // order and stores the fp16 result.  The slot order fixes every rounding, so
-// repeated runs are bit-identical.
+// repeated runs are bit-identical.  At M = 1, where at most 63 waves share a
+// row block, the partials go into fixed-point output words instead (see
+// fx_word): one atomic round trip instead of the store, the count and the
+// reads, and a sum that does not depend on the order of arrival.
 // ---------------------------------------------------------------------------
 struct TrArgs {
   const uint32_t* codes;   // [U][64][3]
@@ -163,6 +166,7 @@ struct TrArgs {
   uint16_t* y;             // [M][N] fp16
   float* partial;          // [RB][maxseg][M][16]
   int* counters;           // [RB], zero between launches
+  unsigned long long* acc; // M = 1: [N] fixed-point output words (zero between launches), or NULL: partials
   int M, K, N, G, RB, maxseg, W;
   int64_t U;
 };
@@ -194,15 +198,18 @@ __device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT>& t, int64_t 
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + uc * 16, uu * 32u);
   t.s = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(lane & 14) * 2u, 0, 0);
   if (lane & 1) t.s >>= 16;
+  // one descriptor over all of x (wave-uniform, so no per-lane descriptor
+  // loop); the lane's row and quarter go into the offset, and a row past M
+  // (or a dead unit) takes an offset past the range: zeros, no memory access
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(a.x), (uint32_t)a.M * (uint32_t)a.K * 2u);
 #pragma unroll
   for (int mt = 0; mt < TrUnit<MT>::XR; ++mt) {
     const int m = MT == 0 ? 0 : 16 * mt + (lane & 15);
     const bool ok = live && m < a.M;
-    const __amdgpu_buffer_rsrc_t rx =
-        make_rsrc(a.x + (size_t)(ok ? m : 0) * a.K + (size_t)g * 128 + 32 * kq, ok ? 64u : 0u);
+    const uint32_t off = ok ? (uint32_t)(((size_t)m * a.K + (size_t)g * 128 + 32 * kq) * 2) : 0x80000000u;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const u4_t q = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)v * 16u, 0, 0);
+      const u4_t q = __builtin_amdgcn_raw_buffer_load_b128(rx, off + (uint32_t)v * 16u, 0, 0);
       t.xv[mt][v] = make_uint4(q.x, q.y, q.z, q.w);
     }
   }
@@ -323,6 +330,18 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
       v += __shfl_xor(v, 32);
       if (nseg == 1) {
         if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(v);
+      } else if (a.acc) {
+        // fixed-point words (see fx_word): one round trip; the arrival that
+        // completes the count stores the result and re-arms the word
+        if (lane < 16) {
+          unsigned long long* w = a.acc + (size_t)rb * 16 + n;
+          const unsigned long long mine = fx_word(v);
+          const unsigned long long before = fx_add(w, mine);
+          if ((int)(before & 63ull) == nseg - 1) {
+            a.y[(size_t)rb * 16 + n] = f2h(fx_value(before + mine));
+            __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
       } else {
         if (lane < 16) st_partial(base + (size_t)seg * 16 + n, v);
         if (tr_arrive_last(a.counters + rb, nseg, lane)) {

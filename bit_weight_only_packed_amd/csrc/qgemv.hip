@@ -88,6 +88,7 @@ struct qg_plan {
   uint16_t* xrot = nullptr;       // device [max_M][K] fp16, rotated activations
   int64_t tr_units = 0;           // (N/16) * G
   int tr_grid = 0, tr_maxseg = 0;
+  bool tr_fx = false;             // M = 1 trellis GEMV hands row blocks on through fixed-point words (acc64)
 };
 
 namespace {
@@ -436,6 +437,9 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
     const int W = (int)std::min<int64_t>((int64_t)h->tr_grid * nw, h->tr_units);
     h->tr_maxseg = std::max(h->tr_maxseg, tr_maxseg_of(RB, G, h->tr_units, W));
   }
+  // the M = 1 GEMV's row blocks meet in fixed-point words (one round trip)
+  // where at most 63 waves share one (the words count arrivals in 6 bits)
+  h->tr_fx = tr_maxseg_of(RB, G, h->tr_units, (int)std::min<int64_t>((int64_t)h->tr_grid * 16, h->tr_units)) <= 63;
   h->tr_maxseg = std::max({h->tr_maxseg, tb_slices(h, TbShape<1>::NW), tb_slices(h, TbShape<2>::NW)});
   const size_t ncode = (size_t)h->tr_units * 64 * 3;
   QG_HIP(hipMalloc(&h->tcodes, ncode * sizeof(uint32_t)));
@@ -445,6 +449,11 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   const size_t nf = (size_t)RB * h->tr_maxseg * h->max_M * 16;
   QG_HIP(hipMalloc(&h->partial, nf * sizeof(float)));
   h->partial_floats = nf;
+  if (h->tr_fx) {
+    // fixed-point output words of the M = 1 GEMV, zero between runs
+    QG_HIP(hipMalloc(&h->acc64, (size_t)N * sizeof(unsigned long long)));
+    QG_HIP(hipMemsetAsync(h->acc64, 0, (size_t)N * sizeof(unsigned long long), st));
+  }
   QG_HIP(hipMemcpyAsync(h->codebook, d->codebook, 65536 * sizeof(uint16_t), hipMemcpyDeviceToDevice, st));
   const int64_t threads = h->tr_units * 64;
   k_repack_trellis<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>((const uint16_t*)d->codes, d->scales, K / 16, G,
@@ -509,9 +518,15 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
   a.W = (int)std::min<int64_t>((int64_t)h->tr_grid * nw, h->tr_units);  // every wave's range non-empty
   a.U = h->tr_units;
   const dim3 grid((unsigned)h->tr_grid), block((unsigned)(64 * nw));
-  if (M == 1) k_trellis<0><<<grid, block, 0, st>>>(a);
-  else if (M <= 16) k_trellis<1><<<grid, block, 0, st>>>(a);
-  else k_trellis<2><<<grid, block, 0, st>>>(a);
+  if (M == 1) {
+    const char* f = getenv("QG_TRELLIS_M1");  // =partials: the hand-over through partials and a count
+    a.acc = h->tr_fx && !(f && !strcmp(f, "partials")) ? h->acc64 : nullptr;
+    k_trellis<0><<<grid, block, 0, st>>>(a);
+  } else if (M <= 16) {
+    k_trellis<1><<<grid, block, 0, st>>>(a);
+  } else {
+    k_trellis<2><<<grid, block, 0, st>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(QG_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
   if (getenv("QG_DEBUG_SYNC")) {

@@ -132,3 +132,32 @@ def test_gemm_kernels_both(kernel, M, N, K, codebook, monkeypatch):
     err = O.normwise_rel_err(y1, t.ref(x))
     say("err", err)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("handover", ["words", "partials"])
+@pytest.mark.parametrize("N,K", [(16, 2048), (48, 2048), (400, 2560), (5120, 2048), (4112, 4096), (112, 17408)])
+def test_gemv_handovers_both(handover, N, K, codebook, monkeypatch):
+    """The M = 1 trellis GEMV with both row-block hand-overs, forced: the
+    fixed-point words (one atomic per output and wave) and the partials with an
+    arrival count.  The shapes give one to 16 waves per row block, one to three
+    units per wave, ranges that start and end inside row blocks, and (112 x
+    17408: 136 waves meet in one row block, more than the words count) the
+    partials either way.  The two largest are checked on sampled row blocks."""
+    if handover == "partials":
+        monkeypatch.setenv("QG_TRELLIS_M1", "partials")
+    else:
+        monkeypatch.delenv("QG_TRELLIS_M1", raising=False)
+    say("trellis gemv", handover, N, K)
+    t = Trellis(N, K, codebook, cfg_id=87)
+    x = S.activations(1, K, cfg_id=87, tensor_id=600)
+    y1 = _run(t.lin, x)
+    y2 = _run(t.lin, x)
+    assert np.array_equal(y1, y2)
+    if N * K <= (1 << 22):
+        err = O.normwise_rel_err(y1, t.ref(x))
+    else:
+        blocks = np.unique(np.concatenate([[0, N // 16 - 1], np.random.default_rng(8).choice(N // 16, 6, replace=False)]))
+        rows = (16 * blocks[:, None] + np.arange(16)[None, :]).reshape(-1)
+        err = O.normwise_rel_err(y1[:, rows], O.gemv_trellis_rows(x, t.words, t.cb, t.scales, N, K, rows))
+    say("err", err)
+    assert err <= TOL, err
