@@ -404,7 +404,8 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
 // buffer-to-LDS copies, each wave its share of the rows, XB slots in rotation,
 // PD groups ahead), and every wave reads its A fragments from there.  A wave
 // keeps one row block's sums over the whole slice; K slices meet as in the
-// stream-K kernel (fixed slots, arrival counter, sums in slot order).
+// stream-K kernel (fixed slots, arrival counter, sums in slot order), or, when
+// the outputs are few, in fixed-point output words (one atomic round trip).
 // ---------------------------------------------------------------------------
 template <int MT> struct TbShape {
   static constexpr int NW = MT == 2 ? 8 : 16;  // waves = row blocks per workgroup
@@ -421,8 +422,9 @@ struct TbArgs {
   const uint16_t* cb;      // [65536] fp16
   const uint16_t* x;       // [M][K] fp16, rotated
   uint16_t* y;             // [M][N] fp16
-  float* partial;          // [RB][maxseg][M][16] (S > 1)
+  float* partial;          // [RB][maxseg][M][16] (S > 1, acc NULL)
   int* counters;           // [RB], zero between launches
+  unsigned long long* acc; // [M][N] fixed-point output words (S > 1), zero between launches; or NULL
   int M, K, N, G, RB, maxseg, S;
 };
 
@@ -560,6 +562,30 @@ __global__ __launch_bounds__(64 * TbShape<MT>::NW) void k_trellis_band(TbArgs a)
       for (int e = 0; e < 4; ++e) {
         const int m = 16 * mt + 4 * mq + e;
         if (m < a.M) a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(acc[mt][e]);
+      }
+    return;
+  }
+  if (a.acc) {
+    // few outputs: fixed-point words (see fx_word), one atomic per output and
+    // slice whose returned count tells the last slice to store the result
+    unsigned long long mine[MT][4], before[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * mt + 4 * mq + e;
+        mine[mt][e] = fx_word(acc[mt][e]);
+        before[mt][e] = m < a.M ? fx_add(a.acc + (size_t)m * a.N + (size_t)rb * 16 + n, mine[mt][e]) : 0ull;
+      }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * mt + 4 * mq + e;
+        if (m >= a.M || (int)(before[mt][e] & 63ull) != S - 1) continue;
+        unsigned long long* w = a.acc + (size_t)m * a.N + (size_t)rb * 16 + n;
+        a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(fx_value(before[mt][e] + mine[mt][e]));
+        __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     return;
   }

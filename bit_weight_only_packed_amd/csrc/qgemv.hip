@@ -449,11 +449,9 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   const size_t nf = (size_t)RB * h->tr_maxseg * h->max_M * 16;
   QG_HIP(hipMalloc(&h->partial, nf * sizeof(float)));
   h->partial_floats = nf;
-  if (h->tr_fx) {
-    // fixed-point output words of the M = 1 GEMV, zero between runs
-    QG_HIP(hipMalloc(&h->acc64, (size_t)N * sizeof(unsigned long long)));
-    QG_HIP(hipMemsetAsync(h->acc64, 0, (size_t)N * sizeof(unsigned long long), st));
-  }
+  // fixed-point output words [max_M][N] of the M = 1 GEMV and the banded GEMM, zero between runs
+  QG_HIP(hipMalloc(&h->acc64, (size_t)h->max_M * N * sizeof(unsigned long long)));
+  QG_HIP(hipMemsetAsync(h->acc64, 0, (size_t)h->max_M * N * sizeof(unsigned long long), st));
   QG_HIP(hipMemcpyAsync(h->codebook, d->codebook, 65536 * sizeof(uint16_t), hipMemcpyDeviceToDevice, st));
   const int64_t threads = h->tr_units * 64;
   k_repack_trellis<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>((const uint16_t*)d->codes, d->scales, K / 16, G,
@@ -489,6 +487,11 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
     b.maxseg = h->tr_maxseg;
     b.S = tb_slices(h, nw);
     if (b.S > h->tr_maxseg) return fail(QG_ERR_INVALID_ARG, "%d K slices exceed the workspace's %d", b.S, h->tr_maxseg);
+    // K slices meet in fixed-point words where the atomics are few (and the
+    // words' 6-bit count holds S); QG_TRELLIS_HANDOVER=partials forces the partials
+    const char* fh = getenv("QG_TRELLIS_HANDOVER");
+    const bool fx = b.S > 1 && b.S <= 63 && (int64_t)M * h->N * b.S <= (1 << 20) && !(fh && !strcmp(fh, "partials"));
+    b.acc = fx ? h->acc64 : nullptr;
     const unsigned grid = (unsigned)(((b.RB + nw - 1) / nw) * b.S);
     if (m32) k_trellis_band<2><<<grid, 64 * nw, 0, st>>>(b);
     else k_trellis_band<1><<<grid, 64 * nw, 0, st>>>(b);
@@ -519,7 +522,7 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
   a.U = h->tr_units;
   const dim3 grid((unsigned)h->tr_grid), block((unsigned)(64 * nw));
   if (M == 1) {
-    const char* f = getenv("QG_TRELLIS_M1");  // =partials: the hand-over through partials and a count
+    const char* f = getenv("QG_TRELLIS_HANDOVER");  // =partials: the hand-over through partials and a count
     a.acc = h->tr_fx && !(f && !strcmp(f, "partials")) ? h->acc64 : nullptr;
     k_trellis<0><<<grid, block, 0, st>>>(a);
   } else if (M <= 16) {

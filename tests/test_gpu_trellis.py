@@ -113,16 +113,21 @@ def test_full_size_sampled_columns(K, N, M, codebook):
     assert np.isfinite(y).all()
 
 
-@pytest.mark.parametrize("kernel", ["stream", "banded"])
+@pytest.mark.parametrize("kernel", ["stream", "banded", "banded-partials"])
 @pytest.mark.parametrize("M", [2, 8, 17, 32])
 @pytest.mark.parametrize("N,K", [(48, 384), (400, 2560)])
 def test_gemm_kernels_both(kernel, M, N, K, codebook, monkeypatch):
     """Both trellis GEMMs, forced: the stream-K kernel (every unit loads its own
-    rows of x) and the banded one (x fragments shared through LDS, K slices)."""
+    rows of x) and the banded one (x fragments shared through LDS, K slices
+    meeting in fixed-point words, or, forced, in partials with a count)."""
     if kernel == "stream":
         monkeypatch.setenv("QG_TRELLIS", "stream")
     else:
         monkeypatch.delenv("QG_TRELLIS", raising=False)
+    if kernel == "banded-partials":
+        monkeypatch.setenv("QG_TRELLIS_HANDOVER", "partials")
+    else:
+        monkeypatch.delenv("QG_TRELLIS_HANDOVER", raising=False)
     say("trellis gemm", kernel, M, N, K)
     t = Trellis(N, K, codebook, cfg_id=86)
     x = S.activations(M, K, cfg_id=86, tensor_id=500 + M)
@@ -144,9 +149,9 @@ def test_gemv_handovers_both(handover, N, K, codebook, monkeypatch):
     17408: 136 waves meet in one row block, more than the words count) the
     partials either way.  The two largest are checked on sampled row blocks."""
     if handover == "partials":
-        monkeypatch.setenv("QG_TRELLIS_M1", "partials")
+        monkeypatch.setenv("QG_TRELLIS_HANDOVER", "partials")
     else:
-        monkeypatch.delenv("QG_TRELLIS_M1", raising=False)
+        monkeypatch.delenv("QG_TRELLIS_HANDOVER", raising=False)
     say("trellis gemv", handover, N, K)
     t = Trellis(N, K, codebook, cfg_id=87)
     x = S.activations(1, K, cfg_id=87, tensor_id=600)
