@@ -179,17 +179,22 @@ __device__ __forceinline__ int tr_wave_of(int64_t x, int64_t U, int W) {
   return w;
 }
 
-template <int MT>
+// XL (M = 1): the rotated x sits in LDS beside the codebook (the kernel rotates
+// it itself), so a unit loads only its codes and scale
+constexpr int TR_XL_BYTES = 32768;           // rotated x in LDS: K <= 16384
+constexpr int TR_XL_GMAX = 8;                // groups per wave to rotate (G <= 128, 16 waves)
+
+template <int MT, bool XL = false>
 struct TrUnit {
   static constexpr int XR = MT == 0 ? 1 : MT;  // activation row blocks held
-  static constexpr int loads = 2 + 4 * XR;     // load instructions per unit
+  static constexpr int loads = 2 + (XL ? 0 : 4 * XR);  // load instructions per unit
   u3_t z;                                      // code words
   uint32_t s;                                  // this lane's scale (fp16 in the low half)
   uint4 xv[XR][4];                             // activations: 32 k of row (16*mt + (lane & 15)), or of row 0 (M = 1)
 };
 
-template <int MT>
-__device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT>& t, int64_t u, int g, bool live, int lane) {
+template <int MT, bool XL = false>
+__device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT, XL>& t, int64_t u, int g, bool live, int lane) {
   const int uu = live ? 1 : 0;
   const int64_t uc = live ? u : 0;
   const int kq = lane >> 4;
@@ -201,9 +206,10 @@ __device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT>& t, int64_t 
   // one descriptor over all of x (wave-uniform, so no per-lane descriptor
   // loop); the lane's row and quarter go into the offset, and a row past M
   // (or a dead unit) takes an offset past the range: zeros, no memory access
+  if constexpr (XL) return;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(a.x), (uint32_t)a.M * (uint32_t)a.K * 2u);
 #pragma unroll
-  for (int mt = 0; mt < TrUnit<MT>::XR; ++mt) {
+  for (int mt = 0; mt < TrUnit<MT, XL>::XR; ++mt) {
     const int m = MT == 0 ? 0 : 16 * mt + (lane & 15);
     const bool ok = live && m < a.M;
     const uint32_t off = ok ? (uint32_t)(((size_t)m * a.K + (size_t)g * 128 + 32 * kq) * 2) : 0x80000000u;
@@ -237,12 +243,13 @@ template <int MT> struct TrShape {
   static constexpr int PD = MT == 2 ? 3 : 2;
 };
 
-template <int MT>
+template <int MT, bool XL = false>
 __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
+  static_assert(!XL || MT == 0, "x in LDS: M = 1 only");
   // static (not dynamic) LDS: its address is a compile-time constant, so the
   // gathers use the decoded byte address as is
-  __shared__ __align__(16) char smem[TR_CB_BYTES];
-  constexpr int XR = TrUnit<MT>::XR;
+  __shared__ __align__(16) char smem[TR_CB_BYTES + (XL ? TR_XL_BYTES : 0)];
+  constexpr int XR = TrUnit<MT, XL>::XR;
   const int lane = threadIdx.x & 63;
   const int NW = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -262,15 +269,53 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rcb, (__attribute__((address_space(3))) void*)(smem + (size_t)ci * 1024),
                                                16, (uint32_t)(ci * 1024 + lane * 16), 0, 0, 0);
   }
-  TrUnit<MT> c[PD];
+  // XL: this wave's groups of the unrotated x (groups wave, wave + NW, ...)
+  uint16_t xa[XL ? TR_XL_GMAX : 1], xb[XL ? TR_XL_GMAX : 1];
+  if constexpr (XL) {
+    const int NWv = blockDim.x >> 6;
 #pragma unroll
-  for (int i = 0; i < PD; ++i) tr_load<MT>(a, c[i], lo + i, (int)((lo + i) % a.G), lo + i < hi, lane);
+    for (int i = 0; i < TR_XL_GMAX; ++i) {
+      const int g = wave + i * NWv;
+      xa[i] = g < a.G ? a.x[(size_t)g * 128 + lane] : (uint16_t)0;
+      xb[i] = g < a.G ? a.x[(size_t)g * 128 + 64 + lane] : (uint16_t)0;
+    }
+  }
+  TrUnit<MT, XL> c[PD];
+#pragma unroll
+  for (int i = 0; i < PD; ++i) tr_load<MT, XL>(a, c[i], lo + i, (int)((lo + i) % a.G), lo + i < hi, lane);
   {
-    constexpr int n = PD * TrUnit<MT>::loads;  // loads issued after the codebook's
+    constexpr int n = PD * TrUnit<MT, XL>::loads;  // loads issued after the codebook's (and x's)
     static_assert(n < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
   }
-  lds_barrier();  // every wave's share of the codebook has landed
+  if constexpr (XL) {
+    // rotate each group as k_fwht does (same operations in the same order, so
+    // the same fp16 values) and keep it in LDS after the codebook
+    uint16_t* xr = reinterpret_cast<uint16_t*>(smem + TR_CB_BYTES);
+    const int NWv = blockDim.x >> 6;
+#pragma unroll
+    for (int i = 0; i < TR_XL_GMAX; ++i) {
+      const int g = wave + i * NWv;
+      if (g >= a.G) break;
+      float p = h2f(xa[i]), q = h2f(xb[i]);
+      {
+        const float su = p + q, df = p - q;
+        p = su;
+        q = df;
+      }
+#pragma unroll
+      for (int hh = 32; hh >= 1; hh >>= 1) {
+        const float pp = __shfl_xor(p, hh), pq = __shfl_xor(q, hh);
+        const bool upper = (lane & hh) != 0;
+        p = upper ? pp - p : p + pp;
+        q = upper ? pq - q : q + pq;
+      }
+      const float f = 0.08838834764831845f;  // 2^-3.5
+      xr[g * 128 + lane] = f2h(p * f);
+      xr[g * 128 + 64 + lane] = f2h(q * f);
+    }
+  }
+  lds_barrier();  // every wave's share of the codebook (and of the rotated x) has landed
   if (lo >= hi) return;
   const char* cbl = smem;
   float acc1 = 0.0f;
@@ -283,7 +328,7 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
   int gpf = (int)((lo + PD) % a.G);
   // one unit: decode, contract, reload the same registers with unit u + 3, and
   // flush at the end of a row block or of the range
-  auto step = [&](TrUnit<MT>& cu, int64_t u) {
+  auto step = [&](TrUnit<MT, XL>& cu, int64_t u) {
     const uint32_t z2 = cu.z.x, z1 = cu.z.y, z0 = cu.z.z;
     const uint32_t nz2 = tr_from_next_row_lane(z2), nz1 = tr_from_next_row_lane(z1);
     uint32_t addr[32];
@@ -292,13 +337,21 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
     tr_gather(cbl, addr, pr);
     const float s = h2f((uint16_t)(cu.s & 0xFFFFu));
     if constexpr (MT == 0) {
+      uint4 xv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if constexpr (XL)
+          xv[v] = *reinterpret_cast<const uint4*>(smem + TR_CB_BYTES + ((size_t)g * 128 + 32 * (lane >> 4)) * 2 + v * 16);
+        else
+          xv[v] = cu.xv[0][v];
+      }
       float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        d0 = dot2(pr[4 * v + 0], cu.xv[0][v].x, d0);
-        d1 = dot2(pr[4 * v + 1], cu.xv[0][v].y, d1);
-        d0 = dot2(pr[4 * v + 2], cu.xv[0][v].z, d0);
-        d1 = dot2(pr[4 * v + 3], cu.xv[0][v].w, d1);
+        d0 = dot2(pr[4 * v + 0], xv[v].x, d0);
+        d1 = dot2(pr[4 * v + 1], xv[v].y, d1);
+        d0 = dot2(pr[4 * v + 2], xv[v].z, d0);
+        d1 = dot2(pr[4 * v + 3], xv[v].w, d1);
       }
       acc1 = __builtin_fmaf(s, d0 + d1, acc1);
     } else {
@@ -313,7 +366,7 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
         for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(s, cg[e], acc[mt][e]);
       }
     }
-    tr_load<MT>(a, cu, u + PD, gpf, u + PD < hi, lane);
+    tr_load<MT, XL>(a, cu, u + PD, gpf, u + PD < hi, lane);
     gpf = gpf + 1 == a.G ? 0 : gpf + 1;
     const bool last_unit = u + 1 == hi;
     g = g + 1 == a.G ? 0 : g + 1;

@@ -461,9 +461,19 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   return QG_OK;
 }
 
+// M = 1 GEMV that rotates x itself into LDS (no separate rotation launch):
+// room for the rotated x beside the codebook up to K = 16384
+bool trellis_xl(const qg_plan* h, int M) {
+  const char* f = getenv("QG_TRELLIS_ROT");  // =launch: the separate rotation kernel
+  if (f && !strcmp(f, "launch")) return false;
+  return M == 1 && !(h->flags & QG_FLAG_X_PREROTATED) && (size_t)h->K * 2 <= (size_t)TR_XL_BYTES &&
+         h->G <= TR_XL_GMAX * TrShape<0>::NWMAX;
+}
+
 qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, hipStream_t st) {
   const uint16_t* xr = x;
-  if (!(h->flags & QG_FLAG_X_PREROTATED)) {
+  const bool xl = trellis_xl(h, M);
+  if (!(h->flags & QG_FLAG_X_PREROTATED) && !xl) {
     const int waves = M * h->G;
     k_fwht<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, h->xrot, M, h->K);
     xr = h->xrot;
@@ -524,7 +534,8 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
   if (M == 1) {
     const char* f = getenv("QG_TRELLIS_HANDOVER");  // =partials: the hand-over through partials and a count
     a.acc = h->tr_fx && !(f && !strcmp(f, "partials")) ? h->acc64 : nullptr;
-    k_trellis<0><<<grid, block, 0, st>>>(a);
+    if (xl) k_trellis<0, true><<<grid, block, 0, st>>>(a);  // a.x: the unrotated x
+    else k_trellis<0><<<grid, block, 0, st>>>(a);
   } else if (M <= 16) {
     k_trellis<1><<<grid, block, 0, st>>>(a);
   } else {

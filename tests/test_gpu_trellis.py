@@ -166,3 +166,22 @@ def test_gemv_handovers_both(handover, N, K, codebook, monkeypatch):
         err = O.normwise_rel_err(y1[:, rows], O.gemv_trellis_rows(x, t.words, t.cb, t.scales, N, K, rows))
     say("err", err)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("N,K", [(48, 384), (400, 2560), (1040, 5120), (96, 16384)])
+def test_gemv_rotation_in_kernel(N, K, codebook, monkeypatch):
+    """The M = 1 GEMV that rotates x itself into LDS gives the same bits as the
+    separate rotation launch followed by the GEMV (both compute the same fp16
+    rotated values), and matches the oracle."""
+    t = Trellis(N, K, codebook, cfg_id=88)
+    x = S.activations(1, K, cfg_id=88, tensor_id=700)
+    say("trellis rotation", N, K)
+    monkeypatch.setenv("QG_TRELLIS_ROT", "launch")
+    y_launch = _run(t.lin, x)
+    monkeypatch.delenv("QG_TRELLIS_ROT", raising=False)
+    y_kernel = _run(t.lin, x)
+    assert np.array_equal(y_launch, y_kernel)
+    if N * K <= (1 << 22):
+        err = O.normwise_rel_err(y_kernel, t.ref(x))
+        say("err", err)
+        assert err <= TOL, err
