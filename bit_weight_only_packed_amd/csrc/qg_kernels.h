@@ -349,8 +349,11 @@ __device__ __forceinline__ void gemv_q_body(const RunArgs& a, const SegDev (&sd)
   }
 }
 
+// several widths (BF = 0): the three bodies' registers are allocated together;
+// capped so that six waves fit on each SIMD (the decode shapes' grids stay resident)
 template <int NQ, bool DUAL, int BF>
-__global__ __launch_bounds__(1024) void k_gemv_q(RunArgs a) {
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(BF == 0 && !DUAL && NQ <= 2 ? 6 : 1)))
+void k_gemv_q(RunArgs a) {
   extern __shared__ __align__(16) char smem[];
   constexpr int ND = DUAL ? 2 : 1;
   const int NW = blockDim.x >> 6;

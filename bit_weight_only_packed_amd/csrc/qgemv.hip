@@ -582,8 +582,10 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
     acc += (int64_t)h->col_bits[n] * K / 32;
   }
   h->weight_bytes = acc * 4 + (int64_t)N * G * 2;
+  // widest codes first: their workgroups (the longest) are dispatched first,
+  // so the tail of a launch is the lighter widths'
   int tile0 = 0;
-  for (int b = 2; b <= 4; ++b) {
+  for (int b = 4; b >= 2; --b) {
     std::vector<int32_t> cols;
     for (int n = 0; n < N; ++n)
       if (h->col_bits[n] == b) cols.push_back(n);
