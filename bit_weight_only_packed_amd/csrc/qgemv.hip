@@ -235,37 +235,50 @@ int xs_nq_compiled(int nq) {
 // groups per workgroup GPW and K slices S) for the 27B-class layer shapes; the
 // generic rule in xs_plan covers other shapes.
 struct XsTuned {
-  int N, K, mcls, GPW, S;
+  int N, K, mcls, GPW, S, T;  // T: tiles per tile group (1 or 2)
 };
 constexpr XsTuned kXsTuned[] = {
-    {5120, 5120, 1, 4, 6},  {5120, 5120, 2, 4, 6},    // q, o
-    {1024, 5120, 1, 2, 10}, {1024, 5120, 2, 4, 10},   // k, v
-    {17408, 5120, 1, 4, 3}, {17408, 5120, 2, 8, 3},   // gate, up
-    {5120, 17408, 1, 4, 6}, {5120, 17408, 2, 8, 9},   // down
-    {7168, 5120, 1, 4, 4},  {7168, 5120, 2, 4, 4},    // q | k | v stacked
-    {34816, 5120, 1, 4, 3}, {34816, 5120, 2, 8, 3},   // gate | up stacked
+    {5120, 5120, 1, 8, 6, 1},  {5120, 5120, 2, 8, 4, 1},    // q, o
+    {1024, 5120, 1, 4, 10, 1}, {1024, 5120, 2, 4, 10, 1},   // k, v
+    {17408, 5120, 1, 8, 3, 1}, {17408, 5120, 2, 8, 3, 2},   // gate, up
+    {5120, 17408, 1, 8, 6, 1}, {5120, 17408, 2, 8, 9, 2},   // down
+    {7168, 5120, 1, 8, 4, 1},  {7168, 5120, 2, 8, 4, 1},    // q | k | v stacked
+    {34816, 5120, 1, 8, 3, 1}, {34816, 5120, 2, 8, 3, 2},   // gate | up stacked
 };
 
-// Verify GEMM kind: the x-in-LDS kernel, except where the per-wave-K-split
-// kernel measured faster (k/v at more than 16 rows); QG_GEMM forces one.
+// Verify GEMM kind: the x-in-LDS kernel (measured fastest on every decode
+// shape once its tile groups may hold one tile); QG_GEMM forces one.
 int gemm_kind(const qg_plan* h, int M) {
+  (void)h;
+  (void)M;
   const int f = gemm_forced();
   if (f >= 0) return f;
-  if (h->N == 1024 && h->K == 5120 && M > 16) return GEMM_MFMA;
   return GEMM_XS;
 }
 
 XsPlan xs_plan(const qg_plan* h, int M, bool dual) {
   XsPlan p;
   Launch L = h->over[mclass(M)];
-  if (L.T <= 0 && L.NW <= 0 && L.S <= 0 && !dual)
+  // one-tile groups (twice the waves) measured faster except for wide
+  // matrices at more than 16 rows
+  int tuned_T = (M <= 16 || h->total_tiles <= 512) ? 1 : 2;
+  if (!dual)
     for (const XsTuned& t : kXsTuned)
       if (t.N == h->N && t.K == h->K && t.mcls == mclass(M)) {
-        L.T = t.GPW;
-        L.S = t.S;
+        tuned_T = t.T;
+        if (L.T <= 0 && L.NW <= 0 && L.S <= 0) {
+          L.T = t.GPW;
+          L.S = t.S;
+        }
       }
   p.MT = M <= 16 ? 1 : 2;
-  p.T = dual ? 1 : 2;
+  // tiles per tile group: 1 for the fused gate/up pair; else the tuned count
+  // (QG_XS_T=1|2 forces one)
+  p.T = dual ? 1 : tuned_T;
+  if (!dual) {
+    const char* ft = getenv("QG_XS_T");
+    if (ft && (atoi(ft) == 1 || atoi(ft) == 2)) p.T = atoi(ft);
+  }
   const size_t col_cap = 4096;  // room for the run's column map
   // fewest K slices whose x slice fits LDS (at the compiled slice length)
   p.S = std::max(1, std::min(h->G4, L.S > 0 ? L.S : 1));
@@ -851,6 +864,7 @@ template <int BF>
 hipError_t xs_allow_lds_b() {
   hipError_t e = hipSuccess;
   const hipError_t r[] = {xs_allow_lds<2, 1, false, BF>(), xs_allow_lds<2, 2, false, BF>(),
+                          xs_allow_lds<1, 1, false, BF>(), xs_allow_lds<1, 2, false, BF>(),
                           xs_allow_lds<1, 1, true, BF>(), xs_allow_lds<1, 2, true, BF>()};
   for (hipError_t x : r)
     if (x != hipSuccess) e = x;
@@ -866,15 +880,21 @@ hipError_t xs_allow_lds_all() {
   return e;
 }
 
-template <int MT, bool DUAL, int NQ>
-void launch_xs_q(const XsArgs& a, const XsPlan& p, int bf, hipStream_t st) {
-  constexpr int T = DUAL ? 1 : 2;
+template <int T, int MT, bool DUAL, int NQ>
+void launch_xs_t(const XsArgs& a, const XsPlan& p, int bf, hipStream_t st) {
   switch (bf) {
     case 2: k_gemm_xs<T, MT, DUAL, 2, NQ><<<p.grid, p.NW * 64, p.lds, st>>>(a); break;
     case 3: k_gemm_xs<T, MT, DUAL, 3, NQ><<<p.grid, p.NW * 64, p.lds, st>>>(a); break;
     case 4: k_gemm_xs<T, MT, DUAL, 4, NQ><<<p.grid, p.NW * 64, p.lds, st>>>(a); break;
     default: k_gemm_xs<T, MT, DUAL, 0, NQ><<<p.grid, p.NW * 64, p.lds, st>>>(a); break;
   }
+}
+
+template <int MT, bool DUAL, int NQ>
+void launch_xs_q(const XsArgs& a, const XsPlan& p, int bf, hipStream_t st) {
+  if constexpr (DUAL) launch_xs_t<1, MT, true, NQ>(a, p, bf, st);
+  else if (p.T == 1) launch_xs_t<1, MT, false, NQ>(a, p, bf, st);
+  else launch_xs_t<2, MT, false, NQ>(a, p, bf, st);
 }
 
 template <int MT, bool DUAL>

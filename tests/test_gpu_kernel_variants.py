@@ -57,22 +57,32 @@ def test_m1_kernels_mixed_widths(kernel, monkeypatch):
     _check(u.lin, x, u.ref(x))
 
 
-@pytest.mark.parametrize("gemm", ["v1", "v2", "xs"])
+@pytest.mark.parametrize("gemm", ["v1", "v2", "xs", "xs-t2"])
 @pytest.mark.parametrize("M", [2, 8, 16, 17, 32])
 @pytest.mark.parametrize("N,K,bits", [(48, 384, 3), (272, 1280, 2), (528, 2560, 4)])
 def test_gemm_kernels(gemm, M, N, K, bits, monkeypatch):
-    monkeypatch.setenv("QG_GEMM", gemm)
+    """Every verify GEMM, forced; xs-t2 is the x-in-LDS GEMM with two-tile groups
+    (the default there is one tile per group on these small shapes)."""
+    monkeypatch.setenv("QG_GEMM", gemm.split("-")[0])
+    if gemm == "xs-t2":
+        monkeypatch.setenv("QG_XS_T", "2")
+    else:
+        monkeypatch.delenv("QG_XS_T", raising=False)
     say("gemm", gemm, M, N, K, bits)
     u = Uniform(N, K, bits, cfg_id=92)
     x = S.activations(M, K, cfg_id=92, tensor_id=300 + M)
     _check(u.lin, x, u.ref(x))
 
 
-@pytest.mark.parametrize("gemm", ["v1", "v2", "xs"])
+@pytest.mark.parametrize("gemm", ["v1", "v2", "xs", "xs-t2"])
 @pytest.mark.parametrize("M,tiles,waves,splits", [(8, 1, 4, 1), (8, 2, 8, 3), (32, 1, 8, 5), (32, 4, 4, 2),
                                                   (32, 2, 8, 1), (17, 2, 4, 4)])
 def test_gemm_launch_shapes(gemm, M, tiles, waves, splits, monkeypatch):
-    monkeypatch.setenv("QG_GEMM", gemm)
+    monkeypatch.setenv("QG_GEMM", gemm.split("-")[0])
+    if gemm == "xs-t2":
+        monkeypatch.setenv("QG_XS_T", "2")
+    else:
+        monkeypatch.delenv("QG_XS_T", raising=False)
     N, K = 400, 2560
     say("gemm launch", gemm, M, tiles, waves, splits)
     u = Uniform(N, K, 3, cfg_id=93)
