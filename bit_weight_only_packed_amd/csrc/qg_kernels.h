@@ -222,7 +222,10 @@ __device__ __forceinline__ bool splitk_last(int* counter, int S, int* flag) {
 // slice of quads; wave w owns NQ consecutive quads (the last wave's surplus
 // lies outside its buffer range and reads nothing).  Each wave issues all its
 // code loads at once, right after the x and scale loads of the workgroup
-// prologue, and consumes them in order.
+// prologue, and consumes them in order.  The fused gate/up pass runs either
+// with both matrices in each workgroup (DUAL) or, by default, with one matrix
+// per workgroup (a.pair): the two workgroups of a tile then meet in an
+// exchange word, or, with K slices, in the partials.
 // ---------------------------------------------------------------------------
 
 // LDS layout (bytes): x slice 4*nqs*256 | quarter sums 4*nqs*16 | scales
