@@ -314,7 +314,11 @@ XsPlan xs_plan(const qg_plan* h, int M, bool dual) {
   p.lds = xs_lds_bytes(M, p.MT, p.NQ, p.GPW, p.T);
   // fixed-point words while the atomics stay few (measured: they win at 8 rows
   // on every decode shape, the partials at 32 rows on the widest); <= 63 slices
-  p.fx = p.S > 1 && p.S <= 63 && (int64_t)M * 16 * h->total_tiles * p.S <= (int64_t)1 << 20;
+  // fixed-point words when the atomics are few, or when many slices would make
+  // the last one read its partials in several round trips (measured: down at
+  // 24-32 rows, 9 slices, gains; gate/up, 3 slices, loses)
+  const int64_t atomics = (int64_t)M * 16 * h->total_tiles * p.S;
+  p.fx = p.S > 1 && p.S <= 63 && (atomics <= (int64_t)1 << 20 || (p.S >= 6 && atomics <= (int64_t)1 << 22));
   return p;
 }
 
