@@ -319,6 +319,9 @@ XsPlan xs_plan(const qg_plan* h, int M, bool dual) {
   // 24-32 rows, 9 slices, gains; gate/up, 3 slices, loses)
   const int64_t atomics = (int64_t)M * 16 * h->total_tiles * p.S;
   p.fx = p.S > 1 && p.S <= 63 && (atomics <= (int64_t)1 << 20 || (p.S >= 6 && atomics <= (int64_t)1 << 22));
+  const char* fh = getenv("QG_XS_HANDOVER");  // =partials | =words forces one
+  if (fh && !strcmp(fh, "partials")) p.fx = false;
+  if (fh && !strcmp(fh, "words")) p.fx = p.S > 1 && p.S <= 63;
   return p;
 }
 

@@ -146,6 +146,44 @@ def test_m1_gate_up_pair_matches_dual(mixed, splits, monkeypatch):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("handover", ["partials", "words"])
+@pytest.mark.parametrize("tiles", ["1", "2"])
+@pytest.mark.parametrize("M", [2, 8, 17, 32])
+def test_gemm_xs_handovers(handover, tiles, M, monkeypatch):
+    """x-in-LDS GEMM with its K slices forced to meet through partials and an
+    arrival count or through fixed-point words, with one- and two-tile groups,
+    uniform and several widths, and the fused gate/up pass; repeats are
+    bit-identical."""
+    monkeypatch.setenv("QG_GEMM", "xs")
+    monkeypatch.setenv("QG_XS_HANDOVER", handover)
+    monkeypatch.setenv("QG_XS_T", tiles)
+    N, K = 400, 3072
+    say("gemm xs handover", handover, tiles, M)
+    u = Uniform(N, K, 3, cfg_id=97)
+    u.lin.set_launch(M, 2, 0, 4)
+    x = S.activations(M, K, cfg_id=97, tensor_id=300 + M)
+    _check(u.lin, x, u.ref(x))
+    cb = S.column_bits(N, 0.2, 4, cfg_id=97)
+    v = Uniform(N, K, col_bits=cb, cfg_id=97)
+    v.lin.set_launch(M, 2, 0, 3)
+    _check(v.lin, x, v.ref(x))
+    H, I = 2048, 1408
+    g = Uniform(I, H, bits=3, cfg_id=98, tid=0)
+    up = Uniform(I, H, bits=3, cfg_id=98, tid=1)
+    d = Uniform(H, I, bits=3, cfg_id=98, tid=2)
+    for lin in (g.lin, d.lin):
+        lin.set_launch(M, 2, 0, 2)
+    xm = S.activations(M, H, cfg_id=98, tensor_id=400 + M)
+    xd = dev_f16(xm)
+    o1 = Q.mlp(g.lin, up.lin, d.lin, xd)
+    o2 = Q.mlp(g.lin, up.lin, d.lin, xd)
+    torch.cuda.synchronize()
+    assert sha(o1) == sha(o2)
+    err = O.normwise_rel_err(o1.cpu().numpy().astype(np.float64), O.mlp(xm, g.w(), up.w(), d.w()))
+    say("mlp err", err)
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("M", [3, 16, 32])
 def test_gemm_xs_mixed_widths(M, monkeypatch):
     """x-in-LDS GEMM over three width segments (its workgroups never span two)."""
