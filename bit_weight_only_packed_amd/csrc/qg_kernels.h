@@ -51,7 +51,9 @@ struct RunArgs {
   int M, K, G, G4, ldy, NP;
   int T, S;                // tiles per workgroup, K slices across workgroups
   int pair;                // M = 1 gate/up pass with one matrix per workgroup (w[0], w[1])
-  unsigned long long* xw;  // pair pass, one K slice: per padded column hand-over word, zero between runs
+  unsigned long long* xw;  // per padded column word, zero between runs: the pair pass's exchange
+                           // word (one K slice) or, with fx, the K slices' fixed-point sum
+  int fx;                  // one matrix, K slices: meet in fixed-point words (else partials)
   int ts_prefix[MAX_SEG + 1];  // prefix sums of tile-sets per segment
 };
 
@@ -425,6 +427,20 @@ void k_gemv_q(RunArgs a) {
         const float g = dm == 0 ? v[0] : other, u = dm == 0 ? other : v[0];
         __hip_atomic_store(a.xw + pc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (n_out >= 0) a.y[n_out] = f2h(silu_mul(g, u));
+      }
+    }
+    return;
+  }
+  if (!DUAL && P == 1 && S > 1 && a.fx) {
+    // K slices meet in fixed-point words (see fx_word): one atomic round trip;
+    // the arrival that completes the count stores the result and re-arms the word
+    if (mine) {
+      unsigned long long* w = a.xw + pc;
+      const unsigned long long part = fx_word(v[0]);
+      const unsigned long long before = fx_add(w, part);
+      if ((int)(before & 63ull) == S - 1) {
+        if (n_out >= 0) a.y[n_out] = f2h(fx_value(before + part));
+        __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     return;

@@ -144,7 +144,9 @@ Launch choose(const qg_plan* h, int M, bool dual = false, int force_v2 = -1) {
     // quads (fused gate/up: at most 2 quads per wave for register room)
     L.T = 1;
     const int G4 = h->G4;
-    if (L.S <= 0) L.S = 1;
+    // long K: slices of about 9 quads (measured on 17408 x 5120: 4 slices
+    // 10.6 us against 14.7 in one)
+    if (L.S <= 0) L.S = (!dual && G4 > 16) ? (G4 + 8) / 9 : 1;
     L.S = std::min(L.S, G4);
     const int g4s = (G4 + L.S - 1) / L.S;
     if (L.NW <= 0) {
@@ -773,16 +775,17 @@ qg_status run_sk(const qg_plan* h, const qg_plan* h2, const uint16_t* x, uint16_
   return QG_OK;
 }
 
-// M = 1 kernel choice, measured on the decode shapes: the per-tile-run kernel
-// (run_sk) everywhere except wide, short-K matrices (>= 512 tiles, K <= 8192),
-// where the per-group kernel (k_gemv_q) is faster.  QG_M1_KERNEL=pergroup|runs
+// M = 1 kernel choice, measured on the decode shapes: the per-group kernel
+// (k_gemv_q) for wide, short-K matrices (>= 512 tiles, K <= 8192) and for long
+// K (>= 256 tiles, K > 8192: there in K slices that meet in fixed-point words),
+// the per-tile-run kernel (run_sk) elsewhere.  QG_M1_KERNEL=pergroup|runs
 // forces one.
 bool use_sk(const qg_plan* h) {
   if (!sk_fits(h)) return false;
   const char* f = getenv("QG_M1_KERNEL");
   if (f && !strcmp(f, "pergroup")) return false;
   if (f && !strcmp(f, "runs")) return true;
-  return !(h->total_tiles >= 512 && h->G4 <= 16);
+  return !((h->total_tiles >= 512 && h->G4 <= 16) || (h->total_tiles >= 256 && h->G4 > 16));
 }
 
 template <int T, int MT, int QMAX, bool DUAL>
@@ -999,6 +1002,11 @@ qg_status run_uniform(const qg_plan* h, const qg_plan* h2, const uint16_t* x, in
   a.pair = pair ? 1 : 0;
   a.xw = h->acc64;
   if (pair && S == 1 && !h->acc64) return fail(QG_ERR_INVALID_ARG, "no hand-over words for the paired gate/up pass");
+  {
+    // M = 1, one matrix, K slices: fixed-point words (QG_M1_HANDOVER=partials forces the partials)
+    const char* fh = getenv("QG_M1_HANDOVER");
+    a.fx = (M == 1 && !dual && S > 1 && S <= 63 && h->acc64 && !(fh && !strcmp(fh, "partials"))) ? 1 : 0;
+  }
   int pre = 0;
   for (int i = 0; i < (int)h->segs.size(); ++i) {
     a.ts_prefix[i] = pre;

@@ -49,9 +49,10 @@
  * be ordered (same stream, or caller-ordered).  Different handles are
  * independent.
  *
- * Determinism.  Every reduction runs in a fixed order and no floating-point
- * atomics are used: for the same handle and the same inputs, y is
- * bit-identical across calls, streams and processes.
+ * Determinism.  Every reduction either runs in a fixed order or adds exact
+ * fixed-point integers (whose sum does not depend on the order of arrival);
+ * no floating-point atomics are used: for the same handle and the same
+ * inputs, y is bit-identical across calls, streams and processes.
  *
  * Errors.  Every entry point returns a qg_status; on failure a message is
  * available from qg_last_error() (thread-local, valid until the next call on
@@ -134,11 +135,12 @@ qg_status qgemv_weight_bytes(qg_handle h, int64_t* bytes);
  * `M` (M = 1, or any M in 2..16, or any M in 17..32); for sweeps of launch
  * shapes.  Values <= 0 restore the built-in choice.  Meaning per kernel:
  *   M = 1, per-tile-run GEMV (the default except for >= 512 tiles with
- *     K <= 8192): `tiles` = waves per 16-column tile (each takes a run of at most
+ *     K <= 8192 and >= 256 tiles with K > 8192): `tiles` = waves per 16-column
+ *     tile (each takes a run of at most
  *     8 quads of 512 k), `waves` = waves per workgroup (1..8), `splits` unused.
  *   M = 1, per-group GEMV: `tiles` 16-column tiles per workgroup (1), `waves`
  *     waves per workgroup splitting K (1..16), `splits` K slices across
- *     workgroups (1..16, reduced in a fixed order).
+ *     workgroups (1..16; summed in fixed-point words, exact in any order).
  *   M > 1: `tiles` tiles per wave (1, 2 or 4), `waves` waves per workgroup
  *     (1, 2, 4 or 8), `splits` K slices across workgroups (1..16).
  * Uniform-code handles only; a shape the compiled kernels cannot take fails

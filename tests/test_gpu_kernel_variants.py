@@ -45,6 +45,26 @@ def test_m1_kernels(kernel, N, K, bits, monkeypatch):
     _check(u.lin, x, u.ref(x))
 
 
+@pytest.mark.parametrize("handover", ["words", "partials"])
+@pytest.mark.parametrize("splits", [2, 3, 5])
+@pytest.mark.parametrize("mixed", [False, True])
+def test_m1_pergroup_k_slices(handover, splits, mixed, monkeypatch):
+    """Per-group M = 1 GEMV in K slices that meet in fixed-point words (the
+    default for long K) or, forced, in partials with an arrival count."""
+    monkeypatch.setenv("QG_M1_KERNEL", "pergroup")
+    if handover == "partials":
+        monkeypatch.setenv("QG_M1_HANDOVER", "partials")
+    else:
+        monkeypatch.delenv("QG_M1_HANDOVER", raising=False)
+    N, K = 464, 9216
+    kw = dict(col_bits=S.column_bits(N, 0.2, 2, cfg_id=99)) if mixed else dict(bits=3)
+    say("m1 k slices", handover, splits, mixed)
+    u = Uniform(N, K, cfg_id=99, **kw)
+    u.lin.set_launch(1, 1, 0, splits)
+    x = S.activations(1, K, cfg_id=99, tensor_id=300)
+    _check(u.lin, x, u.ref(x))
+
+
 @pytest.mark.parametrize("kernel", ["pergroup", "runs"])
 def test_m1_kernels_mixed_widths(kernel, monkeypatch):
     monkeypatch.setenv("QG_M1_KERNEL", kernel)
