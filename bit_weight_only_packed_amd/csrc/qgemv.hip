@@ -144,9 +144,10 @@ Launch choose(const qg_plan* h, int M, bool dual = false, int force_v2 = -1) {
     // quads (fused gate/up: at most 2 quads per wave for register room)
     L.T = 1;
     const int G4 = h->G4;
-    // long K: slices of about 9 quads (measured on 17408 x 5120: 4 slices
-    // 10.6 us against 14.7 in one)
-    if (L.S <= 0) L.S = (!dual && G4 > 16) ? (G4 + 8) / 9 : 1;
+    // K slices (one matrix; measured): of about 2 quads up to K = 8192 (a
+    // one-wave workgroup per slice: gate/up 10.4 us against 10.6 in one slice,
+    // q/o 6.4 against 7.0), of about 9 quads beyond (down: 10.6 against 14.7)
+    if (L.S <= 0) L.S = dual ? 1 : (G4 > 16 ? (G4 + 8) / 9 : (G4 + 1) / 2);
     L.S = std::min(L.S, G4);
     const int g4s = (G4 + L.S - 1) / L.S;
     if (L.NW <= 0) {
@@ -776,16 +777,15 @@ qg_status run_sk(const qg_plan* h, const qg_plan* h2, const uint16_t* x, uint16_
 }
 
 // M = 1 kernel choice, measured on the decode shapes: the per-group kernel
-// (k_gemv_q) for wide, short-K matrices (>= 512 tiles, K <= 8192) and for long
-// K (>= 256 tiles, K > 8192: there in K slices that meet in fixed-point words),
-// the per-tile-run kernel (run_sk) elsewhere.  QG_M1_KERNEL=pergroup|runs
-// forces one.
+// (k_gemv_q, in K slices that meet in fixed-point words) from 256 tiles up,
+// the per-tile-run kernel (run_sk) for narrower matrices.
+// QG_M1_KERNEL=pergroup|runs forces one.
 bool use_sk(const qg_plan* h) {
   if (!sk_fits(h)) return false;
   const char* f = getenv("QG_M1_KERNEL");
   if (f && !strcmp(f, "pergroup")) return false;
   if (f && !strcmp(f, "runs")) return true;
-  return !((h->total_tiles >= 512 && h->G4 <= 16) || (h->total_tiles >= 256 && h->G4 > 16));
+  return h->total_tiles < 256;
 }
 
 template <int T, int MT, int QMAX, bool DUAL>

@@ -134,9 +134,8 @@ qg_status qgemv_weight_bytes(qg_handle h, int64_t* bytes);
 /* Override the launch geometry used for runs with M rows in the class of
  * `M` (M = 1, or any M in 2..16, or any M in 17..32); for sweeps of launch
  * shapes.  Values <= 0 restore the built-in choice.  Meaning per kernel:
- *   M = 1, per-tile-run GEMV (the default except for >= 512 tiles with
- *     K <= 8192 and >= 256 tiles with K > 8192): `tiles` = waves per 16-column
- *     tile (each takes a run of at most
+ *   M = 1, per-tile-run GEMV (the default below 256 tiles): `tiles` = waves
+ *     per 16-column tile (each takes a run of at most
  *     8 quads of 512 k), `waves` = waves per workgroup (1..8), `splits` unused.
  *   M = 1, per-group GEMV: `tiles` 16-column tiles per workgroup (1), `waves`
  *     waves per workgroup splitting K (1..16), `splits` K slices across
