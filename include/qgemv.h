@@ -44,10 +44,12 @@
  * enqueue kernels on the given stream and return; x, y and out stay
  * caller-owned and must stay valid until that stream work completes.
  *
- * Concurrency.  A handle is immutable after create, but it owns one split-K
- * workspace and one MLP staging buffer, so runs that use the same handle must
- * be ordered (same stream, or caller-ordered).  Different handles are
- * independent.
+ * Concurrency.  A handle is immutable after create, but it owns its split-K
+ * workspace (fp32 partials, arrival counters and fixed-point column words,
+ * which every run leaves re-armed) and one MLP staging buffer, so runs that
+ * use the same handle must be ordered (same stream, or caller-ordered).
+ * Different handles are independent.  A kernel that faulted may leave the
+ * workspace un-armed: destroy and re-create the handle after a device error.
  *
  * Determinism.  Every reduction either runs in a fixed order or adds exact
  * fixed-point integers (whose sum does not depend on the order of arrival);
