@@ -134,3 +134,25 @@ def test_error_paths_on_device():
         u.lin.set_launch(1, 1, 17, 1)                 # M = 1: at most 16 waves
     with pytest.raises(Q.QGError):
         u.lin.set_launch(8, 1, 6, 1)                  # M > 1: 1, 2, 4 or 8 waves
+
+
+@pytest.mark.parametrize("max_M", [1, 2, 5, 17])
+def test_every_row_count_up_to_max_M(max_M):
+    """A handle sized for max_M rows runs every M <= max_M: the workspace sized
+    at create covers whichever kernel, K slices and hand-over each row count
+    takes (per-group GEMV in fixed-point K slices at M = 1, x-in-LDS GEMM with
+    partials or words above), repeats are bit-identical, sampled rows match."""
+    N, K = 4096, 9216
+    say("row counts up to", max_M)
+    u = Uniform(N, K, 3, cfg_id=58, max_M=max_M)
+    rows = np.random.default_rng(max_M).choice(N, 48, replace=False)
+    for M in range(1, max_M + 1):
+        x = S.activations(M, K, cfg_id=58, tensor_id=700 + M)
+        xd = dev_f16(x)
+        y1 = u.lin.run(xd)
+        y2 = u.lin.run(xd)
+        torch.cuda.synchronize()
+        assert sha(y1) == sha(y2)
+        r = O.gemv_uniform_rows(x, u.words, u.scales, N, K, 3, rows)
+        err = O.normwise_rel_err(y1.cpu().numpy().astype(np.float64)[:, rows], r)
+        assert err <= TOL, (M, err)
