@@ -240,6 +240,10 @@ template <int B, int NQ, int ND>
 __device__ __forceinline__ void gemv_q_body(const RunArgs& a, const SegDev (&sd)[2], int tile, int q_beg, int q_end,
                                             char* smem, float (&R)[2]) {
   using P = Pair<B>;
+  // several widths inline one body per width behind a branch: keep the
+  // compiler from hoisting the bodies' common loads above it (they would then
+  // hold registers through every body)
+  __asm__ volatile("" ::: "memory");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.G, G4 = a.G4;
