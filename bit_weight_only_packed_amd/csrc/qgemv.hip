@@ -148,8 +148,9 @@ Launch choose(const qg_plan* h, int M, bool dual = false, int force_v2 = -1) {
     // about 2 quads (a one-wave workgroup per slice: q/o 6.4 us against 7.0 in
     // one slice, q|k|v stacked 7.1 against 7.2; wider matrices gain nothing:
     // gate/up 10.4-10.9 either way, gate|up stacked 16.7 in one slice against
-    // 16.9-18.8); beyond K = 8192 of about 9 quads (down: 10.6 against 14.7)
-    if (L.S <= 0) L.S = dual ? 1 : (G4 > 16 ? (G4 + 8) / 9 : (h->total_tiles <= 1024 ? (G4 + 1) / 2 : 1));
+    // 16.9-18.8); beyond K = 8192 of about 7 quads (down: 10.6-10.8 against
+    // 14.7 in one slice; with 2- and 3-bit columns 11.8 against 12.9 in 4)
+    if (L.S <= 0) L.S = dual ? 1 : (G4 > 16 ? (G4 + 6) / 8 : (h->total_tiles <= 1024 ? (G4 + 1) / 2 : 1));
     L.S = std::min(L.S, G4);
     const int g4s = (G4 + L.S - 1) / L.S;
     if (L.NW <= 0) {
