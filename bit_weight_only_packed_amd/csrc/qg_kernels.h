@@ -359,9 +359,11 @@ __device__ __forceinline__ void gemv_q_body(const RunArgs& a, const SegDev (&sd)
 }
 
 // several widths (BF = 0): the three bodies' registers are allocated together;
-// capped so that six waves fit on each SIMD (the decode shapes' grids stay resident)
+// capped so that seven waves fit on each SIMD (the decode shapes' grids of
+// 4- and 5-wave workgroups then stay resident; the cap spills 4 registers,
+// an eight-wave cap spills 17 and is slower than no cap)
 template <int NQ, bool DUAL, int BF>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(BF == 0 && !DUAL && NQ <= 2 ? 6 : 1)))
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(BF == 0 && !DUAL && NQ <= 2 ? 7 : 1)))
 void k_gemv_q(RunArgs a) {
   extern __shared__ __align__(16) char smem[];
   constexpr int ND = DUAL ? 2 : 1;
