@@ -46,6 +46,12 @@ def parse():
                         "weight copies, then a 256 MiB device copy (the counter calibration), then exit")
     p.add_argument("--profile-rows", type=int, default=1, choices=(1, 8, 16, 32), metavar="M",
                    help="rows of the profiled gate/up product (1 = the GEMV, more = the verify GEMM)")
+    p.add_argument("--profile-mlp", type=int, default=0, metavar="REPS",
+                   help="profiling mode: REPS graph replays of the fused mixed-width MLP at --profile-rows rows "
+                        "(1, 8 or 32) over weight copies of >= 1 GiB, then exit")
+    p.add_argument("--profile-trellis", type=int, default=0, metavar="REPS",
+                   help="profiling mode: REPS graph replays of the trellis product on the 5120x17408 shape at "
+                        "--profile-rows rows (1 or 8) over weight copies of >= 1 GiB, then exit")
     return p.parse_args()
 
 
@@ -60,6 +66,62 @@ def src_hash() -> str:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def profile_other(args, torch, Q, S, dev, dw, df16, capture, time_graph):
+    """Profiling modes for the fused MLP and the trellis product: one HIP graph
+    over weight copies of at least 1 GiB (every launch reads its weights from
+    HBM), replayed 2 + REPS times, then one JSON line."""
+    M = args.profile_rows
+    if args.profile_mlp:
+        if M not in (1, 8, 32):
+            sys.exit("--profile-mlp takes --profile-rows 1, 8 or 32")
+        H, I = S.MLP["hidden"], S.MLP["inter"]
+        cb_gu = S.column_bits(I, 0.2, 4, cfg_id=S.CFG_MLP, tensor_id=S.T_MASK)
+        cb_dn = S.column_bits(H, 0.2, 2, cfg_id=S.CFG_MLP, tensor_id=S.T_MASK + 100)
+        wg = S.mixed_code_words(cb_gu, H, cfg_id=S.CFG_MLP, tensor_id=S.T_CODES)
+        wu = S.mixed_code_words(cb_gu, H, cfg_id=S.CFG_MLP, tensor_id=S.T_CODES + 10)
+        wd = S.mixed_code_words(cb_dn, I, cfg_id=S.CFG_MLP, tensor_id=S.T_CODES + 20)
+        sg = S.scales(I, H, cfg_id=S.CFG_MLP, tensor_id=S.T_SCALE)
+        su = S.scales(I, H, cfg_id=S.CFG_MLP, tensor_id=S.T_SCALE + 10)
+        sd = S.scales(H, I, cfg_id=S.CFG_MLP, tensor_id=S.T_SCALE + 20)
+        nbytes = wg.nbytes + wu.nbytes + wd.nbytes + sg.nbytes + su.nbytes + sd.nbytes
+        R = int(np.ceil((1 << 30) / nbytes))
+        dg, du, dd = (dw(wg), df16(sg)), (dw(wu), df16(su)), (dw(wd), df16(sd))
+        mlps = [(Q.QLinear(dg[0], dg[1], H, I, col_bits=cb_gu, max_M=32),
+                 Q.QLinear(du[0], du[1], H, I, col_bits=cb_gu, max_M=32),
+                 Q.QLinear(dd[0], dd[1], I, H, col_bits=cb_dn, max_M=32)) for _ in range(R)]
+        x = df16(S.activations(M, H, cfg_id=S.CFG_DECODE, tensor_id=S.T_X + M))
+        out = torch.empty((M, H), dtype=torch.float16, device=dev)
+
+        def f():
+            for (a, b, c) in mlps:
+                Q.mlp(a, b, c, x, out=out)
+        reps, what = args.profile_mlp, f"fused mlp M={M} 5120->17408->5120 mixed widths"
+    else:
+        if M not in (1, 8):
+            sys.exit("--profile-trellis takes --profile-rows 1 or 8")
+        K, N = 5120, 17408
+        cbk = df16(S.codebook(cfg_id=S.CFG_TRELLIS))
+        tw = S.trellis_words(N, K, cfg_id=S.CFG_TRELLIS, tensor_id=S.T_TRELLIS + 40)
+        ts = S.scales(N, K, cfg_id=S.CFG_TRELLIS, tensor_id=S.T_SCALE + 40)
+        nbytes = tw.nbytes + ts.nbytes
+        R = int(np.ceil((1 << 30) / nbytes))
+        dtw = torch.from_numpy(np.ascontiguousarray(tw).view(np.int16).copy()).to(dev)
+        tl = [Q.QLinear(dtw, df16(ts), K, N, trellis=True, codebook=cbk, max_M=8) for _ in range(R)]
+        x = df16(S.activations(M, K, cfg_id=S.CFG_DECODE, tensor_id=S.T_X + M))
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+        def f():
+            for t in tl:
+                t.run(x, out=out)
+        reps, what = args.profile_trellis, f"trellis M={M} 5120x17408"
+    torch.cuda.synchronize()
+    g = capture(f)
+    time_graph(g, 2)
+    us = time_graph(g, reps) / (reps * R) * 1e6
+    print(json.dumps({"profile": what, "launches": reps * R, "graph_us_per_launch": round(us, 3),
+                      "weight_bytes": nbytes, "src_hash": src_hash()}), flush=True)
 
 
 def main():
@@ -84,6 +146,35 @@ def main():
 
     def df16(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16).copy()).to(dev)
+
+    def capture(fn, reps=1):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3  # s
+
+    if args.profile_mlp or args.profile_trellis:
+        profile_other(args, torch, Q, S, dev, dw, df16, capture, time_graph)
+        return
 
     # ---------------- weights: layer set, R copies ----------------
     shapes = S.LAYER_SET
@@ -117,31 +208,6 @@ def main():
         for i, sh in enumerate(shapes):
             lins[r][i].run(xk[(M, sh["K"])], out=ys[M][:, : sh["N"]] if sh["N"] == 17408 else
                            ys[M].view(-1)[: M * sh["N"]].view(M, sh["N"]))
-
-    def capture(fn, reps=1):
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for _ in range(2):
-                fn()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                fn()
-        torch.cuda.synchronize()
-        return g
-
-    def time_graph(g, n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(n):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3  # s
 
     if args.profile_gate:
         # the dominant kernel alone, launched exactly as the per-shape timing below
