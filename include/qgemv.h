@@ -79,7 +79,7 @@ typedef struct qg_plan* qg_handle;
 typedef enum {
   QG_OK = 0,
   QG_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misalignment, mismatched handles      */
-  QG_ERR_UNSUPPORTED = -2,  /* no gfx950 device, or a format/size this build does not handle  */
+  QG_ERR_UNSUPPORTED = -2,  /* no gfx950 device, or a format/size the library does not handle  */
   QG_ERR_DEVICE = -3,       /* a HIP call or kernel launch failed                                */
   QG_ERR_OOM = -4           /* device allocation failed                                          */
 } qg_status;
