@@ -112,6 +112,30 @@ __device__ __forceinline__ void tr_gather(const char* cbl, const uint32_t (&addr
 // fp32 (the sums of 128 fp16 values with signs are exact to fp32 rounding), one
 // rounding to fp16 at the end.
 // ---------------------------------------------------------------------------
+// value of lane l ^ 4: quad mirror (3 - i) then half-row mirror (7 - i)
+__device__ __forceinline__ float dpp_xor4(float v) {
+  const int m = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x1B, 0xF, 0xF, false);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, m, 0x141, 0xF, 0xF, false));
+}
+
+// the six cross-lane butterfly stages of a 128-point transform held as two
+// values per lane (elements lane and lane + 64), partner lane l ^ h for
+// h = 32, 16, 8, 4, 2, 1: the two across rows through the LDS crossbar, the
+// four inside a 16-lane row as DPP moves (no LDS round trip)
+__device__ __forceinline__ void fwht_lanes(float& a, float& b, int lane) {
+  auto stage = [&](float pa, float pb, int h) {
+    const bool upper = (lane & h) != 0;
+    a = upper ? pa - a : a + pa;
+    b = upper ? pb - b : b + pb;
+  };
+  stage(__shfl_xor(a, 32), __shfl_xor(b, 32), 32);
+  stage(__shfl_xor(a, 16), __shfl_xor(b, 16), 16);
+  stage(dpp_row_ror<8>(a), dpp_row_ror<8>(b), 8);  // (i + 8) mod 16 = i ^ 8
+  stage(dpp_xor4(a), dpp_xor4(b), 4);
+  stage(dpp_xor2(a), dpp_xor2(b), 2);
+  stage(dpp_xor1(a), dpp_xor1(b), 1);
+}
+
 __global__ __launch_bounds__(256) void k_fwht(const uint16_t* __restrict__ x, uint16_t* __restrict__ xr, int M,
                                               int K) {
   const int G = K / 128;
@@ -126,13 +150,7 @@ __global__ __launch_bounds__(256) void k_fwht(const uint16_t* __restrict__ x, ui
     a = s;
     b = d;
   }
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) {
-    const float pa = __shfl_xor(a, h), pb = __shfl_xor(b, h);
-    const bool upper = (lane & h) != 0;
-    a = upper ? pa - a : a + pa;
-    b = upper ? pb - b : b + pb;
-  }
+  fwht_lanes(a, b, lane);
   const float f = 0.08838834764831845f;  // 2^-3.5
   uint16_t* q = xr + (size_t)m * K + (size_t)g * 128;
   q[lane] = f2h(a * f);
@@ -303,13 +321,7 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
         p = su;
         q = df;
       }
-#pragma unroll
-      for (int hh = 32; hh >= 1; hh >>= 1) {
-        const float pp = __shfl_xor(p, hh), pq = __shfl_xor(q, hh);
-        const bool upper = (lane & hh) != 0;
-        p = upper ? pp - p : p + pp;
-        q = upper ? pq - q : q + pq;
-      }
+      fwht_lanes(p, q, lane);
       const float f = 0.08838834764831845f;  // 2^-3.5
       xr[g * 128 + lane] = f2h(p * f);
       xr[g * 128 + 64 + lane] = f2h(q * f);
