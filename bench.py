@@ -4,16 +4,20 @@
 A step is one decode pass of a 27B-class dense layer's linear set -- q, k, v, o
 (5120x5120, 5120x1024 x2, 5120x5120), gate, up (5120x17408) and down
 (17408x5120), K x N = in x out -- at M = 1 activation row, 3-bit codes with one
-fp16 scale per 128 weights, fp16 activations.  All inputs are seeded and
-synthetic and already resident in HBM.  The weights exist in R distinct copies
-(>= 1 GiB in total, four times the 256 MB Infinity Cache) and consecutive steps
-use consecutive copies, so every step streams its weights from HBM.  Steps are
-replayed from a captured HIP graph (no host launch gaps between kernels).
+fp16 scale per 128 weights, fp16 activations, one launch per matrix.  All
+inputs are seeded and synthetic and already resident in HBM.  The weights
+exist in R distinct copies (>= 1 GiB in total, four times the 256 MB Infinity
+Cache) and consecutive steps use consecutive copies, so every step streams its
+weights from HBM.  Steps are replayed from captured HIP graphs (no host launch
+gaps between kernels): exactly --warmup untimed steps, then --trials timed
+trials of exactly --steps steps each; the line reports the median trial.
 
 Printed (one JSON line): effective weight GB/s of the step (value), per-shape
-us/call at M = 1, 8, 16, 32 and the M=32 / M=1 ratio, the fused MLP with mixed
-widths, the roofline entry of the dominant kernel (the M = 1 GEMV on the
-5120x17408 gate/up shape) and the CPU oracle's rate on a bounded sample.
+us/call at M = 1, 8, 16, 32 and the M=32 / M=1 ratio, each M = 1 call against
+the measured streaming read of the same bytes, the fused MLP with mixed widths,
+the trellis format, the roofline entry of the dominant kernel (the M = 1 GEMV
+on the 5120x17408 gate/up shape) and the CPU oracle on bounded samples of every
+workload.
 """
 from __future__ import annotations
 
@@ -37,6 +41,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--trials", type=int, default=5, help="timed trials of --steps steps each (median reported)")
     p.add_argument("--copies", type=int, default=0, help="weight copies (default: enough for >= 1 GiB)")
     p.add_argument("--quick", action="store_true", help="skip the verify/MLP/CPU sections")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -63,6 +68,8 @@ def src_hash() -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "bit_weight_only_packed_amd", "csrc")
     for f in sorted(os.listdir(d)):
+        if not f.endswith((".h", ".hip")):
+            continue
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -235,28 +242,46 @@ def main():
         return
 
     # ---------------- the timed step: layer set at M = 1 ----------------
-    def all_copies(M=1):
+    def steps_graph(n, M=1):
+        """One graph of n consecutive steps, on weight copies 0 .. n-1."""
         def f():
-            for r in range(R):
+            for r in range(n):
                 layer_step(r, M)
-        return f
+        return capture(f)
 
-    g_layer = capture(all_copies(1))
-    reps_w = max(1, args.warmup // R)
-    reps_t = max(1, args.steps // R)
-    time_graph(g_layer, reps_w)
-    steps = reps_t * R
-    t_s = time_graph(g_layer, reps_t)
-    ms_per_step = t_s * 1e3 / steps
-    value = per_copy / (t_s / steps) / 1e9
-    log(f"layer set M=1: {ms_per_step * 1e3:.2f} us/step, {value:.0f} GB/s ({100 * value / HBM_PEAK_GBS:.1f} % of 8 TB/s)")
+    def run_steps(n, g_full, g_rem):
+        for _ in range(n // R):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+
+    K_steps, W_steps = max(1, args.steps), max(0, args.warmup)
+    g_layer = steps_graph(R)
+    g_krem = steps_graph(K_steps % R) if K_steps % R else None
+    g_wrem = steps_graph(W_steps % R) if W_steps % R else None
+    torch.cuda.synchronize()
+    run_steps(W_steps, g_layer, g_wrem)
+    trial_s = []
+    for _ in range(max(1, args.trials)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        run_steps(K_steps, g_layer, g_krem)
+        e1.record()
+        torch.cuda.synchronize()
+        trial_s.append(e0.elapsed_time(e1) / 1e3)
+    t_s = float(np.median(trial_s))
+    ms_per_step = t_s * 1e3 / K_steps
+    value = per_copy / (t_s / K_steps) / 1e9
+    log(f"layer set M=1: {ms_per_step * 1e3:.2f} us/step, {value:.0f} GB/s ({100 * value / HBM_PEAK_GBS:.1f} % of 8 TB/s); "
+        f"trials {[round(t * 1e6 / K_steps, 2) for t in trial_s]} us/step")
     result = {
         "metric": "effective weight GB/s & % HBM roofline; us/call at M=1 and M=8/32 verify",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": reps_w * R,
+        "steps": K_steps,
+        "warmup": W_steps,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -265,14 +290,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode GEMV, M=1, 27B-class layer set q,k,v,o,gate,up,down "
                                "(5120x5120 x2, 5120x1024 x2, 5120x17408 x2, 17408x5120), 3-bit codes, "
-                               "fp16 scale per 128, fp16 x", "M": 1, "weight_bytes_per_step": per_copy,
-                   "weight_copies": R, "pct_of_8TBs": round(100 * value / HBM_PEAK_GBS, 2)},
+                               "fp16 scale per 128, fp16 x, one launch per matrix", "M": 1,
+                   "weight_bytes_per_step": per_copy, "weight_copies": R,
+                   "pct_of_8TBs": round(100 * value / HBM_PEAK_GBS, 2)},
+        "trials": {"n": len(trial_s), "us_per_step": [round(t * 1e6 / K_steps, 3) for t in trial_s]},
     }
     if args.only_layer:
         print(json.dumps(result), flush=True)
         return
 
     # ---------------- per shape, per M ----------------
+    def graph_us(g, launches, reps=20, trials=5):
+        """us per launch: median over trials of `reps` replays of graph g."""
+        time_graph(g, 2)
+        return float(np.median([time_graph(g, reps) / (reps * launches) * 1e6 for _ in range(trials)]))
+
     def shape_us(i, M, reps=20):
         sh = shapes[i]
         out = ys[M][:, : sh["N"]] if sh["N"] == 17408 else ys[M].view(-1)[: M * sh["N"]].view(M, sh["N"])
@@ -280,9 +312,21 @@ def main():
         def f():
             for r in range(R):
                 lins[r][i].run(xk[(M, sh["K"])], out=out)
-        g = capture(f)
-        time_graph(g, 2)
-        return time_graph(g, reps) / (reps * R) * 1e6
+        return graph_us(capture(f), R, reps)
+
+    def stream_us(nbytes, reps=20):
+        """The measured read roofline: a plain streaming read of nbytes (buffer
+        copies of >= 1 GiB in rotation, like the weights), us per launch."""
+        nb = (nbytes + 15) // 16 * 16
+        Rs = int(np.ceil((1 << 30) / nb))
+        bufs = [torch.empty(nb // 4, dtype=torch.int32, device=dev) for _ in range(Rs)]
+
+        def f():
+            for b in bufs:
+                Q.stream_read(b)
+        us = graph_us(capture(f), Rs, reps)
+        del bufs
+        return us
 
     distinct = {"qo": 0, "kv": 1, "gateup": 4, "down": 6}
     per_shape = {}
@@ -297,15 +341,20 @@ def main():
                 row["GBs_M1"] = round(wb / us / 1e3, 1)
                 row["pct_8TBs_M1"] = round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1)
         row["ratio_M32_M1"] = round(row["us_M32"] / row["us_M1"], 3)
+        row["ratio_M8_M1"] = round(row["us_M8"] / row["us_M1"], 3)
+        st = stream_us(wb)
+        row["stream_read_us"] = round(st, 3)
+        row["pct_of_stream_read_M1"] = round(100 * st / row["us_M1"], 1)
         per_shape[name] = row
         log(name, row)
     result["per_shape"] = per_shape
+    ls_stream = stream_us(per_copy)
+    result["stream_read_layer_set_us"] = round(ls_stream, 3)
+    result["pct_of_stream_read"] = round(100 * ls_stream * R / (t_s * 1e6 / K_steps * R), 1)
 
     layer_us = {}
     for M in (1, 8, 16, 32):
-        g = capture(all_copies(M))
-        time_graph(g, 1)
-        layer_us[M] = time_graph(g, max(1, reps_t // 2)) / (max(1, reps_t // 2) * R) * 1e6
+        layer_us[M] = graph_us(steps_graph(R, M), R, reps=3)
     result["layer_set_us"] = {f"M{M}": round(v, 3) for M, v in layer_us.items()}
     result["layer_set_ratio_M32_M1"] = round(layer_us[32] / layer_us[1], 3)
     result["layer_set_ratio_M8_M1"] = round(layer_us[8] / layer_us[1], 3)
@@ -337,9 +386,7 @@ def main():
                 for r in range(R):
                     for j in range(4):
                         flins[r][j].run(xk[(M, fks[j])], out=fys[M][j])
-            g = capture(fstep)
-            time_graph(g, 1)
-            fused_us[M] = time_graph(g, max(1, reps_t // 2)) / (max(1, reps_t // 2) * R) * 1e6
+            fused_us[M] = graph_us(capture(fstep), R, reps=3)
         result["layer_set_fused"] = {
             "launches": 4, "note": "q|k|v and gate|up as one launch each over stacked rows",
             **{f"us_M{M}": round(v, 3) for M, v in fused_us.items()},
@@ -448,32 +495,104 @@ def main():
 
 
 def cpu_baseline():
-    """The oracle (unpack, dequantise, fp64 matmul) on every 2nd output column of
-    each layer-set matrix at M = 1; reported as weight GB/s of that sample."""
+    """The oracle (unpack, dequantise, fp64 matmul) timed on the host cores on a
+    bounded sample of every workload: for each matrix shape a sample of output
+    columns (the per-column work is the same for every column), the rest
+    scaled by the column count; reported per workload and row count as us/call
+    and weight GB/s, with the dequantisation and matmul phases apart, at the
+    BLAS thread count of this process and at one thread."""
     import oracle as O
     import qg_synth as S
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count()
-    t_total, bytes_total = 0.0, 0
-    for i, sh in enumerate(S.LAYER_SET):
-        N, K = sh["N"], sh["K"]
-        w = S.uniform_code_words(N, K, 3, cfg_id=S.CFG_DECODE, tensor_id=S.T_CODES + 10 * i)
-        sc = S.scales(N, K, cfg_id=S.CFG_DECODE, tensor_id=S.T_SCALE + 10 * i)
-        x = S.activations(1, K, cfg_id=S.CFG_DECODE, tensor_id=S.T_X + 1)
-        rows = np.arange(N)
+    except Exception:  # pragma: no cover
+        threadpool_limits, cores = None, os.cpu_count()
+
+    def timed(f):
         t0 = time.perf_counter()
-        O.gemv_uniform_rows(x, w, sc, N, K, 3, rows)
-        t_total += time.perf_counter() - t0
-        bytes_total += len(rows) * (K * 3 // 8 + (K // 128) * 2)
-    gbs = bytes_total / t_total / 1e9
-    log(f"cpu oracle: {bytes_total} B in {t_total:.2f} s = {gbs:.3f} GB/s ({cores} threads)")
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "seconds": round(t_total, 2),
-            "sample": "all output columns of q,k,v,o,gate,up,down at M=1 "
-                      f"({bytes_total} weight bytes, one full layer set)"}
+        out = f()
+        return out, time.perf_counter() - t0
+
+    def uniform_case(N, K, Ms, ncols, bits=3, cfg=S.CFG_DECODE, tid=0):
+        """us/call per M: dequant of the sampled columns, matmul of each M, scaled to N columns."""
+        G = K // 128
+        cols = np.arange(min(ncols, N))
+        w = S.code_words(len(cols) * K * bits // 32, cfg_id=cfg, tensor_id=S.T_CODES + 10 * tid)
+        sc = S.scales(len(cols), K, cfg_id=cfg, tensor_id=S.T_SCALE + 10 * tid)
+        wd, t_dq = timed(lambda: O.dequant_uniform(O.unpack_uniform(w, len(cols), K, bits), sc, bits))
+        scale = N / len(cols)
+        res = {}
+        for M in Ms:
+            x = S.activations(M, K, cfg_id=cfg, tensor_id=S.T_X + M)
+            _, t_mm = timed(lambda: O.matmul(x, wd))
+            res[M] = (t_dq * scale * 1e6, t_mm * scale * 1e6)
+        return res, (N * K * bits // 8 + N * G * 2)
+
+    def trellis_case(N, K, Ms, nrows):
+        nb = max(1, min(nrows, N) // 16)
+        tw = S.trellis_words(16 * nb, K, cfg_id=S.CFG_TRELLIS, tensor_id=S.T_TRELLIS)
+        ts = S.scales(16 * nb, K, cfg_id=S.CFG_TRELLIS, tensor_id=S.T_SCALE)
+        cb = S.codebook(cfg_id=S.CFG_TRELLIS)
+        wd, t_dq = timed(lambda: O.trellis_dequant(O.trellis_states(tw, 16 * nb, K), cb, ts))
+        scale = N / (16 * nb)
+        res = {}
+        for M in Ms:
+            x = S.activations(M, K, cfg_id=S.CFG_TRELLIS, tensor_id=S.T_X + M)
+            _, t_mm = timed(lambda: O.matmul(O.rotate(x), wd))
+            res[M] = (t_dq * scale * 1e6, t_mm * scale * 1e6)
+        return res, (N * K * 3 // 8 + N * (K // 128) * 2)
+
+    def fmt(res, nbytes):
+        out = {}
+        for M, (dq, mm) in res.items():
+            out[f"M{M}"] = {"us": round(dq + mm, 1), "dequant_us": round(dq, 1), "matmul_us": round(mm, 1),
+                            "weight_GBs": round(nbytes / (dq + mm) / 1e3, 4)}
+        return out
+
+    t_start = time.perf_counter()
+    report = {}
+    # tiny reference (all of it)
+    r, nb = uniform_case(512, 512, (1,), 512, cfg=S.CFG_TINY)
+    report["tiny_512x512"] = fmt(r, nb)
+    # decode and verify: the four distinct layer shapes, 512 sampled columns each
+    ls_us = {M: 0.0 for M in (1, 8, 16, 32)}
+    ls_bytes = 0
+    for name, (K, N, mult) in {"qo": (5120, 5120, 2), "kv": (5120, 1024, 2), "gateup": (5120, 17408, 2),
+                               "down": (17408, 5120, 1)}.items():
+        r, nb = uniform_case(N, K, (1, 8, 16, 32), 2048)
+        report[name] = fmt(r, nb)
+        ls_bytes += mult * nb
+        for M, (dq, mm) in r.items():
+            ls_us[M] += mult * (dq + mm)
+    report["layer_set"] = {f"M{M}": {"us": round(v, 1), "weight_GBs": round(ls_bytes / v / 1e3, 4)}
+                           for M, v in ls_us.items()}
+    # fused MLP (mixed widths counted at 3 bits: the oracle's work per weight is the same)
+    gu, nbg = uniform_case(17408, 5120, (1, 8, 32), 1024, tid=1)
+    dn, nbd = uniform_case(5120, 17408, (1, 8, 32), 1024, tid=2)
+    report["mlp"] = {f"M{M}": {"us": round(2 * sum(gu[M]) + sum(dn[M]), 1)} for M in (1, 8, 32)}
+    # trellis, gate/up shape
+    r, nb = trellis_case(17408, 5120, (1, 8), 512)
+    report["trellis_gateup"] = fmt(r, nb)
+    t_all = time.perf_counter() - t_start
+    # one thread: the layer set at M = 1
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            us1 = 0.0
+            for name, (K, N, mult) in {"qo": (5120, 5120, 2), "kv": (5120, 1024, 2), "gateup": (5120, 17408, 2),
+                                       "down": (17408, 5120, 1)}.items():
+                r, nb = uniform_case(N, K, (1,), 1024)
+                us1 += mult * sum(r[1])
+        one = {"us": round(us1, 1), "weight_GBs": round(ls_bytes / us1 / 1e3, 4)}
+    v = ls_bytes / ls_us[1] / 1e3
+    log(f"cpu oracle: layer set M=1 {ls_us[1]:.0f} us = {v:.3f} GB/s ({cores} threads), 1 thread "
+        f"{one}; sampled in {t_all:.1f} s")
+    return {"value": round(v, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "the first 2048 output columns of each distinct 27B-class layer shape (1024 at one thread "
+                      "and for the MLP, 512 rows of the trellis shape), scaled to whole matrices; the value is the "
+                      "layer set q,k,v,o,gate,up,down at M=1",
+            "seconds": round(t_all, 1), "one_thread_layer_set_M1": one, "per_workload": report}
 
 
 if __name__ == "__main__":

@@ -15,7 +15,7 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["QGError", "lib", "QLinear", "mlp", "declared_symbols", "LIB_PATH", "HEADER_PATH"]
+__all__ = ["QGError", "lib", "QLinear", "mlp", "stream_read", "declared_symbols", "LIB_PATH", "HEADER_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemv.so")
@@ -25,6 +25,9 @@ QG_OK, QG_ERR_INVALID_ARG, QG_ERR_UNSUPPORTED, QG_ERR_DEVICE, QG_ERR_OOM = 0, -1
 FMT_UNIFORM, FMT_TRELLIS3 = 0, 1
 FLAG_X_PREROTATED = 1
 GROUP = 128
+# pins (include/qgemv.h): force a kernel or hand-over
+PIN_M1_PERGROUP, PIN_M1_RUNS, PIN_PARTIALS, PIN_WORDS = 1 << 0, 1 << 1, 1 << 2, 1 << 3
+PIN_XS_T1, PIN_XS_T2, PIN_TRELLIS_ROT_LAUNCH = 1 << 4, 1 << 5, 1 << 6
 
 
 class QGError(RuntimeError):
@@ -33,11 +36,15 @@ class QGError(RuntimeError):
         self.status = status
 
 
+class _Launch(ctypes.Structure):
+    _fields_ = [("tiles", ctypes.c_int32), ("waves", ctypes.c_int32), ("splits", ctypes.c_int32)]
+
+
 class _Desc(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("format", ctypes.c_int32), ("bits", ctypes.c_int32), ("col_bits", ctypes.c_void_p),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("pins", ctypes.c_uint32), ("launch", _Launch * 3)]
 
 
 _lib = None
@@ -60,12 +67,13 @@ def lib() -> ctypes.CDLL:
     L.qg_last_error.argtypes = []
     L.qg_last_error.restype = ctypes.c_char_p
     L.qgemv_weight_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
-    L.qgemv_set_launch.argtypes = [vp, i32, i32, i32, i32]
+    L.qg_stream_read.argtypes = [vp, ctypes.c_int64, vp]
     L.qgemv_debug_unpack.argtypes = [vp, vp, vp]
     L.qgemv_debug_dequant.argtypes = [vp, vp, u16p, vp]
+    L.qgemv_debug_operand.argtypes = [vp, vp, vp, vp, vp]
     L.qgemv_debug_trellis.argtypes = [vp, vp, vp]
-    for f in ("qgemv_create", "qgemv_run", "qmlp_run", "qgemv_destroy", "qgemv_weight_bytes",
-              "qgemv_set_launch", "qgemv_debug_unpack", "qgemv_debug_dequant", "qgemv_debug_trellis"):
+    for f in ("qgemv_create", "qgemv_run", "qmlp_run", "qgemv_destroy", "qgemv_weight_bytes", "qg_stream_read",
+              "qgemv_debug_unpack", "qgemv_debug_dequant", "qgemv_debug_operand", "qgemv_debug_trellis"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -101,10 +109,13 @@ class QLinear:
     words, any 4-byte dtype; trellis: uint16 words [N/16][K/16][48], any 2-byte
     dtype).  scales: CUDA fp16 tensor [N][K/128].  bits: 2/3/4, or col_bits
     (host array of per-column widths).  codebook: CUDA fp16 [65536] (trellis).
+    pins: PIN_* bits; launch: optional {row class 0/1/2: (tiles, waves, splits)}
+    launch-geometry overrides (both fixed at create).
     """
 
     def __init__(self, codes, scales, K: int, N: int, bits: int = 3, col_bits=None, max_M: int = 32,
-                 trellis: bool = False, codebook=None, prerotated: bool = False, stream=None):
+                 trellis: bool = False, codebook=None, prerotated: bool = False, stream=None,
+                 pins: int = 0, launch=None):
         d = _Desc()
         d.K, d.N, d.group_size = int(K), int(N), GROUP
         d.format = FMT_TRELLIS3 if trellis else FMT_UNIFORM
@@ -119,6 +130,9 @@ class QLinear:
         d.scales = _ptr(scales)
         d.codebook = _ptr(codebook) if codebook is not None else None
         d.flags = FLAG_X_PREROTATED if prerotated else 0
+        d.pins = int(pins)
+        for c, (t, w, s) in (launch or {}).items():
+            d.launch[int(c)] = _Launch(int(t), int(w), int(s))
         h = ctypes.c_void_p()
         _check(lib().qgemv_create(ctypes.byref(h), ctypes.byref(d), int(max_M), _stream(stream)))
         self._h = h
@@ -143,9 +157,6 @@ class QLinear:
         _check(lib().qgemv_weight_bytes(self._h, ctypes.byref(b)))
         return int(b.value)
 
-    def set_launch(self, M: int, tiles: int = 0, waves: int = 0, splits: int = 0):
-        _check(lib().qgemv_set_launch(self._h, int(M), int(tiles), int(waves), int(splits)))
-
     def debug_unpack(self, stream=None):
         import torch
         c = torch.full((self.N, self.K), -1, dtype=torch.int32, device="cuda")
@@ -158,6 +169,15 @@ class QLinear:
         q = torch.zeros((self.N, self.K), dtype=torch.float16, device="cuda") if with_q16 else None
         _check(lib().qgemv_debug_dequant(self._h, _ptr(w), _ptr(q) if q is not None else None, _stream(stream)))
         return w, q
+
+    def debug_operand(self, stream=None):
+        """The verify GEMM's operand decode: (codes int32, operand fp16 bits, w fp32), all [N][K]."""
+        import torch
+        c = torch.full((self.N, self.K), -1, dtype=torch.int32, device="cuda")
+        b = torch.zeros((self.N, self.K), dtype=torch.int16, device="cuda")
+        w = torch.full((self.N, self.K), float("nan"), dtype=torch.float32, device="cuda")
+        _check(lib().qgemv_debug_operand(self._h, _ptr(c), _ptr(b), _ptr(w), _stream(stream)))
+        return c, b, w
 
     def debug_trellis(self, stream=None):
         import torch
@@ -175,6 +195,11 @@ class QLinear:
             self.close()
         except Exception:
             pass
+
+
+def stream_read(buf, stream=None):
+    """Plain streaming read of a CUDA tensor's bytes (the measured read roofline)."""
+    _check(lib().qg_stream_read(_ptr(buf), int(buf.numel() * buf.element_size()), _stream(stream)))
 
 
 def mlp(gate: QLinear, up: QLinear, down: QLinear, x, out=None, stream=None):

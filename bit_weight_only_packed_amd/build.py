@@ -1,31 +1,56 @@
-"""Build the HIP library libqgemv.so in-tree for gfx950 (hipcc, no torch involved)."""
+"""Build the HIP library libqgemv.so in-tree for gfx950 (hipcc, no torch involved).
+
+Each kernel family is a translation unit of its own (csrc/*.hip); they are
+compiled in parallel to objects under csrc/_build and linked into one shared
+library."""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "csrc", "qgemv.hip")
+CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(CSRC, "_build")
 OUT = os.path.join(HERE, "libqgemv.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-    # keep the compiler from forming packed-fp32 VALU ops (see the build notes)
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", OUT + ".tmp", SRC]
+def sources() -> list:
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(OBJ, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = [ex.submit(_run, [hipcc, *HIPCC_FLAGS, "-c", "-o", o, s], verbose) for s, o in zip(srcs, objs)]
+        results = [f.result() for f in futs]
+    bad = [(s, r) for s, r in zip(srcs, results) if r.returncode != 0]
+    for s, r in bad:
+        sys.stderr.write(f"--- {s}\n{r.stdout}{r.stderr}")
+    if bad:
+        raise RuntimeError("hipcc failed building libqgemv.so")
+    r = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", OUT + ".tmp", *objs], verbose)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libqgemv.so")
+        raise RuntimeError("hipcc failed linking libqgemv.so")
     os.replace(OUT + ".tmp", OUT)
     return OUT
 

@@ -27,10 +27,10 @@
 // (c_lo * 2^(p-24), c_hi * 2^(p-24)) -- exact, no conversion instruction.
 // gfx950's v_dot2_f32_f16 and v_mfma_f32_16x16x32_f16 consume such subnormal
 // fp16 operands exactly.  Codes at offsets beyond the exact range are first
-// shifted down.  The M = 1 GEMVs scale each x by 2^-class of the code position
-// it meets (or, in the per-group-staged GEMV, keep one fp32 accumulator per
-// offset "class" and rescale them per group); the MFMA path shifts every pair to
-// offset 1 so a whole operand shares one scale.
+// shifted down.  The M = 1 GEMVs stage each x multiplied by 2^(e - class) of
+// the code position it meets, e a power-of-two block exponent of its 32-element
+// quarter (qg_stage.h), so one dot2 chain serves every class; the MFMA path
+// shifts every pair to offset 1 so a whole operand shares one scale.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -78,6 +78,11 @@ template <int B> __device__ constexpr uint32_t class_scale_pair(int i) {
   const uint32_t h = (uint32_t)(15 - Pair<B>::cls(i)) << 10;
   return h | (h << 16);
 }
+// fp16x2 bits of (2^p, 2^p): undoes the class scaling of a staged x pair
+template <int B> __device__ constexpr uint32_t class_unscale_pair(int i) {
+  const uint32_t h = (uint32_t)(15 + Pair<B>::cls(i)) << 10;
+  return h | (h << 16);
+}
 
 // ---- MFMA decode: every pair at offset 1 (value 2*c*2^-24 = c*2^-23)
 template <int B>
@@ -95,10 +100,21 @@ __device__ __forceinline__ void decode_off1(const uint32_t (&w)[B], uint32_t (&r
   }
 }
 
-// fp16 bits of -o_b * 2^-23 = -(2^B - 1) * 2^-24: the per-weight offset at the MFMA scale
-template <int B> __device__ constexpr uint32_t off1_offset_pair() {
-  return ((0x8000u | ((1u << B) - 1u)) * 0x10001u);
+// -o_b * 2^-23: the code offset at the MFMA scale (codes decoded at offset 1,
+// value c * 2^-23); a group's MFMA chain starts from this times the group sum
+// of x, so it yields 2^-23 * sum x * (c - o_b)
+template <int B> __host__ __device__ constexpr float off1_ko() {
+  return -0.5f * (float)((1 << B) - 1) * 1.1920928955078125e-07f;
 }
+// -o_b * 2^-24: the same at the GEMV scale (codes decoded at their class
+// offsets, met by x staged at 2^-class: every product lands at 2^-24)
+template <int B> __host__ __device__ constexpr float cls_ko() {
+  return -0.5f * (float)((1 << B) - 1) * 5.9604644775390625e-08f;
+}
+
+// the lane's group gi of a quad decoded for the MFMA B operand (offset 1)
+template <int B>
+__device__ __forceinline__ void decode_group_off1(const uint32_t (&w)[4 * B], int gi, uint32_t (&r)[16]);
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 
@@ -172,6 +188,20 @@ template <int B>
 __device__ __forceinline__ void quad_group(const uint32_t (&w)[4 * B], int i, uint32_t (&g)[B]) {
 #pragma unroll
   for (int u = 0; u < B; ++u) g[u] = w[i * B + u];
+}
+
+template <int B>
+__device__ __forceinline__ void decode_group_off1(const uint32_t (&w)[4 * B], int gi, uint32_t (&r)[16]) {
+  uint32_t g[B];
+  quad_group<B>(w, gi, g);
+  decode_off1<B>(g, r);
+}
+
+template <int B>
+__device__ __forceinline__ void decode_group_classes(const uint32_t (&w)[4 * B], int gi, uint32_t (&r)[16]) {
+  uint32_t g[B];
+  quad_group<B>(w, gi, g);
+  decode_classes<B>(g, r);
 }
 
 // Word u of group g of lane `lane` in tile t (plain pointer form; G4 quads per tile)

@@ -31,11 +31,10 @@
 // entry in LDS, whose fp16 value is used as is (exact); the scale multiplies
 // each group's fp32 partial sum.
 #pragma once
-#include "qg_kernels.h"
+#include "qg_common.h"
 
 namespace qg {
 
-constexpr int TR_CB_BYTES = 65536 * 2;   // codebook in LDS
 
 // ---------------------------------------------------------------------------
 // create-time re-layout (one thread per unit and lane)
@@ -158,36 +157,19 @@ __global__ __launch_bounds__(256) void k_fwht(const uint16_t* __restrict__ x, ui
 }
 
 // ---------------------------------------------------------------------------
-// GEMV (MT = 0, M = 1) and GEMM (MT = 1: M <= 16, MT = 2: M <= 32); the GEMM
-// form is selected only with QG_TRELLIS=stream (the banded kernel below is
-// the default for more than one row).
-//
-// One workgroup per compute unit holds the codebook in LDS for the whole launch.
-// The RB * G units are split into W equal contiguous ranges in row-block-major
-// order, one per wave (stream-K): a wave walks its range with the next units'
-// loads in flight (PD register sets in rotation), accumulates while
-// the row block stays the same and leaves a partial sum per row block it
-// touches.  A row block's partials sit
-// in fixed slots (slot = wave - first wave of the row block); the wave that
-// completes a row block (device-scope arrival counter) adds the slots in slot
-// order and stores the fp16 result.  The slot order fixes every rounding, so
-// repeated runs are bit-identical.  At M = 1, where at most 63 waves share a
-// row block, the partials go into fixed-point output words instead (see
-// fx_word): one atomic round trip instead of the store, the count and the
-// reads, and a sum that does not depend on the order of arrival.
+// M = 1 GEMV (dot2).  One workgroup per compute unit holds the codebook in LDS
+// for the whole launch.  The RB * G units are split into W equal contiguous
+// ranges in row-block-major order, one per wave (stream-K): a wave walks its
+// range with the next units' loads in flight (PD register sets in rotation),
+// accumulates while the row block stays the same and hands a partial sum on
+// per row block it touches.  Where at most 63 waves share a row block the
+// partials go into fixed-point output words (qg_common.h): one atomic round
+// trip, and a sum that does not depend on the order of arrival.  Otherwise a
+// row block's partials sit in fixed slots (slot = wave - first wave of the row
+// block); the wave that completes the row block (device-scope arrival counter)
+// adds the slots in slot order and stores the fp16 result.  Either way,
+// repeated runs are bit-identical.
 // ---------------------------------------------------------------------------
-struct TrArgs {
-  const uint32_t* codes;   // [U][64][3]
-  const uint16_t* scales;  // [U][16]
-  const uint16_t* cb;      // [65536] fp16
-  const uint16_t* x;       // [M][K] fp16, rotated
-  uint16_t* y;             // [M][N] fp16
-  float* partial;          // [RB][maxseg][M][16]
-  int* counters;           // [RB], zero between launches
-  unsigned long long* acc; // M = 1: [N] fixed-point output words (zero between launches), or NULL: partials
-  int M, K, N, G, RB, maxseg, W;
-  int64_t U;
-};
 
 // first wave whose range holds unit x (ranges [w*U/W, (w+1)*U/W))
 __device__ __forceinline__ int tr_wave_of(int64_t x, int64_t U, int W) {
@@ -197,22 +179,17 @@ __device__ __forceinline__ int tr_wave_of(int64_t x, int64_t U, int W) {
   return w;
 }
 
-// XL (M = 1): the rotated x sits in LDS beside the codebook (the kernel rotates
-// it itself), so a unit loads only its codes and scale
-constexpr int TR_XL_BYTES = 32768;           // rotated x in LDS: K <= 16384
-constexpr int TR_XL_GMAX = 8;                // groups per wave to rotate (G <= 128, 16 waves)
 
-template <int MT, bool XL = false>
+template <bool XL>
 struct TrUnit {
-  static constexpr int XR = MT == 0 ? 1 : MT;  // activation row blocks held
-  static constexpr int loads = 2 + (XL ? 0 : 4 * XR);  // load instructions per unit
-  u3_t z;                                      // code words
-  uint32_t s;                                  // this lane's scale (fp16 in the low half)
-  uint4 xv[XR][4];                             // activations: 32 k of row (16*mt + (lane & 15)), or of row 0 (M = 1)
+  static constexpr int loads = 2 + (XL ? 0 : 4);  // load instructions per unit
+  u3_t z;                                         // code words
+  uint32_t s;                                     // this lane's scale (fp16 in the low half)
+  uint4 xv[4];                                    // activations: the lane's 32 k (not XL)
 };
 
-template <int MT, bool XL = false>
-__device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT, XL>& t, int64_t u, int g, bool live, int lane) {
+template <bool XL>
+__device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<XL>& t, int64_t u, int g, bool live, int lane) {
   const int uu = live ? 1 : 0;
   const int64_t uc = live ? u : 0;
   const int kq = lane >> 4;
@@ -221,21 +198,16 @@ __device__ __forceinline__ void tr_load(const TrArgs& a, TrUnit<MT, XL>& t, int6
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + uc * 16, uu * 32u);
   t.s = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(lane & 14) * 2u, 0, 0);
   if (lane & 1) t.s >>= 16;
-  // one descriptor over all of x (wave-uniform, so no per-lane descriptor
-  // loop); the lane's row and quarter go into the offset, and a row past M
-  // (or a dead unit) takes an offset past the range: zeros, no memory access
   if constexpr (XL) return;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(a.x), (uint32_t)a.M * (uint32_t)a.K * 2u);
+  // one descriptor over all of x (wave-uniform, so no per-lane descriptor
+  // loop); the lane's quarter goes into the offset, and a dead unit takes an
+  // offset past the range: zeros, no memory access
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(a.x), (uint32_t)a.K * 2u);
+  const uint32_t off = live ? (uint32_t)(((size_t)g * 128 + 32 * kq) * 2) : 0x80000000u;
 #pragma unroll
-  for (int mt = 0; mt < TrUnit<MT, XL>::XR; ++mt) {
-    const int m = MT == 0 ? 0 : 16 * mt + (lane & 15);
-    const bool ok = live && m < a.M;
-    const uint32_t off = ok ? (uint32_t)(((size_t)m * a.K + (size_t)g * 128 + 32 * kq) * 2) : 0x80000000u;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const u4_t q = __builtin_amdgcn_raw_buffer_load_b128(rx, off + (uint32_t)v * 16u, 0, 0);
-      t.xv[mt][v] = make_uint4(q.x, q.y, q.z, q.w);
-    }
+  for (int v = 0; v < 4; ++v) {
+    const u4_t q = __builtin_amdgcn_raw_buffer_load_b128(rx, off + (uint32_t)v * 16u, 0, 0);
+    t.xv[v] = make_uint4(q.x, q.y, q.z, q.w);
   }
 }
 
@@ -253,21 +225,11 @@ __device__ __forceinline__ bool tr_arrive_last(int* counter, int nseg, int lane)
   return true;
 }
 
-// NWMAX: waves per workgroup the kernel is built for (16 keeps four waves on
-// each SIMD; the 32-row variant needs the registers of eight); PD: units whose
-// loads are in flight while one is computed.
-template <int MT> struct TrShape {
-  static constexpr int NWMAX = MT == 2 ? 8 : 16;
-  static constexpr int PD = MT == 2 ? 3 : 2;
-};
-
-template <int MT, bool XL = false>
-__global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
-  static_assert(!XL || MT == 0, "x in LDS: M = 1 only");
+template <bool XL = false>
+__global__ __launch_bounds__(64 * TR_NW) void k_trellis(TrArgs a) {
   // static (not dynamic) LDS: its address is a compile-time constant, so the
   // gathers use the decoded byte address as is
   __shared__ __align__(16) char smem[TR_CB_BYTES + (XL ? TR_XL_BYTES : 0)];
-  constexpr int XR = TrUnit<MT, XL>::XR;
   const int lane = threadIdx.x & 63;
   const int NW = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -276,33 +238,31 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
   // counts rely on it); waves past W only help load the codebook
   const int64_t lo = gw < a.W ? (int64_t)gw * a.U / a.W : a.U;
   const int64_t hi = gw < a.W ? (int64_t)(gw + 1) * a.U / a.W : a.U;
-  constexpr int PD = TrShape<MT>::PD;
+  constexpr int PD = TR_PD;
   // codebook -> LDS straight from memory (buffer loads to LDS, 1 KiB per wave
   // instruction), then this wave's first units: waiting for the codebook does
   // not wait for those
   {
     const __amdgpu_buffer_rsrc_t rcb = make_rsrc(uniform_ptr(a.cb), TR_CB_BYTES);
-    const int NWv = blockDim.x >> 6;
-    for (int ci = wave; ci < TR_CB_BYTES / 1024; ci += NWv)
+    for (int ci = wave; ci < TR_CB_BYTES / 1024; ci += NW)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rcb, (__attribute__((address_space(3))) void*)(smem + (size_t)ci * 1024),
                                                16, (uint32_t)(ci * 1024 + lane * 16), 0, 0, 0);
   }
   // XL: this wave's groups of the unrotated x (groups wave, wave + NW, ...)
   uint16_t xa[XL ? TR_XL_GMAX : 1], xb[XL ? TR_XL_GMAX : 1];
   if constexpr (XL) {
-    const int NWv = blockDim.x >> 6;
 #pragma unroll
     for (int i = 0; i < TR_XL_GMAX; ++i) {
-      const int g = wave + i * NWv;
+      const int g = wave + i * NW;
       xa[i] = g < a.G ? a.x[(size_t)g * 128 + lane] : (uint16_t)0;
       xb[i] = g < a.G ? a.x[(size_t)g * 128 + 64 + lane] : (uint16_t)0;
     }
   }
-  TrUnit<MT, XL> c[PD];
+  TrUnit<XL> c[PD];
 #pragma unroll
-  for (int i = 0; i < PD; ++i) tr_load<MT, XL>(a, c[i], lo + i, (int)((lo + i) % a.G), lo + i < hi, lane);
+  for (int i = 0; i < PD; ++i) tr_load<XL>(a, c[i], lo + i, (int)((lo + i) % a.G), lo + i < hi, lane);
   {
-    constexpr int n = PD * TrUnit<MT, XL>::loads;  // loads issued after the codebook's (and x's)
+    constexpr int n = PD * TrUnit<XL>::loads;  // loads issued after the codebook's (and x's)
     static_assert(n < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
   }
@@ -310,10 +270,9 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
     // rotate each group as k_fwht does (same operations in the same order, so
     // the same fp16 values) and keep it in LDS after the codebook
     uint16_t* xr = reinterpret_cast<uint16_t*>(smem + TR_CB_BYTES);
-    const int NWv = blockDim.x >> 6;
 #pragma unroll
     for (int i = 0; i < TR_XL_GMAX; ++i) {
-      const int g = wave + i * NWv;
+      const int g = wave + i * NW;
       if (g >= a.G) break;
       float p = h2f(xa[i]), q = h2f(xb[i]);
       {
@@ -331,16 +290,13 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
   if (lo >= hi) return;
   const char* cbl = smem;
   float acc1 = 0.0f;
-  f4_t acc[XR];
-#pragma unroll
-  for (int mt = 0; mt < XR; ++mt) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // row block and group of the unit being computed, group of the next unit to
   // load (kept as counters: no division per unit)
   int rb = (int)(lo / a.G), g = (int)(lo - (int64_t)rb * a.G);
   int gpf = (int)((lo + PD) % a.G);
-  // one unit: decode, contract, reload the same registers with unit u + 3, and
-  // flush at the end of a row block or of the range
-  auto step = [&](TrUnit<MT, XL>& cu, int64_t u) {
+  // one unit: decode, contract, reload the same registers with unit u + PD, and
+  // hand the row block on at the end of a row block or of the range
+  auto step = [&](TrUnit<XL>& cu, int64_t u) {
     const uint32_t z2 = cu.z.x, z1 = cu.z.y, z0 = cu.z.z;
     const uint32_t nz2 = tr_from_next_row_lane(z2), nz1 = tr_from_next_row_lane(z1);
     uint32_t addr[32];
@@ -348,37 +304,24 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
     uint32_t pr[16];
     tr_gather(cbl, addr, pr);
     const float s = h2f((uint16_t)(cu.s & 0xFFFFu));
-    if constexpr (MT == 0) {
-      uint4 xv[4];
+    uint4 xv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if constexpr (XL)
-          xv[v] = *reinterpret_cast<const uint4*>(smem + TR_CB_BYTES + ((size_t)g * 128 + 32 * (lane >> 4)) * 2 + v * 16);
-        else
-          xv[v] = cu.xv[0][v];
-      }
-      float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        d0 = dot2(pr[4 * v + 0], xv[v].x, d0);
-        d1 = dot2(pr[4 * v + 1], xv[v].y, d1);
-        d0 = dot2(pr[4 * v + 2], xv[v].z, d0);
-        d1 = dot2(pr[4 * v + 3], xv[v].w, d1);
-      }
-      acc1 = __builtin_fmaf(s, d0 + d1, acc1);
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < XR; ++mt) {
-        f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          cg = mfma16(__builtin_bit_cast(h8_t, cu.xv[mt][v]), as_h8(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]),
-                      cg);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(s, cg[e], acc[mt][e]);
-      }
+    for (int v = 0; v < 4; ++v) {
+      if constexpr (XL)
+        xv[v] = *reinterpret_cast<const uint4*>(smem + TR_CB_BYTES + ((size_t)g * 128 + 32 * (lane >> 4)) * 2 + v * 16);
+      else
+        xv[v] = cu.xv[v];
     }
-    tr_load<MT, XL>(a, cu, u + PD, gpf, u + PD < hi, lane);
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      d0 = dot2(pr[4 * v + 0], xv[v].x, d0);
+      d1 = dot2(pr[4 * v + 1], xv[v].y, d1);
+      d0 = dot2(pr[4 * v + 2], xv[v].z, d0);
+      d1 = dot2(pr[4 * v + 3], xv[v].w, d1);
+    }
+    acc1 = __builtin_fmaf(s, d0 + d1, acc1);
+    tr_load<XL>(a, cu, u + PD, gpf, u + PD < hi, lane);
     gpf = gpf + 1 == a.G ? 0 : gpf + 1;
     const bool last_unit = u + 1 == hi;
     g = g + 1 == a.G ? 0 : g + 1;
@@ -388,66 +331,32 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
     const int w1 = tr_wave_of((int64_t)rb * a.G + a.G - 1, a.U, a.W);
     const int nseg = w1 - w0 + 1, seg = gw - w0;
     const int n = lane & 15;
-    float* base = a.partial + ((size_t)rb * a.maxseg) * a.M * 16;
-    if constexpr (MT == 0) {
-      float v = acc1;
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (nseg == 1) {
-        if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(v);
-      } else if (a.acc) {
-        // fixed-point words (see fx_word): one round trip; the arrival that
-        // completes the count stores the result and re-arms the word
-        if (lane < 16) {
-          unsigned long long* w = a.acc + (size_t)rb * 16 + n;
-          const unsigned long long mine = fx_word(v);
-          const unsigned long long before = fx_add(w, mine);
-          if ((int)(before & 63ull) == nseg - 1) {
-            a.y[(size_t)rb * 16 + n] = f2h(fx_value(before + mine));
-            __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      } else {
-        if (lane < 16) st_partial(base + (size_t)seg * 16 + n, v);
-        if (tr_arrive_last(a.counters + rb, nseg, lane)) {
-          const float t = sum_partials(base + n, 16, nseg, seg, v);
-          if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(t);
+    float* base = a.partial + ((size_t)rb * a.maxseg) * 16;
+    float v = acc1;
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (nseg == 1) {
+      if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(v);
+    } else if (a.acc) {
+      // fixed-point words: one round trip; the arrival that completes the
+      // count stores the result and re-arms the word
+      if (lane < 16) {
+        unsigned long long* w = a.acc + (size_t)rb * 16 + n;
+        const unsigned long long mine = fx_word(v);
+        const unsigned long long before = fx_add(w, mine);
+        if (fx_count(before) == nseg - 1) {
+          a.y[(size_t)rb * 16 + n] = f2h(fx_value(before + mine));
+          fx_rearm(w);
         }
       }
-      acc1 = 0.0f;
     } else {
-      const int mq = lane >> 4;
-      if (nseg == 1) {
-#pragma unroll
-        for (int mt = 0; mt < XR; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int m = 16 * mt + 4 * mq + e;
-            if (m < a.M) a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(acc[mt][e]);
-          }
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < XR; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int m = 16 * mt + 4 * mq + e;
-            if (m < a.M) st_partial(base + ((size_t)seg * a.M + m) * 16 + n, acc[mt][e]);
-          }
-        if (tr_arrive_last(a.counters + rb, nseg, lane)) {
-#pragma unroll
-          for (int mt = 0; mt < XR; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int m = 16 * mt + 4 * mq + e;
-              if (m >= a.M) continue;
-              const float t = sum_partials(base + (size_t)m * 16 + n, (size_t)a.M * 16, nseg, seg, acc[mt][e]);
-              a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(t);
-            }
-        }
+      if (lane < 16) st_partial(base + (size_t)seg * 16 + n, v);
+      if (tr_arrive_last(a.counters + rb, nseg, lane)) {
+        const float t = sum_partials(base + n, 16, nseg, seg, v);
+        if (lane < 16) a.y[(size_t)rb * 16 + n] = f2h(t);
       }
-#pragma unroll
-      for (int mt = 0; mt < XR; ++mt) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    acc1 = 0.0f;
     rb = rb_next;
   };
   for (int64_t u = lo; u < hi; u += PD) {
@@ -472,26 +381,7 @@ __global__ __launch_bounds__(64 * TrShape<MT>::NWMAX) void k_trellis(TrArgs a) {
 // stream-K kernel (fixed slots, arrival counter, sums in slot order), or, when
 // the outputs are few, in fixed-point output words (one atomic round trip).
 // ---------------------------------------------------------------------------
-template <int MT> struct TbShape {
-  static constexpr int NW = MT == 2 ? 8 : 16;  // waves = row blocks per workgroup
-  static constexpr int PD = MT == 2 ? 2 : 3;   // groups whose copies and code loads are in flight
-  static constexpr int XB = PD + 1;            // x slots
-  static constexpr int MR = 16 * MT;           // rows of an x slot
-  static constexpr int XRD = MR / NW;          // 256-byte row copies per wave per group
-  static constexpr int SLOT = MR * 256;        // bytes per x slot
-};
 
-struct TbArgs {
-  const uint32_t* codes;   // [U][64][3]
-  const uint16_t* scales;  // [U][16]
-  const uint16_t* cb;      // [65536] fp16
-  const uint16_t* x;       // [M][K] fp16, rotated
-  uint16_t* y;             // [M][N] fp16
-  float* partial;          // [RB][maxseg][M][16] (S > 1, acc NULL)
-  int* counters;           // [RB], zero between launches
-  unsigned long long* acc; // [M][N] fixed-point output words (S > 1), zero between launches; or NULL
-  int M, K, N, G, RB, maxseg, S;
-};
 
 // 4 bytes per lane from a buffer into LDS at lds + 4 * lane (lds wave-uniform),
 // as assembly so the compiler does not make LDS reads wait for it (the kernel
@@ -647,10 +537,10 @@ __global__ __launch_bounds__(64 * TbShape<MT>::NW) void k_trellis_band(TbArgs a)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 16 * mt + 4 * mq + e;
-        if (m >= a.M || (int)(before[mt][e] & 63ull) != S - 1) continue;
+        if (m >= a.M || fx_count(before[mt][e]) != S - 1) continue;
         unsigned long long* w = a.acc + (size_t)m * a.N + (size_t)rb * 16 + n;
         a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(fx_value(before[mt][e] + mine[mt][e]));
-        __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        fx_rearm(w);
       }
     return;
   }

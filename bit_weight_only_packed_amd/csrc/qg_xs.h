@@ -18,7 +18,10 @@
 // form the B operand.  Each group's MFMA chain starts from the offset term
 // -o * 2^-23 * sum_{k in g} x[m][k], from group sums computed once per
 // workgroup out of LDS, so the chain yields 2^-23 * sum x (c - o); the fp16
-// scale multiplies it into the fp32 accumulator.
+// scale multiplies it into the fp32 accumulator.  The fused MLP's down pass
+// (XSC) takes its x as fp16 values scaled by a power of two per (row, group)
+// (the fp32 intermediate rounded once with a block exponent, qg_misc.h), and
+// multiplies each row's chain by that row and group's 2^-e as well.
 //
 // K slices meet in one of two ways, both independent of the order of arrival.
 // Few outputs: in fixed-point words (see fx_word), one integer atomic per
@@ -30,38 +33,12 @@
 // partials of each output (several slices' loads in flight at once) and adds
 // them in slice order 0..S-1.  With one slice the result is stored directly.
 #pragma once
-#include "qg_kernels.h"
+#include "qg_common.h"
 
 namespace qg {
 
-constexpr int XS_PD = 3;  // units whose code loads are in flight per wave
 
-struct XsArgs {
-  WSet w[2];                  // w[1]: up matrix of the fused gate/up pass
-  const uint16_t* x;          // [M][K] fp16
-  uint16_t* y;                // [M][ldy] fp16 (fused pass: h)
-  float* partial;             // [ND][S][M][NP] fp32 (S > 1, acc == NULL)
-  int* counters;              // one per tile group, zero between launches
-  unsigned long long* acc;    // [ND][M][NP] fixed-point words (S > 1), zero between launches; or NULL
-  int M, K, G, G4, ldy, NP, S;
-  int GPW;                    // tile groups per workgroup
-  int wg_prefix[MAX_SEG + 1]; // workgroups (per slice) before each width segment
-  int tg_prefix[MAX_SEG + 1]; // tile groups before each width segment
-};
 
-// LDS: the x slice as [row m][group] 256-byte rows of 128 fp16, row m at
-// m * NQ KiB (a compile-time stride, so every A-fragment read is one base
-// register plus an immediate offset); the 16-byte chunk p of a row sits at
-// position p ^ (m & 15), so the 16 rows an A fragment reads fall on distinct
-// banks.  Then the group sums as [group][16 * MT] floats, then the output
-// column of each padded column of the workgroup's run (read there, not from
-// memory, so storing a result never waits behind code loads).
-__host__ __device__ constexpr size_t xs_x_bytes(int M, int NQ) { return (size_t)M * NQ * 1024; }
-__host__ __device__ constexpr size_t xs_sum_bytes(int MT, int NQ) { return (size_t)NQ * 4 * 16 * MT * 4; }
-__host__ __device__ constexpr size_t xs_col_bytes(int GPW, int T) { return ((size_t)GPW * T * 64 + 1023) / 1024 * 1024; }
-__host__ __device__ constexpr size_t xs_lds_bytes(int M, int MT, int NQ, int GPW, int T) {
-  return xs_x_bytes(M, NQ) + xs_sum_bytes(MT, NQ) + xs_col_bytes(GPW, T);
-}
 
 template <int B, int T, int ND>
 struct XsUnit {
@@ -92,32 +69,31 @@ __device__ __forceinline__ void xs_load(XsUnit<B, T, ND>& c, const SegDev (&sd)[
 
 // one unit: groups gl0 .. gl0 + ngr - 1 of the slice against the unit's tiles;
 // xa[mt][v]: this lane's A-fragment address of group 0 (add 256 per group)
-template <int B, int T, int MT, int ND>
+template <int B, int T, int MT, int ND, bool XSC>
 __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* const (&xa)[MT][4], const float* xsum,
-                                        int gl0, int ngr, int lane, f4_t (&R)[ND][T][MT]) {
+                                        const float* xfac, int gl0, int ngr, int lane, f4_t (&R)[ND][T][MT]) {
   const int kq = lane >> 4;
-  const float ko = -0.5f * (float)((1 << B) - 1) * 1.1920928955078125e-07f;  // -o * 2^-23
+  const float ko = off1_ko<B>();  // -o * 2^-23
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
     if (gi >= ngr) break;
     const int gl = gl0 + gi;
     h8_t A[MT][4];
-    f4_t C0[MT];
+    f4_t C0[MT], F[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) A[mt][v] = *reinterpret_cast<const h8_t*>(xa[mt][v] + gl * 256);
       // chain start: rows 16 mt + 4 kq + e (sums past M are never stored either)
       C0[mt] = *reinterpret_cast<const f4_t*>(xsum + gl * (16 * MT) + 16 * mt + 4 * kq) * ko;
+      if constexpr (XSC) F[mt] = *reinterpret_cast<const f4_t*>(xfac + gl * (16 * MT) + 16 * mt + 4 * kq);
     }
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        uint32_t g3[B];
-        quad_group<B>(c.cw[d][t], gi, g3);
         uint32_t r[16];
-        decode_off1<B>(g3, r);
+        decode_group_off1<B>(c.cw[d][t], gi, r);
         const uint32_t sw = (gi < 2) ? c.sc[d][t].x : c.sc[d][t].y;
         const float s = h2f((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
 #pragma unroll
@@ -125,6 +101,7 @@ __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* c
           f4_t cc = C0[mt];
 #pragma unroll
           for (int v = 0; v < 4; ++v) cc = mfma16(A[mt][v], as_h8(r[4 * v], r[4 * v + 1], r[4 * v + 2], r[4 * v + 3]), cc);
+          if constexpr (XSC) cc = cc * F[mt];
 #pragma unroll
           for (int e = 0; e < 4; ++e) R[d][t][mt][e] = __builtin_fmaf(s, cc[e], R[d][t][mt][e]);
         }
@@ -132,7 +109,7 @@ __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* c
   }
 }
 
-template <int B, int T, int MT, int ND, int NQ>
+template <int B, int T, int MT, int ND, int NQ, bool XSC>
 __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], int s, int q0, int nq, int tgb, int tge,
                                         int tgbase, char* smem) {
   const int lane = threadIdx.x & 63;
@@ -142,7 +119,8 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
   constexpr int RS = NQ * 1024;  // bytes per row of x in LDS
   char* xl = smem;
   float* xsum = reinterpret_cast<float*>(smem + xs_x_bytes(M, NQ));
-  int* cols = reinterpret_cast<int*>(smem + xs_x_bytes(M, NQ) + xs_sum_bytes(MT, NQ));
+  float* xfac = xsum + NQ * 4 * 16 * MT;  // XSC only
+  int* cols = reinterpret_cast<int*>(smem + xs_x_bytes(M, NQ) + (XSC ? 2 : 1) * xs_sum_bytes(MT, NQ));
   // ---- the x slice -> LDS: one wave instruction per (row m, 4 groups) = 1 KiB;
   // groups past G read zeros
   {
@@ -172,6 +150,19 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rcm, (__attribute__((address_space(3))) void*)(cols + base), 16,
                                                (uint32_t)(base + 4 * lane) * 4u, 0, 0, 0);
   }
+  // XSC: the factors of the slice's (group, row) pairs, [group][16 * MT] (rows
+  // past M and groups past G: 0), loaded into registers ahead of the code loads
+  constexpr int XFR = XSC ? NQ * MT : 1;  // factors per thread at one wave (fewer with more)
+  float xfr[XFR];
+  if constexpr (XSC) {
+#pragma unroll
+    for (int r = 0; r < XFR; ++r) {
+      const int idx = threadIdx.x + r * (int)blockDim.x;
+      const int gl = idx / (16 * MT), m = idx - gl * (16 * MT);
+      const int g = 4 * q0 + gl;
+      xfr[r] = (gl < 4 * nq && m < M && g < G) ? a.xf[(size_t)m * G + g] : 0.0f;
+    }
+  }
   // ---- this wave's tile group tgb + wave: its units are the slice's quads
   const int tg = tgb + wave;
   const bool mine = tg < tge;
@@ -185,6 +176,13 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
     constexpr int n = XS_PD * xs_loads<B, T, ND>();  // issued after the x copy
     static_assert(n < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  }
+  if constexpr (XSC) {
+#pragma unroll
+    for (int r = 0; r < XFR; ++r) {
+      const int idx = threadIdx.x + r * (int)blockDim.x;
+      if (idx < 4 * nq * 16 * MT) xfac[idx] = xfr[r];
+    }
   }
   lds_barrier();  // every wave's share of the slice has landed
   // ---- group sums of x: lane gl of a wave sums group gl of one row (reading
@@ -240,7 +238,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
   // it the wait for that unit's codes)
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    if (i < nq) xs_unit<B, T, MT, ND>(c[i % XS_PD], xa, xsum, 4 * i, min(4, G - 4 * (q0 + i)), lane, R);
+    if (i < nq) xs_unit<B, T, MT, ND, XSC>(c[i % XS_PD], xa, xsum, xfac, 4 * i, min(4, G - 4 * (q0 + i)), lane, R);
     __builtin_amdgcn_sched_barrier(0);
     if (i + XS_PD < NQ) xs_load<B, T, ND>(c[i % XS_PD], sd, tg, q0 + i + XS_PD, i + XS_PD < nq, G4, (uint32_t)lane);
     __builtin_amdgcn_sched_barrier(0);
@@ -264,7 +262,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
           if (m >= M) continue;
           const float v0 = R[0][t][mt][e] * 8388608.0f;  // 2^23
           const float v1 = R[ND - 1][t][mt][e] * 8388608.0f;
-          a.y[(size_t)m * a.ldy + n] = f2h(ND == 2 ? silu_mul(v0, v1) : v0);
+          store_y(a.y, (size_t)m * a.ldy + n, ND == 2 ? silu_mul(v0, v1) : v0, a.yf32);
         }
     }
     return;
@@ -322,16 +320,16 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = 16 * mt + 4 * mq + e;
-          if (m >= M || (int)(og[t][mt][e] & 63ull) != S - 1) continue;
+          if (m >= M || fx_count(og[t][mt][e]) != S - 1) continue;
           unsigned long long* wg = W + (size_t)m * a.NP + pc;
           float v = fx_value(og[t][mt][e] + ag[t][mt][e]);
           if constexpr (ND == 2) {
             unsigned long long* wu = wg + up_off;
             v = silu_mul(v, fx_value(fx_add(wu, 0ull)));
-            __hip_atomic_store(wu, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            fx_rearm(wu);
           }
-          __hip_atomic_store(wg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (n >= 0) a.y[(size_t)m * a.ldy + n] = f2h(v);
+          fx_rearm(wg);
+          if (n >= 0) store_y(a.y, (size_t)m * a.ldy + n, v, a.yf32);
         }
     }
     return;
@@ -418,14 +416,16 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
       for (int e = 0; e < 4; ++e) {
         const int m = 16 * mt + 4 * mq + e;
         if (m >= M) continue;
-        a.y[(size_t)m * a.ldy + n] = f2h(ND == 2 ? silu_mul(acc[0][t][mt][e], acc[ND - 1][t][mt][e]) : acc[0][t][mt][e]);
+        store_y(a.y, (size_t)m * a.ldy + n,
+                ND == 2 ? silu_mul(acc[0][t][mt][e], acc[ND - 1][t][mt][e]) : acc[0][t][mt][e], a.yf32);
       }
   }
 }
 
 // NQ: the most quads a slice may have (the kernel is straight-line code over them)
-template <int T, int MT, bool DUAL, int BF, int NQ>
+template <int T, int MT, bool DUAL, int BF, int NQ, bool XSC>
 __global__ __launch_bounds__(512) void k_gemm_xs(XsArgs a) {
+  static_assert(!(DUAL && XSC), "the fused gate/up pass reads plain fp16 x");
   extern __shared__ __align__(16) char smem[];
   constexpr int ND = DUAL ? 2 : 1;
   const int S = a.S, G4 = a.G4;
@@ -440,9 +440,11 @@ __global__ __launch_bounds__(512) void k_gemm_xs(XsArgs a) {
   const int tgb = (pw - a.wg_prefix[si]) * a.GPW, tge = min(tgb + a.GPW, ngr);
   const int q0 = (int)((int64_t)s * G4 / S), q1 = (int)((int64_t)(s + 1) * G4 / S);
   const int bits = sd[0].bits;
-  if (BF == 2 || (BF == 0 && bits == 2)) xs_body<2, T, MT, ND, NQ>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
-  else if (BF == 3 || (BF == 0 && bits == 3)) xs_body<3, T, MT, ND, NQ>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
-  else xs_body<4, T, MT, ND, NQ>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
+  if (BF == 2 || (BF == 0 && bits == 2))
+    xs_body<2, T, MT, ND, NQ, XSC>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
+  else if (BF == 3 || (BF == 0 && bits == 3))
+    xs_body<3, T, MT, ND, NQ, XSC>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
+  else xs_body<4, T, MT, ND, NQ, XSC>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
 }
 
 }  // namespace qg

@@ -22,7 +22,7 @@
  *                   into a 65536-entry fp16 codebook; w = codebook[state] * s.
  *                   The activations are rotated by the normalised 128-point
  *                   Walsh-Hadamard transform per 128-group before the product
- *                   (trellis family: EXL3 of the OrcaSAQ2 page).
+ *                   (trellis family: EXL3 of the OrcaSAQ2 page, intro).
  *
  * Canonical (input) layouts, all little-endian:
  *   x        fp16 [M][K] row-major, y fp16 [M][N] row-major.
@@ -40,21 +40,28 @@
  * Ownership.  qgemv_create copies and re-lays-out codes, scales and codebook
  * into device memory owned by the handle, synchronises the given stream and
  * returns; the caller may free its inputs afterwards.  qgemv_destroy frees
- * everything the handle owns.  qgemv_run / qmlp_run allocate nothing: they
+ * everything the handle owns.  The run entry points allocate nothing: they
  * enqueue kernels on the given stream and return; x, y and out stay
  * caller-owned and must stay valid until that stream work completes.
  *
- * Concurrency.  A handle is immutable after create, but it owns its split-K
+ * Handles are immutable after create: every launch choice (including the
+ * optional overrides and pins of the descriptor) is fixed there, and the
+ * library reads no environment variable on a run.  A handle owns its split-K
  * workspace (fp32 partials, arrival counters and fixed-point column words,
- * which every run leaves re-armed) and one MLP staging buffer, so runs that
- * use the same handle must be ordered (same stream, or caller-ordered).
- * Different handles are independent.  A kernel that faulted may leave the
- * workspace un-armed: destroy and re-create the handle after a device error.
+ * which every run leaves re-armed) and the fused MLP's intermediate buffers, so
+ * runs that use the same handle must be ordered (same stream, or
+ * caller-ordered).  Different handles are independent.  A kernel that faulted
+ * may leave the workspace un-armed: destroy and re-create the handle after a
+ * device error.
  *
- * Determinism.  Every reduction either runs in a fixed order or adds exact
+ * Determinism ("Outputs are bit-exact repeatable", results paragraph of the
+ * OrcaSAQ2 page).  Every reduction either runs in a fixed order or adds exact
  * fixed-point integers (whose sum does not depend on the order of arrival);
  * no floating-point atomics are used: for the same handle and the same
  * inputs, y is bit-identical across calls, streams and processes.
+ *
+ * Non-finite inputs.  A NaN or infinite activation, scale or partial sum makes
+ * the outputs it reaches NaN (or +-inf where a single fp32 chain carries it).
  *
  * Errors.  Every entry point returns a qg_status; on failure a message is
  * available from qg_last_error() (thread-local, valid until the next call on
@@ -90,7 +97,36 @@ enum {
   QG_FLAG_X_PREROTATED = 1u << 0 /* TRELLIS3: x already rotated, skip the Walsh-Hadamard step */
 };
 
+/* Pins (qg_weight_desc.pins): force a kernel or hand-over that the built-in
+ * choice takes only for other shapes.  For tests that cover every variant and
+ * for launch sweeps; 0 keeps the built-in (measured) choice. */
+enum {
+  QG_PIN_M1_PERGROUP = 1u << 0, /* UNIFORM, M = 1: the per-group GEMV (default from 256 tiles up)    */
+  QG_PIN_M1_RUNS = 1u << 1,     /* UNIFORM, M = 1: the per-tile-run GEMV (default below 256 tiles)  */
+  QG_PIN_PARTIALS = 1u << 2,    /* K slices / trellis row blocks meet through fp32 partials summed
+                                   in slice order (default: fixed-point words where they fit)       */
+  QG_PIN_WORDS = 1u << 3,       /* UNIFORM, M >= 2: K slices meet through fixed-point words whenever
+                                   at most 63 slices meet                                            */
+  QG_PIN_XS_T1 = 1u << 4,       /* UNIFORM, M >= 2: one 16-column tile per tile group               */
+  QG_PIN_XS_T2 = 1u << 5,       /* UNIFORM, M >= 2: two tiles per tile group                        */
+  QG_PIN_TRELLIS_ROT_LAUNCH = 1u << 6 /* TRELLIS3, M = 1: rotate x in a launch of its own            */
+};
+
 enum { QG_GROUP = 128, QG_MAX_M = 32 };
+
+/* Optional launch geometry of one row class; 0 in a field keeps the built-in
+ * choice.  Meaning (UNIFORM handles):
+ *   M = 1, per-group GEMV: `waves` waves per workgroup splitting the K slice
+ *     (1..16), `splits` K slices across workgroups; `tiles` unused.
+ *   M = 1, per-tile-run GEMV: `tiles` waves per 16-column tile (each takes a
+ *     run of at most 8 quads of 512 k), `waves` waves per workgroup (1..8).
+ *   M >= 2: `tiles` (or `waves`) tile groups per workgroup (1..8, one per
+ *     wave), `splits` K slices across workgroups.
+ * A geometry the compiled kernels cannot take fails with QG_ERR_INVALID_ARG at
+ * create or on the run that needs it. */
+typedef struct {
+  int32_t tiles, waves, splits;
+} qg_launch;
 
 typedef struct {
   int32_t K;                /* in-features; multiple of 128                                   */
@@ -103,25 +139,39 @@ typedef struct {
   const uint16_t* scales;   /* device, fp16 bits [N][K/128]; 16-byte aligned                   */
   const uint16_t* codebook; /* device, fp16 bits [65536]; TRELLIS3 only                        */
   uint32_t flags;           /* QG_FLAG_*                                                       */
+  uint32_t pins;            /* QG_PIN_*, 0 = built-in choices                                  */
+  qg_launch launch[3];      /* per row class: [0] M = 1, [1] M = 2..16, [2] M = 17..32; zeros =
+                               built-in (zero-initialise the whole descriptor)                  */
 } qg_weight_desc;
 
-/* Validate the descriptor, check the current device is gfx950, re-lay-out the
- * weights into handle-owned device memory and size the workspace for runs of
- * up to max_M rows (1 <= max_M <= 32).  Synchronises `stream` before it
- * returns.  On failure *out is set to NULL. */
+/* Validate the descriptor, check the current device is gfx950 (the pages'
+ * kernels target RDNA and refuse other GPUs -- OrcaSAQ2 page, "Supported GPUs";
+ * this library likewise runs on gfx950 only), re-lay-out the weights into
+ * handle-owned device memory and size the workspace for runs of up to max_M
+ * rows (1 <= max_M <= 32, the verify batch bound of the Qwen3.8-27B page, "What
+ * we added on top of upstream").  Synchronises `stream` before it returns.  On
+ * failure *out is set to NULL and nothing stays allocated. */
 qg_status qgemv_create(qg_handle* out, const qg_weight_desc* desc, int32_t max_M, void* stream);
 
-/* y[M][N] = x[M][K] * W^T (TRELLIS3: rotate(x) * W^T unless pre-rotated).
- * x, y: device, fp16, 16-byte aligned; 1 <= M <= max_M.  Enqueues on stream. */
+/* y[M][N] = x[M][K] * W^T (TRELLIS3: rotate(x) * W^T unless pre-rotated): the
+ * decode GEMV at M = 1 ("The Rock8", decode-features table: a memory-bound
+ * decode GEMV) and the speculative-decode verify product at M = 2..32
+ * (Qwen3.8-27B page, "What we added on top of upstream": an 8-token verify,
+ * batches up to 32 rows).  x, y: device, fp16, 16-byte aligned, [M][K] and
+ * [M][N] row-major; 1 <= M <= max_M.  Enqueues on stream. */
 qg_status qgemv_run(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* stream);
 
-/* Fused MLP: out = down( SiLU(gate(x)) * up(x) ), SiLU(z) = z / (1 + e^-z).
- * gate and up: same K (= hidden), same N (= intermediate), same per-column
- * widths; down: K = intermediate.  x: device fp16 [M][hidden]; out: device
- * fp16 [M][down N].  The intermediate h = SiLU(g)*u is kept as fp16 in the
- * gate handle's staging buffer.  UNIFORM handles only. */
-qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t* x, int32_t M,
-                   uint16_t* out, void* stream);
+/* Fused MLP: out = down( SiLU(gate(x)) * up(x) ), SiLU(z) = z / (1 + e^-z)
+ * (Qwen3.8-27B page, "What we added on top of upstream": a fused MLP path for
+ * the verify batches; OrcaSAQ2 page, intro: fewer launches).  gate and up:
+ * same K (= hidden), same N (= intermediate), same per-column widths; down:
+ * K = intermediate.  x: device fp16 [M][hidden]; out: device fp16 [M][down N];
+ * both 16-byte aligned.  gate and up run as one pass over x; the intermediate
+ * h = SiLU(g)*u stays fp32 in the gate handle (for 2..32 rows it is rounded
+ * once more to fp16 with a power-of-two exponent per 128 values for the
+ * matrix cores).  UNIFORM handles only. */
+qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t* x, int32_t M, uint16_t* out,
+                   void* stream);
 
 /* Free everything the handle owns (NULL is accepted). */
 qg_status qgemv_destroy(qg_handle h);
@@ -130,33 +180,36 @@ qg_status qgemv_destroy(qg_handle h);
 const char* qg_last_error(void);
 
 /* Bytes the weights occupy in the canonical format (codes + scales; a
- * trellis codebook is not counted).  Host out-pointer. */
+ * trellis codebook is not counted): the algorithmic bytes a run must read.
+ * Host out-pointer. */
 qg_status qgemv_weight_bytes(qg_handle h, int64_t* bytes);
 
-/* Override the launch geometry used for runs with M rows in the class of
- * `M` (M = 1, or any M in 2..16, or any M in 17..32); for sweeps of launch
- * shapes.  Values <= 0 restore the built-in choice.  Meaning per kernel:
- *   M = 1, per-tile-run GEMV (the default below 256 tiles): `tiles` = waves
- *     per 16-column tile (each takes a run of at most
- *     8 quads of 512 k), `waves` = waves per workgroup (1..8), `splits` unused.
- *   M = 1, per-group GEMV: `tiles` 16-column tiles per workgroup (1), `waves`
- *     waves per workgroup splitting K (1..16), `splits` K slices across
- *     workgroups (1..16; summed in fixed-point words, exact in any order).
- *   M > 1: `tiles` tiles per wave (1, 2 or 4), `waves` waves per workgroup
- *     (1, 2, 4 or 8), `splits` K slices across workgroups (1..16).
- * Uniform-code handles only; a shape the compiled kernels cannot take fails
- * with QG_ERR_INVALID_ARG when it is run. */
-qg_status qgemv_set_launch(qg_handle h, int32_t M, int32_t tiles, int32_t waves, int32_t splits);
+/* Measurement aid, not part of the product: a plain streaming read of `bytes`
+ * (a multiple of 16) at device address buf (16-byte aligned) on `stream`, the
+ * measured read roofline the GEMV timings are set against ("The Rock8",
+ * decode-features table: a decode GEMV at 95-97 % of the measured DRAM
+ * roofline).  Reads only; writes nothing. */
+qg_status qg_stream_read(const void* buf, int64_t bytes, void* stream);
 
-/* ---- checking entry points (same device decode functions as the run kernels) ---- */
+/* ---- checking entry points: the run kernels' own device decode functions,
+ *      written back per weight so tests can compare them bit for bit ---- */
 
-/* codes: device int32 [N][K], the unpacked code of every weight (UNIFORM). */
+/* codes: device int32 [N][K], the unpacked code of every weight, as the M = 1
+ * GEMVs decode it (UNIFORM). */
 qg_status qgemv_debug_unpack(qg_handle h, int32_t* codes, void* stream);
 
-/* w: device fp32 [N][K], exact dequantised weight (c - o_b) * s (UNIFORM) or
- * codebook[state] * s (TRELLIS3).  q16 (UNIFORM, may be NULL): device fp16
- * bits [N][K] of c - o_b. */
+/* w: device fp32 [N][K], exact dequantised weight (c - o_b) * s (UNIFORM, as
+ * the M = 1 GEMVs decode it) or codebook[state] * s (TRELLIS3).  q16 (UNIFORM,
+ * may be NULL): device fp16 bits [N][K] of c - o_b. */
 qg_status qgemv_debug_dequant(qg_handle h, float* w, uint16_t* q16, void* stream);
+
+/* The verify GEMM's (M >= 2) decode of UNIFORM codes into the matrix-core
+ * operand: codes (device int32 [N][K]) read back out of the operand registers,
+ * b16 (device fp16 bits [N][K]) the operand element itself (c * 2^-23, i.e. the
+ * integer 2c as fp16 bits), and w (device fp32 [N][K]) the dequantised weight
+ * rebuilt from the operand value and the kernel's offset constant,
+ * (op - o_b * 2^-23) * 2^23 * s.  Each pointer may be NULL, not all three. */
+qg_status qgemv_debug_operand(qg_handle h, int32_t* codes, uint16_t* b16, float* w, void* stream);
 
 /* states: device uint16 [N][K], the trellis state of every weight (TRELLIS3). */
 qg_status qgemv_debug_trellis(qg_handle h, uint16_t* states, void* stream);

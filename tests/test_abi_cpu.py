@@ -20,8 +20,9 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = Q.declared_symbols()
     assert {"qgemv_create", "qgemv_run", "qmlp_run", "qgemv_destroy", "qg_last_error",
-            "qgemv_debug_unpack", "qgemv_debug_dequant", "qgemv_debug_trellis",
-            "qgemv_weight_bytes", "qgemv_set_launch"} <= set(names)
+            "qgemv_debug_unpack", "qgemv_debug_dequant", "qgemv_debug_operand", "qgemv_debug_trellis",
+            "qgemv_weight_bytes", "qg_stream_read"} <= set(names)
+    assert "qgemv_set_launch" not in names    # launch choices are fixed at create
     for n in names:
         assert hasattr(L, n), n
 
@@ -49,6 +50,25 @@ def test_create_rejects_bad_descriptor(L, kw, frag):
     assert frag in L.qg_last_error().decode()
 
 
+@pytest.mark.parametrize("cls,launch,frag", [(0, (0, 17, 0), "16 waves"), (1, (9, 0, 0), "8 tile groups"),
+                                              (2, (0, 0, 64), "63 K slices"), (1, (-1, 0, 0), "negative")])
+def test_create_rejects_bad_launch_override(L, cls, launch, frag):
+    d = _desc()
+    d.launch[cls] = Q._Launch(*launch)
+    h = ctypes.c_void_p()
+    assert L.qgemv_create(ctypes.byref(h), ctypes.byref(d), 8, None) == Q.QG_ERR_INVALID_ARG
+    assert frag in L.qg_last_error().decode()
+
+
+@pytest.mark.parametrize("pins", [Q.PIN_M1_PERGROUP | Q.PIN_M1_RUNS, Q.PIN_XS_T1 | Q.PIN_XS_T2,
+                                  Q.PIN_PARTIALS | Q.PIN_WORDS])
+def test_create_rejects_conflicting_pins(L, pins):
+    d = _desc(pins=pins)
+    h = ctypes.c_void_p()
+    assert L.qgemv_create(ctypes.byref(h), ctypes.byref(d), 8, None) == Q.QG_ERR_INVALID_ARG
+    assert "pins" in L.qg_last_error().decode()
+
+
 @pytest.mark.parametrize("max_M", [0, 33, -1])
 def test_create_rejects_bad_max_m(L, max_M):
     h = ctypes.c_void_p()
@@ -66,7 +86,9 @@ def test_null_arguments(L):
     assert L.qgemv_debug_unpack(None, 0x1000, None) == Q.QG_ERR_INVALID_ARG
     assert L.qgemv_debug_dequant(None, 0x1000, None, None) == Q.QG_ERR_INVALID_ARG
     assert L.qgemv_debug_trellis(None, 0x1000, None) == Q.QG_ERR_INVALID_ARG
-    assert L.qgemv_set_launch(None, 1, 1, 4, 1) == Q.QG_ERR_INVALID_ARG
+    assert L.qgemv_debug_operand(None, 0x1000, None, None, None) == Q.QG_ERR_INVALID_ARG
+    assert L.qg_stream_read(None, 1024, None) == Q.QG_ERR_INVALID_ARG
+    assert L.qg_stream_read(0x1000, 1000, None) == Q.QG_ERR_INVALID_ARG
     assert L.qgemv_weight_bytes(None, None) == Q.QG_ERR_INVALID_ARG
     assert L.qgemv_destroy(None) == Q.QG_OK
     assert L.qg_last_error() == b""

@@ -94,3 +94,28 @@ def test_mlp_full_size_mixed(M):
     err = O.normwise_rel_err(out.cpu().numpy().astype(np.float64)[:, rows], r)
     say("mlp full err", err)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+@pytest.mark.parametrize("name,N", [("qkv", 7168), ("gateup", 34816)])
+def test_stacked_sibling_shapes(name, N, M):
+    """The sibling projections stacked into one matrix (q|k|v: 7168 x 5120,
+    gate|up: 34816 x 5120), each with its own tuned launch, on sampled
+    columns."""
+    K = 5120
+    say("stacked", name, N, "M", M)
+    w = S.uniform_code_words(N, K, 3, cfg_id=S.CFG_DECODE, tensor_id=S.T_CODES + 900)
+    sc = S.scales(N, K, cfg_id=S.CFG_DECODE, tensor_id=S.T_SCALE + 900)
+    lin = Q.QLinear(dev_words(w), dev_f16(sc), K, N, bits=3, max_M=32)
+    x = S.activations(M, K, cfg_id=S.CFG_DECODE, tensor_id=S.T_X + 50 + M)
+    xd = dev_f16(x)
+    y = lin.run(xd)
+    y2 = lin.run(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    rows = _sample(N, n=96, seed=5)
+    r = O.gemv_uniform_rows(x, w, sc, N, K, 3, rows)
+    err = O.normwise_rel_err(y.cpu().numpy().astype(np.float64)[:, rows], r)
+    say("err", err)
+    assert err <= TOL, err
+    lin.close()

@@ -19,8 +19,7 @@ def test_graph_replays_match_eager(M, splits):
         pytest.skip("no GPU")
     say("graph", M, splits)
     N, K = 1024, 5120
-    u = Uniform(N, K, 3, cfg_id=60)
-    u.lin.set_launch(M, 0, 0, splits)
+    u = Uniform(N, K, 3, cfg_id=60, launch={0 if M == 1 else (1 if M <= 16 else 2): (0, 0, splits)})
     x = dev_f16(S.activations(M, K, cfg_id=60))
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     eager = sha(u.lin.run(x))

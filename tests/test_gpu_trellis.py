@@ -2,7 +2,7 @@
 codebook, Walsh-Hadamard-rotated activations) against the CPU oracle, through
 the C ABI: bit-exact states and dequantised weights from the checking entry
 points, outputs within the normwise 2e-3 budget at M = 1 (vector-ALU GEMV)
-and M = 2..32 (matrix-core GEMMs: banded, the default, and stream-K), pre-rotated
+and M = 2..32 (the banded matrix-core GEMM), pre-rotated
 input, bit-identical repeats and sampled columns of the 27B-class shapes."""
 from __future__ import annotations
 
@@ -31,7 +31,7 @@ def codebook():
 
 
 class Trellis:
-    def __init__(self, N, K, cb, cfg_id=80, max_M=32, prerotated=False):
+    def __init__(self, N, K, cb, cfg_id=80, max_M=32, prerotated=False, pins=0):
         self.N, self.K = N, K
         self.words = S.trellis_words(N, K, cfg_id=cfg_id)
         self.scales = S.scales(N, K, cfg_id=cfg_id)
@@ -39,7 +39,7 @@ class Trellis:
         self.dw = dev_u16(self.words)
         self.ds = dev_f16(self.scales)
         self.lin = Q.QLinear(self.dw, self.ds, K, N, trellis=True, codebook=cb[1], max_M=max_M,
-                             prerotated=prerotated)
+                             prerotated=prerotated, pins=pins)
 
     def ref(self, x, prerotated=False):
         return O.gemv_trellis(x, self.words, self.cb, self.scales, self.N, self.K, prerotated=prerotated)
@@ -113,23 +113,15 @@ def test_full_size_sampled_columns(K, N, M, codebook):
     assert np.isfinite(y).all()
 
 
-@pytest.mark.parametrize("kernel", ["stream", "banded", "banded-partials"])
+@pytest.mark.parametrize("handover", ["words", "partials"])
 @pytest.mark.parametrize("M", [2, 8, 17, 32])
 @pytest.mark.parametrize("N,K", [(48, 384), (400, 2560)])
-def test_gemm_kernels_both(kernel, M, N, K, codebook, monkeypatch):
-    """Both trellis GEMMs, forced: the stream-K kernel (every unit loads its own
-    rows of x) and the banded one (x fragments shared through LDS, K slices
-    meeting in fixed-point words, or, forced, in partials with a count)."""
-    if kernel == "stream":
-        monkeypatch.setenv("QG_TRELLIS", "stream")
-    else:
-        monkeypatch.delenv("QG_TRELLIS", raising=False)
-    if kernel == "banded-partials":
-        monkeypatch.setenv("QG_TRELLIS_HANDOVER", "partials")
-    else:
-        monkeypatch.delenv("QG_TRELLIS_HANDOVER", raising=False)
-    say("trellis gemm", kernel, M, N, K)
-    t = Trellis(N, K, codebook, cfg_id=86)
+def test_banded_gemm_handovers(handover, M, N, K, codebook):
+    """The banded GEMM (x fragments shared through LDS) with its K slices
+    meeting in fixed-point words (the default where they fit) or, pinned, in
+    partials with a count."""
+    say("trellis gemm", handover, M, N, K)
+    t = Trellis(N, K, codebook, cfg_id=86, pins=Q.PIN_PARTIALS if handover == "partials" else 0)
     x = S.activations(M, K, cfg_id=86, tensor_id=500 + M)
     y1 = _run(t.lin, x)
     y2 = _run(t.lin, x)
@@ -141,19 +133,15 @@ def test_gemm_kernels_both(kernel, M, N, K, codebook, monkeypatch):
 
 @pytest.mark.parametrize("handover", ["words", "partials"])
 @pytest.mark.parametrize("N,K", [(16, 2048), (48, 2048), (400, 2560), (5120, 2048), (4112, 4096), (112, 17408)])
-def test_gemv_handovers_both(handover, N, K, codebook, monkeypatch):
+def test_gemv_handovers_both(handover, N, K, codebook):
     """The M = 1 trellis GEMV with both row-block hand-overs, forced: the
     fixed-point words (one atomic per output and wave) and the partials with an
     arrival count.  The shapes give one to 16 waves per row block, one to three
     units per wave, ranges that start and end inside row blocks, and (112 x
     17408: 136 waves meet in one row block, more than the words count) the
     partials either way.  The two largest are checked on sampled row blocks."""
-    if handover == "partials":
-        monkeypatch.setenv("QG_TRELLIS_HANDOVER", "partials")
-    else:
-        monkeypatch.delenv("QG_TRELLIS_HANDOVER", raising=False)
     say("trellis gemv", handover, N, K)
-    t = Trellis(N, K, codebook, cfg_id=87)
+    t = Trellis(N, K, codebook, cfg_id=87, pins=Q.PIN_PARTIALS if handover == "partials" else 0)
     x = S.activations(1, K, cfg_id=87, tensor_id=600)
     y1 = _run(t.lin, x)
     y2 = _run(t.lin, x)
@@ -169,16 +157,15 @@ def test_gemv_handovers_both(handover, N, K, codebook, monkeypatch):
 
 
 @pytest.mark.parametrize("N,K", [(48, 384), (400, 2560), (1040, 5120), (96, 16384)])
-def test_gemv_rotation_in_kernel(N, K, codebook, monkeypatch):
+def test_gemv_rotation_in_kernel(N, K, codebook):
     """The M = 1 GEMV that rotates x itself into LDS gives the same bits as the
     separate rotation launch followed by the GEMV (both compute the same fp16
     rotated values), and matches the oracle."""
     t = Trellis(N, K, codebook, cfg_id=88)
+    tl = Trellis(N, K, codebook, cfg_id=88, pins=Q.PIN_TRELLIS_ROT_LAUNCH)
     x = S.activations(1, K, cfg_id=88, tensor_id=700)
     say("trellis rotation", N, K)
-    monkeypatch.setenv("QG_TRELLIS_ROT", "launch")
-    y_launch = _run(t.lin, x)
-    monkeypatch.delenv("QG_TRELLIS_ROT", raising=False)
+    y_launch = _run(tl.lin, x)
     y_kernel = _run(t.lin, x)
     assert np.array_equal(y_launch, y_kernel)
     if N * K <= (1 << 22):

@@ -65,6 +65,32 @@ def test_debug_exact_mixed_widths():
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (272, 1280)])
+def test_debug_operand_bit_exact(bits, N, K):
+    """The verify GEMM's decode into the matrix-core operand (decode_off1 and
+    its offset constant, the functions the verify kernel runs): codes read back
+    out of the operand registers, the operand's fp16 bits (c * 2^-23 = the
+    integer 2c) and the dequantised weight rebuilt from them, all bit-exact."""
+    say("operand exact", bits, N, K)
+    u = Uniform(N, K, bits, cfg_id=51)
+    c, b, w = u.lin.debug_operand()
+    np.testing.assert_array_equal(c.cpu().numpy(), u.codes())
+    np.testing.assert_array_equal(b.cpu().numpy().view(np.uint16), (2 * u.codes()).astype(np.uint16))
+    np.testing.assert_array_equal(w.cpu().numpy().astype(np.float64), u.w())
+
+
+def test_debug_operand_mixed_widths():
+    N, K = 160, 512
+    cb = S.column_bits(N, 0.3, 4, cfg_id=52)
+    cb[::7] = 2
+    u = Uniform(N, K, col_bits=cb, cfg_id=52)
+    c, b, w = u.lin.debug_operand()
+    np.testing.assert_array_equal(c.cpu().numpy(), u.codes())
+    np.testing.assert_array_equal(b.cpu().numpy().view(np.uint16), (2 * u.codes()).astype(np.uint16))
+    np.testing.assert_array_equal(w.cpu().numpy().astype(np.float64), u.w())
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("M", [1, 2, 5, 8, 16, 17, 32])
 @pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (272, 1280)])
 def test_matmul_parity(bits, M, N, K):
@@ -97,8 +123,8 @@ def test_launch_shapes(M, tiles, waves, splits):
     tile sets, uneven K slices, slices with fewer groups than waves)."""
     N, K = 400, 1280
     say("launch", M, tiles, waves, splits)
-    u = Uniform(N, K, 3, cfg_id=55)
-    u.lin.set_launch(M, tiles, waves, splits)
+    cls = 0 if M == 1 else (1 if M <= 16 else 2)
+    u = Uniform(N, K, 3, cfg_id=55, launch={cls: (tiles, waves, splits)})
     x = S.activations(M, K, cfg_id=55, tensor_id=100 + M)
     xd = dev_f16(x)
     y1 = u.lin.run(xd)
@@ -131,9 +157,9 @@ def test_error_paths_on_device():
     with pytest.raises(Q.QGError):
         u.lin.run(xb)                                 # misaligned x
     with pytest.raises(Q.QGError):
-        u.lin.set_launch(1, 1, 17, 1)                 # M = 1: at most 16 waves
+        u.relinked(launch={0: (1, 17, 1)})           # M = 1: at most 16 waves
     with pytest.raises(Q.QGError):
-        u.lin.set_launch(8, 1, 6, 1)                  # M > 1: 1, 2, 4 or 8 waves
+        u.relinked(launch={1: (9, 0, 1)})            # M > 1: at most 8 tile groups
 
 
 @pytest.mark.parametrize("max_M", [1, 2, 5, 17])
