@@ -1,5 +1,7 @@
 // k_misc.hip -- launchers of the create-time, checking and measurement kernels
 // (qg_misc.h) and of the fused MLP's block-exponent rounding of h.
+#include <algorithm>
+
 #include "qg_launch.h"
 #include "qg_misc.h"
 
@@ -32,6 +34,12 @@ hipError_t launch_h_to_f16(const float* h, uint16_t* x16, float* xf, int M, int 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int cus, hipStream_t st) {
   const int64_t n16 = bytes / 16;
   k_stream_read<<<(unsigned)(4 * cus), 512, 0, st>>>(reinterpret_cast<const uint4*>(buf), n16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  k_fill_zero<<<(unsigned)std::min<int64_t>(1024, (n16 + 255) / 256), 256, 0, st>>>(reinterpret_cast<uint4*>(p), n16);
   return hipGetLastError();
 }
 

@@ -42,5 +42,6 @@ hipError_t launch_debug_uniform(const SegDev& sg, const int32_t* col_map, int G,
                                 int32_t* codes, float* w, uint16_t* q16, hipStream_t st);
 hipError_t launch_h_to_f16(const float* h, uint16_t* x16, float* xf, int M, int K, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int cus, hipStream_t st);
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);  // bytes: a multiple of 16
 
 }  // namespace qg

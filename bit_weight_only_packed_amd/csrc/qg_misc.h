@@ -177,4 +177,11 @@ __global__ __launch_bounds__(512) void k_stream_read(const uint4* __restrict__ b
   if (acc == 0x9E3779B9u && sink) sink[0] = acc;
 }
 
+// zero [p, p + n16 * 16): a plain kernel (not a memset node), so it can sit in
+// a captured graph
+__global__ __launch_bounds__(256) void k_fill_zero(uint4* __restrict__ p, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 }  // namespace qg

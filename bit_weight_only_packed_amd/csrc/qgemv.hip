@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -43,6 +44,20 @@ struct Launch {
   int T = 0, NW = 0, S = 0;  // 0 = built-in choice
 };
 
+// Device workspace of a run: fp32 split-K partials, arrival counters and
+// fixed-point output words (counters and words zero between runs: every
+// kernel re-arms what it used), and the trellis path's rotated activations.
+struct Work {
+  float* partial = nullptr;
+  size_t partial_floats = 0;
+  int* counters = nullptr;
+  size_t ncounters = 0;
+  unsigned long long* acc64 = nullptr;
+  size_t acc64_words = 0;
+  uint16_t* xrot = nullptr;
+  size_t xrot_halves = 0;
+};
+
 struct HostSeg {
   int bits, tiles, tile0, ncols;
   uint32_t* codes = nullptr;
@@ -67,11 +82,7 @@ struct qg_plan {
   int total_tiles = 0;
   int32_t* col_map = nullptr;     // device [16*total_tiles]
   int64_t weight_bytes = 0;
-  float* partial = nullptr;       // device workspace
-  size_t partial_floats = 0;
-  int* counters = nullptr;        // device [total_tiles] split-K arrival counters, zero between runs
-  unsigned long long* acc64 = nullptr;  // device fixed-point output words, zero between runs
-  size_t acc64_words = 0;
+  Work ws;                        // the handle's own workspace (allocated at create)
   // the fused MLP's intermediate (in the gate handle): fp32 h [max_M][N], and
   // for 2..32 rows its block-exponent fp16 form [max_M][N] with the factors
   // [max_M][N/128]
@@ -82,7 +93,6 @@ struct qg_plan {
   uint32_t* tcodes = nullptr;     // device layout of trellis tiles
   uint16_t* tscales = nullptr;    // [N/16 tiles][G][16]
   uint16_t* codebook = nullptr;   // device copy, 65536 fp16
-  uint16_t* xrot = nullptr;       // device [max_M][K] fp16, rotated activations
   int64_t tr_units = 0;           // (N/16) * G
   int tr_grid = 0, tr_maxseg = 0;
   bool tr_fx = false;             // M = 1 trellis GEMV hands row blocks on through fixed-point words (acc64)
@@ -349,8 +359,8 @@ void free_plan(qg_plan* h) {
     if (s.codes) hipFree(s.codes);
     if (s.scales) hipFree(s.scales);
   }
-  void* bufs[] = {h->col_map, h->partial, h->counters, h->acc64, h->h32, h->h16, h->hf,
-                  h->tcodes,  h->tscales, h->codebook, h->xrot};
+  void* bufs[] = {h->col_map, h->ws.partial, h->ws.counters, h->ws.acc64, h->h32,     h->h16,
+                  h->hf,      h->tcodes,     h->tscales,     h->codebook, h->ws.xrot};
   for (void* p : bufs)
     if (p) hipFree(p);
   delete h;
@@ -404,14 +414,17 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   QG_HIP(hipMalloc(&h->tcodes, ncode * sizeof(uint32_t)));
   QG_HIP(hipMalloc(&h->tscales, (size_t)h->tr_units * 16 * sizeof(uint16_t)));
   QG_HIP(hipMalloc(&h->codebook, 65536 * sizeof(uint16_t)));
-  if (!(d->flags & QG_FLAG_X_PREROTATED)) QG_HIP(hipMalloc(&h->xrot, (size_t)h->max_M * K * sizeof(uint16_t)));
+  if (!(d->flags & QG_FLAG_X_PREROTATED)) {
+    h->ws.xrot_halves = (size_t)h->max_M * K;
+    QG_HIP(hipMalloc(&h->ws.xrot, h->ws.xrot_halves * sizeof(uint16_t)));
+  }
   const size_t nf = (size_t)RB * h->tr_maxseg * h->max_M * 16;
-  QG_HIP(hipMalloc(&h->partial, nf * sizeof(float)));
-  h->partial_floats = nf;
+  QG_HIP(hipMalloc(&h->ws.partial, nf * sizeof(float)));
+  h->ws.partial_floats = nf;
   // fixed-point output words [max_M][N] of the M = 1 GEMV and the banded GEMM, zero between runs
-  h->acc64_words = (size_t)h->max_M * N;
-  QG_HIP(hipMalloc(&h->acc64, h->acc64_words * sizeof(unsigned long long)));
-  QG_HIP(hipMemsetAsync(h->acc64, 0, h->acc64_words * sizeof(unsigned long long), st));
+  h->ws.acc64_words = (size_t)h->max_M * N;
+  QG_HIP(hipMalloc(&h->ws.acc64, h->ws.acc64_words * sizeof(unsigned long long)));
+  QG_HIP(hipMemsetAsync(h->ws.acc64, 0, h->ws.acc64_words * sizeof(unsigned long long), st));
   QG_HIP(hipMemcpyAsync(h->codebook, d->codebook, 65536 * sizeof(uint16_t), hipMemcpyDeviceToDevice, st));
   QG_HIP(launch_repack_trellis((const uint16_t*)d->codes, d->scales, K / 16, G, h->tr_units, h->tcodes, h->tscales, st));
   return QG_OK;
@@ -425,13 +438,13 @@ bool trellis_xl(const qg_plan* h, int M) {
          h->G <= TR_XL_GMAX * TR_NW;
 }
 
-qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, hipStream_t st) {
+qg_status run_trellis(const qg_plan* h, const Work& w, const uint16_t* x, int M, uint16_t* y, hipStream_t st) {
   const uint16_t* xr = x;
   const bool xl = trellis_xl(h, M);
   if (!(h->flags & QG_FLAG_X_PREROTATED) && !xl) {
-    const hipError_t e = launch_fwht(x, h->xrot, M, h->K, st);
+    const hipError_t e = launch_fwht(x, w.xrot, M, h->K, st);
     if (e != hipSuccess) return fail(QG_ERR_DEVICE, "rotation launch failed: %s", hipGetErrorString(e));
-    xr = h->xrot;
+    xr = w.xrot;
   }
   if (M > 1) {
     const int MT = M > 16 ? 2 : 1;
@@ -442,8 +455,8 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
     b.cb = h->codebook;
     b.x = xr;
     b.y = y;
-    b.partial = h->partial;
-    b.counters = h->counters;
+    b.partial = w.partial;
+    b.counters = w.counters;
     b.M = M;
     b.K = h->K;
     b.N = h->N;
@@ -455,7 +468,7 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
     // K slices meet in fixed-point words where the atomics are few (and the
     // words' 6-bit count holds S)
     const bool fx = b.S > 1 && b.S <= 63 && (int64_t)M * h->N * b.S <= (1 << 20) && !(h->pins & QG_PIN_PARTIALS);
-    b.acc = fx ? h->acc64 : nullptr;
+    b.acc = fx ? w.acc64 : nullptr;
     const unsigned grid = (unsigned)(((b.RB + nw - 1) / nw) * b.S);
     return after_launch(h, launch_trellis_band(b, MT, grid, st), st);
   }
@@ -465,9 +478,9 @@ qg_status run_trellis(const qg_plan* h, const uint16_t* x, int M, uint16_t* y, h
   a.cb = h->codebook;
   a.x = xr;
   a.y = y;
-  a.partial = h->partial;
-  a.counters = h->counters;
-  a.acc = h->tr_fx ? h->acc64 : nullptr;
+  a.partial = w.partial;
+  a.counters = w.counters;
+  a.acc = h->tr_fx ? w.acc64 : nullptr;
   a.K = h->K;
   a.N = h->N;
   a.G = h->G;
@@ -546,16 +559,16 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   const qg_status s = size_workspace(h, &nf);
   if (s != QG_OK) return s;
   if (nf > 0) {
-    if (hipMalloc(&h->partial, nf * sizeof(float)) != hipSuccess)
+    if (hipMalloc(&h->ws.partial, nf * sizeof(float)) != hipSuccess)
       return fail(QG_ERR_OOM, "workspace allocation of %zu bytes failed", nf * sizeof(float));
-    h->partial_floats = nf;
+    h->ws.partial_floats = nf;
   }
   // fixed-point output words [2][max_M][16 * total_tiles]: the M = 1 GEMVs use
   // the first 2 * 16 * total_tiles (the fused gate/up pass the first
   // 16 * total_tiles as exchange words), the verify GEMM [matrix][row][column]
-  h->acc64_words = (size_t)2 * h->max_M * 16 * h->total_tiles;
-  QG_HIP(hipMalloc(&h->acc64, h->acc64_words * sizeof(unsigned long long)));
-  QG_HIP(hipMemsetAsync(h->acc64, 0, h->acc64_words * sizeof(unsigned long long), st));
+  h->ws.acc64_words = (size_t)2 * h->max_M * 16 * h->total_tiles;
+  QG_HIP(hipMalloc(&h->ws.acc64, h->ws.acc64_words * sizeof(unsigned long long)));
+  QG_HIP(hipMemsetAsync(h->ws.acc64, 0, h->ws.acc64_words * sizeof(unsigned long long), st));
   // the fused MLP's intermediate, when this handle is an MLP's gate
   QG_HIP(hipMalloc(&h->h32, (size_t)h->max_M * N * sizeof(float)));
   if (h->max_M > 1) {
@@ -568,7 +581,8 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
 // ---- dispatch ------------------------------------------------------------------
 // One M = 1 GEMV over a uniform handle, or the fused gate + up pair when h2 !=
 // NULL (h = SiLU(g) * u into y).  xf32: x is fp32; yf32: y receives fp32.
-qg_status run_m1(const qg_plan* h, const qg_plan* h2, const void* x, bool xf32, void* y, bool yf32, hipStream_t st) {
+qg_status run_m1(const qg_plan* h, const Work& w, const qg_plan* h2, const void* x, bool xf32, void* y, bool yf32,
+                 hipStream_t st) {
   const bool dual = h2 != nullptr;
   const int bf = single_bits(h);
   if (use_sk(h)) {
@@ -579,7 +593,7 @@ qg_status run_m1(const qg_plan* h, const qg_plan* h2, const void* x, bool xf32, 
     a.x = x;
     a.y = y;
     a.yf32 = yf32 ? 1 : 0;
-    a.acc = h->acc64;
+    a.acc = w.acc64;
     a.K = h->K;
     a.N = h->N;
     a.G = h->G;
@@ -604,15 +618,15 @@ qg_status run_m1(const qg_plan* h, const qg_plan* h2, const void* x, bool xf32, 
   a.x = x;
   a.y = y;
   a.yf32 = yf32 ? 1 : 0;
-  a.partial = h->partial;
-  a.counters = h->counters;
+  a.partial = w.partial;
+  a.counters = w.counters;
   a.K = h->K;
   a.G = h->G;
   a.G4 = h->G4;
   a.NP = 16 * h->total_tiles;
   a.S = p.S;
   a.pair = dual ? 1 : 0;
-  a.xw = h->acc64;
+  a.xw = w.acc64;
   a.fx = (!dual && m1_fx(h, p.S)) ? 1 : 0;
   int pre = 0;
   for (int i = 0; i < (int)h->segs.size(); ++i) {
@@ -621,7 +635,7 @@ qg_status run_m1(const qg_plan* h, const qg_plan* h2, const void* x, bool xf32, 
   }
   for (int i = (int)h->segs.size(); i <= MAX_SEG; ++i) a.ts_prefix[i] = pre;
   const size_t need = dual ? (size_t)2 * p.S * a.NP : (a.fx ? 0 : partial_need(h, p.S, 1, 1));
-  if (need > h->partial_floats) return fail(QG_ERR_INVALID_ARG, "workspace too small for %d K slices", p.S);
+  if (need > w.partial_floats) return fail(QG_ERR_INVALID_ARG, "workspace too small for %d K slices", p.S);
   const unsigned grid = (unsigned)pre * (unsigned)p.S * (dual ? 2u : 1u);
   return after_launch(h, launch_gemv_q(a, p.NQ, p.NW, lds, grid, bf, xf32, st), st);
 }
@@ -629,16 +643,16 @@ qg_status run_m1(const qg_plan* h, const qg_plan* h2, const void* x, bool xf32, 
 // One verify GEMM (2..32 rows) over a uniform handle, or the fused gate + up
 // pair when h2 != NULL.  xf: (the MLP's down pass) per (row, group) factors
 // of x, [M][G]; yf32: y receives fp32.
-qg_status run_xs(const qg_plan* h, const qg_plan* h2, const uint16_t* x, const float* xf, int M, void* y, bool yf32,
-                 int ldy, hipStream_t st) {
+qg_status run_xs(const qg_plan* h, const Work& w, const qg_plan* h2, const uint16_t* x, const float* xf, int M, void* y,
+                 bool yf32, int ldy, hipStream_t st) {
   const bool dual = h2 != nullptr;
   const bool xsc = xf != nullptr;
   const XsPlan p = xs_plan(h, M, dual, xsc);
   if (p.NQ == 0 || p.lds > kLdsMax)
     return fail(QG_ERR_INVALID_ARG, "x slice of %d quads at M=%d does not fit LDS", p.nq, M);
-  if (!p.fx && partial_need(h, p.S, M, dual ? 2 : 1) > h->partial_floats)
+  if (!p.fx && partial_need(h, p.S, M, dual ? 2 : 1) > w.partial_floats)
     return fail(QG_ERR_INVALID_ARG, "workspace too small for %d K-slices at M=%d", p.S, M);
-  if (p.tg_prefix[MAX_SEG] > std::max(1, h->total_tiles)) return fail(QG_ERR_INVALID_ARG, "more tile groups than counters");
+  if ((size_t)p.tg_prefix[MAX_SEG] > w.ncounters) return fail(QG_ERR_INVALID_ARG, "more tile groups than counters");
   XsArgs a{};
   a.w[0] = wset_of(h);
   if (h2) a.w[1] = wset_of(h2);
@@ -646,9 +660,9 @@ qg_status run_xs(const qg_plan* h, const qg_plan* h2, const uint16_t* x, const f
   a.xf = xf;
   a.y = y;
   a.yf32 = yf32 ? 1 : 0;
-  a.partial = h->partial;
-  a.counters = h->counters;
-  a.acc = p.fx ? h->acc64 : nullptr;
+  a.partial = w.partial;
+  a.counters = w.counters;
+  a.acc = p.fx ? w.acc64 : nullptr;
   a.M = M;
   a.K = h->K;
   a.G = h->G;
@@ -667,6 +681,42 @@ qg_status run_xs(const qg_plan* h, const qg_plan* h2, const uint16_t* x, const f
   return after_launch(h, e, st);
 }
 
+// The workspace one qgemv_run of M rows takes (sizes in elements; the
+// allocation-free entry point carves it out of its static array).
+Work run_need(const qg_plan* h, int M) {
+  Work n;
+  n.ncounters = (size_t)std::max(1, h->total_tiles);
+  const size_t NP = (size_t)16 * h->total_tiles;
+  if (h->format == QG_FMT_TRELLIS3) {
+    const int RB = h->N / 16;
+    if (!(h->flags & QG_FLAG_X_PREROTATED) && !trellis_xl(h, M)) n.xrot_halves = (size_t)M * h->K;
+    if (M > 1) {
+      const int S = tb_slices(h, M > 16 ? TbShape<2>::NW : TbShape<1>::NW);
+      const bool fx = S > 1 && S <= 63 && (int64_t)M * h->N * S <= (1 << 20) && !(h->pins & QG_PIN_PARTIALS);
+      if (fx) n.acc64_words = (size_t)M * h->N;
+      else if (S > 1) n.partial_floats = (size_t)RB * h->tr_maxseg * M * 16;
+    } else {
+      if (h->tr_fx) n.acc64_words = (size_t)h->N;
+      else n.partial_floats = (size_t)RB * h->tr_maxseg * 16;
+    }
+    return n;
+  }
+  if (M == 1) {
+    if (use_sk(h)) {
+      n.acc64_words = NP;
+    } else {
+      const M1Plan p = m1_plan(h, false);
+      if (m1_fx(h, p.S)) n.acc64_words = NP;
+      else n.partial_floats = partial_need(h, p.S, 1, 1);
+    }
+    return n;
+  }
+  const XsPlan p = xs_plan(h, M, false, false);
+  if (p.fx) n.acc64_words = (size_t)M * NP;
+  else n.partial_floats = partial_need(h, p.S, M, 1);
+  return n;
+}
+
 qg_status check_launch_overrides(const qg_weight_desc* d) {
   for (int c = 0; c < 3; ++c) {
     const qg_launch& L = d->launch[c];
@@ -679,6 +729,70 @@ qg_status check_launch_overrides(const qg_weight_desc* d) {
       return fail(QG_ERR_INVALID_ARG, "launch[%d]: at most 8 tile groups per workgroup", c);
   }
   return QG_OK;
+}
+
+}  // namespace
+
+// ---- the allocation-free entry point's workspace -----------------------------------
+// A file-scope device array (each GPU the library runs on holds its own copy
+// until the process ends).  In host code its name is a host-side stand-in, not
+// a device address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, once per device, and only that address is ever handed
+// to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[QG_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's copy of `scratch`; the first call on
+// a device also clears it (a fill kernel on `st`, in order before the caller's
+// work), so counters and fixed-point words start at zero there
+qg_status scratch_of(int dev, hipStream_t st, unsigned char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(QG_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(QG_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    QG_HIP(launch_fill_zero(p, QG_SCRATCH_BYTES, st));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<unsigned char*>(g_scratch_ptr[dev]);
+  return QG_OK;
+}
+
+// The scratch array's fixed regions: arrival counters and fixed-point words
+// (which must read zero when a run starts: every run re-arms what it used, and
+// no run ever writes anything else there), then partials and the rotated x
+// (written before they are read).  Fixed, so that no run's partials can land
+// where a later run expects zeros.
+constexpr size_t kScrCounters = 64 << 10;
+constexpr size_t kScrWords = 4 << 20;
+constexpr size_t kScrRest = (size_t)QG_SCRATCH_BYTES - kScrCounters - kScrWords;
+static_assert(QG_SCRATCH_BYTES > kScrCounters + kScrWords, "scratch regions");
+
+// the run's workspace in the scratch array at `base`; false (and a message)
+// when a region is too small for it
+bool carve(const Work& need, uintptr_t base, Work* w) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  const size_t cb = need.ncounters * sizeof(int), wb = need.acc64_words * sizeof(unsigned long long);
+  const size_t pb = up(need.partial_floats * sizeof(float)), xb = need.xrot_halves * sizeof(uint16_t);
+  if (cb > kScrCounters || wb > kScrWords || pb + xb > kScrRest) {
+    fail(QG_ERR_INVALID_ARG,
+         "this run needs %zu B of counters, %zu B of words and %zu B of partials and staging; the static scratch "
+         "array holds %zu, %zu and %zu",
+         cb, wb, pb + xb, kScrCounters, kScrWords, kScrRest);
+    return false;
+  }
+  *w = need;
+  w->counters = reinterpret_cast<int*>(base);
+  w->acc64 = reinterpret_cast<unsigned long long*>(base + kScrCounters);
+  w->partial = reinterpret_cast<float*>(base + kScrCounters + kScrWords);
+  w->xrot = reinterpret_cast<uint16_t*>(base + kScrCounters + kScrWords + pb);
+  return true;
 }
 
 }  // namespace
@@ -742,8 +856,9 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   s = d->format == QG_FMT_UNIFORM ? create_uniform(h, d, st) : create_trellis(h, d, st);
   if (s == QG_OK) {
     const int nc = std::max(1, h->total_tiles);
-    if (hipMalloc(&h->counters, nc * sizeof(int)) != hipSuccess) s = fail(QG_ERR_OOM, "counter allocation failed");
-    else if (hipMemsetAsync(h->counters, 0, nc * sizeof(int), st) != hipSuccess)
+    h->ws.ncounters = (size_t)nc;
+    if (hipMalloc(&h->ws.counters, nc * sizeof(int)) != hipSuccess) s = fail(QG_ERR_OOM, "counter allocation failed");
+    else if (hipMemsetAsync(h->ws.counters, 0, nc * sizeof(int), st) != hipSuccess)
       s = fail(QG_ERR_DEVICE, "counter initialisation failed");
   }
   if (s == QG_OK && h->format == QG_FMT_UNIFORM) {
@@ -778,9 +893,30 @@ qg_status qgemv_run(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void
   if (M < 1 || M > h->max_M) return fail(QG_ERR_INVALID_ARG, "M = %d is not in [1, %d]", M, h->max_M);
   if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
-  if (h->format == QG_FMT_TRELLIS3) return run_trellis(h, x, M, y, st);
-  if (M == 1) return run_m1(h, nullptr, x, false, y, false, st);
-  return run_xs(h, nullptr, x, nullptr, M, y, false, h->N, st);
+  if (h->format == QG_FMT_TRELLIS3) return run_trellis(h, h->ws, x, M, y, st);
+  if (M == 1) return run_m1(h, h->ws, nullptr, x, false, y, false, st);
+  return run_xs(h, h->ws, nullptr, x, nullptr, M, y, false, h->N, st);
+}
+
+qg_status qgemv_run_noalloc(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* stream) {
+  g_err.clear();
+  if (!h || !x || !y) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  if (M < 1 || M > h->max_M) return fail(QG_ERR_INVALID_ARG, "M = %d is not in [1, %d]", M, h->max_M);
+  if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  int dev = -1;
+  QG_HIP(hipGetDevice(&dev));
+  if (dev != h->device) return fail(QG_ERR_INVALID_ARG, "the handle lives on device %d, the current one is %d", h->device, dev);
+  hipStream_t st = (hipStream_t)stream;
+  Work w;
+  const Work need = run_need(h, M);
+  if (!carve(need, 0, &w)) return QG_ERR_INVALID_ARG;  // sizes only: nothing enqueued when the run does not fit
+  unsigned char* base = nullptr;
+  const qg_status s = scratch_of(dev, st, &base);
+  if (s != QG_OK) return s;
+  carve(need, reinterpret_cast<uintptr_t>(base), &w);
+  if (h->format == QG_FMT_TRELLIS3) return run_trellis(h, w, x, M, y, st);
+  if (M == 1) return run_m1(h, w, nullptr, x, false, y, false, st);
+  return run_xs(h, w, nullptr, x, nullptr, M, y, false, h->N, st);
 }
 
 qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t* x, int32_t M, uint16_t* out,
@@ -796,15 +932,15 @@ qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t*
   if (!aligned16(x) || !aligned16(out)) return fail(QG_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   if (M == 1) {
-    const qg_status s = run_m1(gate, up, x, false, gate->h32, true, st);
+    const qg_status s = run_m1(gate, gate->ws, up, x, false, gate->h32, true, st);
     if (s != QG_OK) return s;
-    return run_m1(down, nullptr, gate->h32, true, out, false, st);
+    return run_m1(down, down->ws, nullptr, gate->h32, true, out, false, st);
   }
-  qg_status s = run_xs(gate, up, x, nullptr, M, gate->h32, true, gate->N, st);
+  qg_status s = run_xs(gate, gate->ws, up, x, nullptr, M, gate->h32, true, gate->N, st);
   if (s != QG_OK) return s;
   s = after_launch(gate, launch_h_to_f16(gate->h32, gate->h16, gate->hf, M, gate->N, st), st);
   if (s != QG_OK) return s;
-  return run_xs(down, nullptr, gate->h16, gate->hf, M, out, false, down->N, st);
+  return run_xs(down, down->ws, nullptr, gate->h16, gate->hf, M, out, false, down->N, st);
 }
 
 qg_status qg_stream_read(const void* buf, int64_t bytes, void* stream) {

@@ -161,6 +161,28 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* desc, int32_t max_M
  * [M][N] row-major; 1 <= M <= max_M.  Enqueues on stream. */
 qg_status qgemv_run(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* stream);
 
+/* Bytes of the static scratch array qgemv_run_noalloc works in (per GPU):
+ * 64 KiB of arrival counters, 4 MiB of fixed-point words, the rest for fp32
+ * partials and staging. */
+#define QG_SCRATCH_BYTES (16 << 20)
+
+/* For callers that cannot allocate device memory at run time (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same product as qgemv_run, by the same kernels and launch plans (so the
+ * same bits), but its workspace (split-K partials, arrival counters,
+ * fixed-point words, the trellis path's rotated x) lives in a file-scope
+ * static device array of QG_SCRATCH_BYTES per GPU, held until the process
+ * ends, instead of in the handle.  It calls no hipMalloc, hipFree or other
+ * allocating routine.  A run whose workspace exceeds a region of the array
+ * fails with QG_ERR_INVALID_ARG before enqueueing anything (each 27B-class
+ * layer shape fits at every row count; at most about 7 MB of partials, for
+ * 5120 x 17408 at 32 rows).  The first call on a GPU also
+ * enqueues a kernel that clears the array; every run leaves its counters and
+ * words cleared again.  All calls on one GPU share the array: calls that
+ * overlap on one GPU (other streams, or other threads) race, and must be
+ * ordered by the caller.  The current device must be the handle's. */
+qg_status qgemv_run_noalloc(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* stream);
+
 /* Fused MLP: out = down( SiLU(gate(x)) * up(x) ), SiLU(z) = z / (1 + e^-z)
  * (Qwen3.8-27B page, "What we added on top of upstream": a fused MLP path for
  * the verify batches; OrcaSAQ2 page, intro: fewer launches).  gate and up:
