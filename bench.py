@@ -360,6 +360,33 @@ def main():
     result["layer_set_ratio_M8_M1"] = round(layer_us[8] / layer_us[1], 3)
     log("layer set us", result["layer_set_us"])
 
+    # ---------------- the layer set through qgemv_run_batch ----------------
+    # all seven products in one launch (independent inputs, as in the timed
+    # step), and in decode order with siblings batched: q|k|v (one x), o,
+    # gate|up (one x), down -- 4 launches
+    yb = {M: [torch.empty((M, sh["N"]), dtype=torch.float16, device=dev) for sh in shapes] for M in (1,)}
+
+    def batch_all(r, M=1):
+        Q.run_batch(lins[r], [xk[(M, sh["K"])] for sh in shapes], yb[M])
+
+    def batch_siblings(r, M=1):
+        L, x5, x17 = lins[r], xk[(M, 5120)], xk[(M, 17408)]
+        Q.run_batch([L[0], L[1], L[2]], [x5, x5, x5], yb[M][0:3])
+        L[3].run(x5, out=yb[M][3])
+        Q.run_batch([L[4], L[5]], [x5, x5], yb[M][4:6])
+        L[6].run(x17, out=yb[M][6])
+
+    for name, fn in (("layer_set_one_launch", batch_all), ("layer_set_siblings_batched", batch_siblings)):
+        def f(fn=fn):
+            for r in range(R):
+                fn(r)
+        us = graph_us(capture(f), R, reps=5)
+        result[name] = {"us_M1": round(us, 3), "GBs_M1": round(per_copy / us / 1e3, 1),
+                        "pct_8TBs_M1": round(100 * per_copy / us / 1e3 / HBM_PEAK_GBS, 2),
+                        "pct_of_stream_read": round(100 * ls_stream / us, 1),
+                        "launches": 1 if name == "layer_set_one_launch" else 4}
+        log(name, result[name])
+
     # ---------------- the same layer set with sibling projections fused ----------------
     # q|k|v and gate|up read the same input: each pair of siblings runs as one
     # launch over its rows stacked (N = 7168 and 34816) -- the same weights, bytes

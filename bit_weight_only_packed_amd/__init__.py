@@ -15,7 +15,8 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["QGError", "lib", "QLinear", "mlp", "stream_read", "declared_symbols", "LIB_PATH", "HEADER_PATH"]
+__all__ = ["QGError", "lib", "QLinear", "mlp", "run_batch", "stream_read", "declared_symbols", "LIB_PATH",
+           "HEADER_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemv.so")
@@ -68,11 +69,14 @@ def lib() -> ctypes.CDLL:
     L.qg_last_error.restype = ctypes.c_char_p
     L.qgemv_weight_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
     L.qg_stream_read.argtypes = [vp, ctypes.c_int64, vp]
+    L.qgemv_run_batch.argtypes = [i32, vp, vp, vp, i32, vp]
+    L.qgemv_run_noalloc.argtypes = [vp, vp, i32, vp, vp]
     L.qgemv_debug_unpack.argtypes = [vp, vp, vp]
     L.qgemv_debug_dequant.argtypes = [vp, vp, u16p, vp]
     L.qgemv_debug_operand.argtypes = [vp, vp, vp, vp, vp]
     L.qgemv_debug_trellis.argtypes = [vp, vp, vp]
     for f in ("qgemv_create", "qgemv_run", "qmlp_run", "qgemv_destroy", "qgemv_weight_bytes", "qg_stream_read",
+              "qgemv_run_batch", "qgemv_run_noalloc",
               "qgemv_debug_unpack", "qgemv_debug_dequant", "qgemv_debug_operand", "qgemv_debug_trellis"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -195,6 +199,21 @@ class QLinear:
             self.close()
         except Exception:
             pass
+
+
+def run_batch(lins, xs, outs=None, stream=None):
+    """Several independent products y_i = x_i W_i^T (same row count) in one call
+    (one launch at M = 1).  lins: QLinear list; xs: CUDA fp16 tensors [M][K_i]."""
+    import torch
+    n = len(lins)
+    M = xs[0].shape[0]
+    if outs is None:
+        outs = [torch.empty((M, l.N), dtype=torch.float16, device=x.device) for l, x in zip(lins, xs)]
+    H = (ctypes.c_void_p * n)(*[l.handle.value for l in lins])
+    X = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    Y = (ctypes.c_void_p * n)(*[_ptr(y) for y in outs])
+    _check(lib().qgemv_run_batch(n, H, X, Y, int(M), _stream(stream)))
+    return outs
 
 
 def stream_read(buf, stream=None):

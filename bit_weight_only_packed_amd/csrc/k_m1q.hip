@@ -27,7 +27,31 @@ void lq_x(const GvArgs& a, int NW, size_t lds, unsigned grid, int bf, bool xf, h
   else lq_b<NQ, false>(a, NW, lds, grid, bf, st);
 }
 
+template <int NQ, int BF>
+void lb(const GvBatch& b, int NW, size_t lds, unsigned grid, hipStream_t st) {
+  k_gemv_batch<NQ, BF><<<grid, NW * 64, lds, st>>>(b);
+}
+
+template <int NQ>
+void lb_b(const GvBatch& b, int NW, size_t lds, unsigned grid, int bf, hipStream_t st) {
+  switch (bf) {
+    case 2: lb<NQ, 2>(b, NW, lds, grid, st); break;
+    case 3: lb<NQ, 3>(b, NW, lds, grid, st); break;
+    case 4: lb<NQ, 4>(b, NW, lds, grid, st); break;
+    default: lb<NQ, 0>(b, NW, lds, grid, st); break;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gemv_batch(const GvBatch& b, int NQ, int NW, size_t lds, unsigned grid, int bf, hipStream_t st) {
+  switch (NQ) {
+    case 2: lb_b<2>(b, NW, lds, grid, bf, st); break;
+    case 3: lb_b<3>(b, NW, lds, grid, bf, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gemv_q(const GvArgs& a, int NQ, int NW, size_t lds, unsigned grid, int bf, bool xf, hipStream_t st) {
   switch (NQ) {

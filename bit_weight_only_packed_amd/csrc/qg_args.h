@@ -40,6 +40,14 @@ struct GvArgs {
   int ts_prefix[MAX_SEG + 1];  // prefix sums of tiles per segment
 };
 
+// several independent M = 1 products in one launch (qgemv_run_batch)
+constexpr int GV_MAX_TASKS = 8;
+struct GvBatch {
+  GvArgs task[GV_MAX_TASKS];
+  int wg0[GV_MAX_TASKS + 1];   // first workgroup of each task; wg0[n] = the grid
+  int n;
+};
+
 // LDS layout (bytes): per wave its staged activations NQ*1024 and quarter
 // sums NQ*64 | cross-wave partials NW*16*4 | flag 16
 constexpr int M1_WAVE_LDS = 1088;  // per quad of a wave

@@ -108,10 +108,10 @@ __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, 
 // capped so that seven waves fit on each SIMD (the decode shapes' grids of
 // 4- and 5-wave workgroups then stay resident; the cap spills a few registers,
 // an eight-wave cap spills more and is slower than no cap)
+// workgroup `bid` of the launch described by `a` (a tile and K slice of one
+// matrix, or of one of the fused pass's two)
 template <int NQ, int BF, bool XF>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(BF == 0 && NQ <= 2 ? 7 : 1)))
-void k_gemv_q(GvArgs a) {
-  extern __shared__ __align__(16) char smem[];
+__device__ __forceinline__ void gemv_q_block(const GvArgs& a, int bid, char* smem) {
   const int NW = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -121,7 +121,7 @@ void k_gemv_q(GvArgs a) {
   // slices and applies SiLU(g) * u
   const int P = a.pair ? 2 : 1;
   const int SP = S * P;
-  const int sx = blockIdx.x % SP, tsg = blockIdx.x / SP;
+  const int sx = bid % SP, tsg = bid / SP;
   const int dm = sx / S, s = sx - dm * S;
   // single-width handles have one segment: no data-dependent argument loads
   int si = 0;
@@ -209,6 +209,26 @@ void k_gemv_q(GvArgs a) {
     }
   }
   if (mine && n_out >= 0) store_y(a.y, n_out, v, a.yf32);
+}
+
+template <int NQ, int BF, bool XF>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(BF == 0 && NQ <= 2 ? 7 : 1)))
+void k_gemv_q(GvArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  gemv_q_block<NQ, BF, XF>(a, blockIdx.x, smem);
+}
+
+// Several independent M = 1 products in one launch: task t owns workgroups
+// [wg0[t], wg0[t + 1]) and runs exactly as its own launch would (same plan
+// shape: every task is planned for the launch's NQ and NW).
+template <int NQ, int BF>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(BF == 0 && NQ <= 2 ? 7 : 1)))
+void k_gemv_batch(GvBatch b) {
+  extern __shared__ __align__(16) char smem[];
+  const int bid = blockIdx.x;
+  int t = 0;
+  while (t + 1 < b.n && bid >= b.wg0[t + 1]) ++t;
+  gemv_q_block<NQ, BF, false>(b.task[t], bid - b.wg0[t], smem);
 }
 
 }  // namespace qg

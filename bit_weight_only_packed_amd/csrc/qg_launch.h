@@ -12,6 +12,7 @@ constexpr size_t kLdsMax = 163840;  // LDS per workgroup on gfx950
 // M = 1 GEMVs (k_m1q.hip, k_m1sk.hip).  bf: the single code width of the
 // matrix (2, 3, 4) or 0 for several widths; xf: x is fp32.
 hipError_t launch_gemv_q(const GvArgs& a, int NQ, int NW, size_t lds, unsigned grid, int bf, bool xf, hipStream_t st);
+hipError_t launch_gemv_batch(const GvBatch& b, int NQ, int NW, size_t lds, unsigned grid, int bf, hipStream_t st);
 hipError_t launch_gemv_sk(const SkArgs& a, bool dual, int NW, size_t lds, unsigned grid, int bf, bool xf,
                           hipStream_t st);
 hipError_t m1_allow_lds();  // lets the M = 1 kernels take more than 64 KiB of dynamic LDS

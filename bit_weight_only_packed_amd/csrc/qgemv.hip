@@ -681,6 +681,55 @@ qg_status run_xs(const qg_plan* h, const Work& w, const qg_plan* h2, const uint1
   return after_launch(h, e, st);
 }
 
+// Several independent M = 1 products (uniform handles, distinct) in one
+// launch of the per-group GEMV: one plan shape for all (2 quads per wave, NW
+// waves per workgroup covering the longest K slice), each matrix cut into as
+// many K slices as that takes, slices meeting in fixed-point words (or, with
+// the partials pinned, in the handle's partials when they fit).
+qg_status run_batch_m1(int n, const qg_plan* const* hs, const uint16_t* const* xs, uint16_t* const* ys, hipStream_t st) {
+  constexpr int NQ = 2;
+  int maxg4 = 1, bf = single_bits(hs[0]);
+  for (int i = 0; i < n; ++i) {
+    maxg4 = std::max(maxg4, hs[i]->G4);
+    if (single_bits(hs[i]) != bf) bf = 0;
+  }
+  const int NW = (std::min(10, maxg4) + NQ - 1) / NQ;  // slices of at most 10 quads (5 waves)
+  GvBatch b{};
+  b.n = n;
+  int wg = 0;
+  for (int i = 0; i < n; ++i) {
+    const qg_plan* h = hs[i];
+    GvArgs& a = b.task[i];
+    const int S = (h->G4 + NW * NQ - 1) / (NW * NQ);
+    a.w[0] = wset_of(h);
+    a.x = xs[i];
+    a.y = ys[i];
+    a.partial = h->ws.partial;
+    a.counters = h->ws.counters;
+    a.K = h->K;
+    a.G = h->G;
+    a.G4 = h->G4;
+    a.NP = 16 * h->total_tiles;
+    a.S = S;
+    a.xw = h->ws.acc64;
+    a.fx = m1_fx(h, S) ? 1 : 0;
+    if (S > 1 && !a.fx && partial_need(h, S, 1, 1) > h->ws.partial_floats)
+      return fail(QG_ERR_INVALID_ARG, "batch entry %d: %d K slices need more partials than its handle holds", i, S);
+    if (S > 63) return fail(QG_ERR_UNSUPPORTED, "batch entry %d: K = %d is too long for one launch", i, h->K);
+    int pre = 0;
+    for (int k = 0; k < (int)h->segs.size(); ++k) {
+      a.ts_prefix[k] = pre;
+      pre += h->segs[k].tiles;
+    }
+    for (int k = (int)h->segs.size(); k <= MAX_SEG; ++k) a.ts_prefix[k] = pre;
+    b.wg0[i] = wg;
+    wg += pre * S;
+  }
+  b.wg0[n] = wg;
+  for (int i = n + 1; i <= GV_MAX_TASKS; ++i) b.wg0[i] = wg;
+  return after_launch(hs[0], launch_gemv_batch(b, NQ, NW, m1_lds_bytes(NQ, NW), (unsigned)wg, bf, st), st);
+}
+
 // The workspace one qgemv_run of M rows takes (sizes in elements; the
 // allocation-free entry point carves it out of its static array).
 Work run_need(const qg_plan* h, int M) {
@@ -917,6 +966,29 @@ qg_status qgemv_run_noalloc(qg_handle h, const uint16_t* x, int32_t M, uint16_t*
   if (h->format == QG_FMT_TRELLIS3) return run_trellis(h, w, x, M, y, st);
   if (M == 1) return run_m1(h, w, nullptr, x, false, y, false, st);
   return run_xs(h, w, nullptr, x, nullptr, M, y, false, h->N, st);
+}
+
+qg_status qgemv_run_batch(int32_t n, const qg_handle* hs, const uint16_t* const* xs, uint16_t* const* ys, int32_t M,
+                          void* stream) {
+  g_err.clear();
+  if (n < 1 || n > GV_MAX_TASKS) return fail(QG_ERR_INVALID_ARG, "n = %d is not in [1, %d]", n, GV_MAX_TASKS);
+  if (!hs || !xs || !ys) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  bool one_launch = M == 1;
+  for (int i = 0; i < n; ++i) {
+    if (!hs[i] || !xs[i] || !ys[i]) return fail(QG_ERR_INVALID_ARG, "NULL entry %d", i);
+    if (M < 1 || M > hs[i]->max_M) return fail(QG_ERR_INVALID_ARG, "M = %d is not in [1, %d] for entry %d", M, hs[i]->max_M, i);
+    if (!aligned16(xs[i]) || !aligned16(ys[i])) return fail(QG_ERR_INVALID_ARG, "x and y of entry %d must be 16-byte aligned", i);
+    for (int k = 0; k < i; ++k)
+      if (hs[k] == hs[i]) return fail(QG_ERR_INVALID_ARG, "entries %d and %d share a handle (and its workspace)", k, i);
+    if (hs[i]->format != QG_FMT_UNIFORM || hs[i]->device != hs[0]->device) one_launch = false;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (one_launch) return run_batch_m1(n, hs, xs, ys, st);
+  for (int i = 0; i < n; ++i) {  // other formats and row counts: one launch per entry, in order
+    const qg_status s = qgemv_run(hs[i], xs[i], M, ys[i], stream);
+    if (s != QG_OK) return s;
+  }
+  return QG_OK;
 }
 
 qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t* x, int32_t M, uint16_t* out,

@@ -161,6 +161,22 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* desc, int32_t max_M
  * [M][N] row-major; 1 <= M <= max_M.  Enqueues on stream. */
 qg_status qgemv_run(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* stream);
 
+/* Several independent products of the same row count in one call: for i < n,
+ * y_i = x_i * W_i^T with W_i the matrix of hs[i] -- the sibling projections of
+ * a layer that read the same input (pass the same x pointer: "The Rock8",
+ * env-var table, sibling matmuls that read the same input tensor), or a whole
+ * layer's linear set at one step (OrcaSAQ2 page, intro: launch counts cut by
+ * fusing).  hs, xs, ys: host arrays of n entries (1 <= n <= 8); xs[i], ys[i]:
+ * device fp16 [M][K_i] and [M][N_i], 16-byte aligned; the handles must be
+ * distinct (each brings its own workspace).  At M = 1 with UNIFORM handles
+ * all n products run in one launch, each matrix in K slices of at most 10
+ * quads that meet in fixed-point words (results within the matmul tolerance
+ * of qgemv_run's, not bit-identical to them where the slicing differs, and
+ * bit-identical across repeats); otherwise each entry runs as qgemv_run, in
+ * order, on `stream`. */
+qg_status qgemv_run_batch(int32_t n, const qg_handle* hs, const uint16_t* const* xs, uint16_t* const* ys, int32_t M,
+                          void* stream);
+
 /* Bytes of the static scratch array qgemv_run_noalloc works in (per GPU):
  * 64 KiB of arrival counters, 4 MiB of fixed-point words, the rest for fp32
  * partials and staging. */
