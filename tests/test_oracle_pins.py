@@ -399,10 +399,24 @@ def test_mlp_brute_force_tiny():
     assert np.all(O.mlp(np.zeros((1, H)), wg, wu, wd) == 0.0)
 
 
-def test_silu_definition_points():
-    z = np.array([0.0, 1.0, -1.0, 20.0, -20.0])
-    want = [0.0, 1 / (1 + math.exp(-1)), -1 / (1 + math.exp(1)), 20 / (1 + math.exp(-20)), -20 / (1 + math.exp(20))]
-    np.testing.assert_allclose(O.silu(z), want, rtol=1e-15, atol=0)
+def test_silu_identities():
+    """SiLU(z) = z * sigmoid(z), pinned by identities that do not retype it:
+    the tanh form z (1 + tanh(z / 2)) / 2, the odd part SiLU(z) - SiLU(-z) = z,
+    slope 1/2 at 0, the asymptotes, and the stationary point z* (where the
+    derivative vanishes, which forces SiLU(z*) = z* + 1)."""
+    z = np.linspace(-30.0, 30.0, 1201)
+    # (1 + tanh) cancels for large negative z: compare absolutely there
+    np.testing.assert_allclose(O.silu(z), z * (1.0 + np.tanh(z / 2.0)) / 2.0, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(O.silu(z) - O.silu(-z), z, rtol=1e-13, atol=1e-13)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    h = 1e-7
+    assert abs(O.silu(np.array([h]))[0] / h - 0.5) < 1e-7
+    assert abs(O.silu(np.array([40.0]))[0] - 40.0) < 1e-15
+    assert 0.0 > O.silu(np.array([-40.0]))[0] > -1e-15
+    from scipy.optimize import minimize_scalar
+    r = minimize_scalar(lambda t: float(O.silu(np.array([t]))[0]), bracket=(-3.0, -1.0, 0.0), tol=1e-12)
+    assert abs(float(O.silu(np.array([r.x]))[0]) - (r.x + 1.0)) < 1e-10
+    assert -1.2785 < r.x < -1.2784
 
 
 # ---------------------------------------------------------------------------
