@@ -25,6 +25,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qgemv.h")
 QG_OK, QG_ERR_INVALID_ARG, QG_ERR_UNSUPPORTED, QG_ERR_DEVICE, QG_ERR_OOM = 0, -1, -2, -3, -4
 FMT_UNIFORM, FMT_TRELLIS3 = 0, 1
 FLAG_X_PREROTATED = 1
+FLAG_BATCH_INVARIANT = 2
 GROUP = 128
 # pins (include/qgemv.h): force a kernel or hand-over
 PIN_M1_PERGROUP, PIN_M1_RUNS, PIN_PARTIALS, PIN_WORDS = 1 << 0, 1 << 1, 1 << 2, 1 << 3
@@ -114,12 +115,13 @@ class QLinear:
     dtype).  scales: CUDA fp16 tensor [N][K/128].  bits: 2/3/4, or col_bits
     (host array of per-column widths).  codebook: CUDA fp16 [65536] (trellis).
     pins: PIN_* bits; launch: optional {row class 0/1/2: (tiles, waves, splits)}
-    launch-geometry overrides (both fixed at create).
+    launch-geometry overrides (both fixed at create).  batch_invariant: row m of
+    an M-row run is bit-identical to running that row alone (uniform codes).
     """
 
     def __init__(self, codes, scales, K: int, N: int, bits: int = 3, col_bits=None, max_M: int = 32,
                  trellis: bool = False, codebook=None, prerotated: bool = False, stream=None,
-                 pins: int = 0, launch=None):
+                 pins: int = 0, launch=None, batch_invariant: bool = False):
         d = _Desc()
         d.K, d.N, d.group_size = int(K), int(N), GROUP
         d.format = FMT_TRELLIS3 if trellis else FMT_UNIFORM
@@ -133,7 +135,7 @@ class QLinear:
         d.codes = _ptr(codes)
         d.scales = _ptr(scales)
         d.codebook = _ptr(codebook) if codebook is not None else None
-        d.flags = FLAG_X_PREROTATED if prerotated else 0
+        d.flags = (FLAG_X_PREROTATED if prerotated else 0) | (FLAG_BATCH_INVARIANT if batch_invariant else 0)
         d.pins = int(pins)
         for c, (t, w, s) in (launch or {}).items():
             d.launch[int(c)] = _Launch(int(t), int(w), int(s))

@@ -185,8 +185,11 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
     }
   }
   lds_barrier();  // every wave's share of the slice has landed
-  // ---- group sums of x: lane gl of a wave sums group gl of one row (reading
-  // the row's chunks in a lane-rotated order, so 16 lanes hit 16 bank groups)
+  // ---- group sums of x: lane gl of a wave sums group gl of one row, its 16
+  // chunks in the order (cc + gl) & 15 of their place in the row (so 16 lanes
+  // hit 16 bank groups); the order depends on the group only, never on the
+  // row's place in the batch (the row swizzle is undone on the address), so a
+  // row's sums round the same at every row count
   {
     const uint32_t ones = 0x3C003C00u;
     const int gl = lane & 31;
@@ -197,7 +200,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
         float acc = 0.0f;
 #pragma unroll
         for (int cc = 0; cc < 16; ++cc) {
-          const uint4 v = *reinterpret_cast<const uint4*>(rp + ((cc + gl) & 15) * 16);
+          const uint4 v = *reinterpret_cast<const uint4*>(rp + (((cc + gl) & 15) ^ (m & 15)) * 16);
           acc = dot2(v.x, ones, acc);
           acc = dot2(v.y, ones, acc);
           acc = dot2(v.z, ones, acc);

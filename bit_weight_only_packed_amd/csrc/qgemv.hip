@@ -249,15 +249,24 @@ constexpr XsTuned kXsTuned[] = {
     {34816, 5120, 1, 8, 3, 1}, {34816, 5120, 2, 8, 3, 2},   // gate | up stacked
 };
 
+bool invariant(const qg_plan* h) { return (h->flags & QG_FLAG_BATCH_INVARIANT) != 0; }
+
+// Batch-invariant handles plan every row count as max_M rows (at least 2):
+// the K slices, tile grouping, workgroup split and hand-over are then the same
+// for every M, and only the row tiles actually computed (MT) and the LDS taken
+// follow M.  Each output element's arithmetic -- its MFMA chains over the
+// slice's groups in order, its scale products and the slices' hand-over --
+// does not depend on the other rows.
 XsPlan xs_plan(const qg_plan* h, int M, bool dual, bool xsc) {
   XsPlan p;
-  Launch L = h->over[mclass(M)];
+  const int Mp = invariant(h) ? std::max(2, h->max_M) : M;  // the row count the plan is made for
+  Launch L = h->over[mclass(Mp)];
   // one-tile groups (twice the waves) measured faster except for wide
   // matrices at more than 16 rows
-  int tuned_T = (M <= 16 || h->total_tiles <= 512) ? 1 : 2;
+  int tuned_T = (Mp <= 16 || h->total_tiles <= 512) ? 1 : 2;
   if (!dual)
     for (const XsTuned& t : kXsTuned)
-      if (t.N == h->N && t.K == h->K && t.mcls == mclass(M)) {
+      if (t.N == h->N && t.K == h->K && t.mcls == mclass(Mp)) {
         tuned_T = t.T;
         if (L.T <= 0 && L.NW <= 0 && L.S <= 0) {
           L.T = t.GPW;
@@ -265,6 +274,7 @@ XsPlan xs_plan(const qg_plan* h, int M, bool dual, bool xsc) {
         }
       }
   p.MT = M <= 16 ? 1 : 2;
+  const int MTp = Mp <= 16 ? 1 : 2;
   // tiles per tile group: 1 for the fused gate/up pair; else the tuned count
   p.T = dual ? 1 : tuned_T;
   if (!dual && (h->pins & QG_PIN_XS_T1)) p.T = 1;
@@ -276,12 +286,12 @@ XsPlan xs_plan(const qg_plan* h, int M, bool dual, bool xsc) {
   for (;; ++p.S) {
     p.nq = (h->G4 + p.S - 1) / p.S;
     p.NQ = xs_nq_compiled(p.nq);
-    if (p.NQ > 0 && xs_x_bytes(M, p.NQ) + nsum * xs_sum_bytes(p.MT, p.NQ) + col_cap <= kLdsMax) break;
+    if (p.NQ > 0 && xs_x_bytes(Mp, p.NQ) + nsum * xs_sum_bytes(MTp, p.NQ) + col_cap <= kLdsMax) break;
     if (p.S >= h->G4) break;
   }
   int tg = 0;
   for (const auto& sg : h->segs) tg += (sg.tiles + p.T - 1) / p.T;
-  const size_t lds0 = xs_x_bytes(M, p.NQ) + nsum * xs_sum_bytes(p.MT, p.NQ) + 1024;
+  const size_t lds0 = xs_x_bytes(Mp, p.NQ) + nsum * xs_sum_bytes(MTp, p.NQ) + 1024;
   const int per_cu = std::max(1, (int)(kLdsMax / lds0));
   const int64_t want = (int64_t)std::max(1, h->cus) * per_cu;  // workgroups that fit at once
   if (L.T > 0) p.GPW = L.T;
@@ -307,7 +317,7 @@ XsPlan xs_plan(const qg_plan* h, int M, bool dual, bool xsc) {
   // on every decode shape, the partials at 32 rows on the widest), or when many
   // slices would make the last one read its partials in several round trips
   // (measured: down at 24-32 rows, 9 slices, gains; gate/up, 3 slices, loses)
-  const int64_t atomics = (int64_t)M * 16 * h->total_tiles * p.S;
+  const int64_t atomics = (int64_t)Mp * 16 * h->total_tiles * p.S;
   p.fx = p.S > 1 && p.S <= 63 && (atomics <= (int64_t)1 << 20 || (p.S >= 6 && atomics <= (int64_t)1 << 22));
   if (h->pins & QG_PIN_PARTIALS) p.fx = false;
   if (h->pins & QG_PIN_WORDS) p.fx = p.S > 1 && p.S <= 63;
@@ -330,7 +340,7 @@ qg_status size_workspace(qg_plan* h, size_t* floats) {
     const M1Plan p2 = m1_plan(h, true);  // the fused gate/up pass: both matrices' slices
     need = std::max(need, (size_t)2 * std::max(p2.S, 1) * (size_t)(16 * h->total_tiles));
   }
-  for (int M = 2; M <= h->max_M; ++M)
+  for (int M = invariant(h) ? 1 : 2; M <= h->max_M; ++M)
     for (int v = 0; v < 3; ++v) {
       const bool dual = v == 1, xsc = v == 2;
       const XsPlan p = xs_plan(h, M, dual, xsc);
@@ -750,7 +760,7 @@ Work run_need(const qg_plan* h, int M) {
     }
     return n;
   }
-  if (M == 1) {
+  if (M == 1 && !invariant(h)) {
     if (use_sk(h)) {
       n.acc64_words = NP;
     } else {
@@ -869,6 +879,8 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   if (d->format == QG_FMT_TRELLIS3) {
     if (!d->codebook || !aligned16(d->codebook)) return fail(QG_ERR_INVALID_ARG, "trellis needs a 16-byte aligned codebook");
   }
+  if ((d->flags & QG_FLAG_BATCH_INVARIANT) && d->format != QG_FMT_UNIFORM)
+    return fail(QG_ERR_UNSUPPORTED, "batch-invariant rows are built for uniform-code handles only");
   if ((d->pins & QG_PIN_M1_PERGROUP) && (d->pins & QG_PIN_M1_RUNS))
     return fail(QG_ERR_INVALID_ARG, "pins: one M = 1 kernel at a time");
   if ((d->pins & QG_PIN_XS_T1) && (d->pins & QG_PIN_XS_T2))
@@ -943,7 +955,7 @@ qg_status qgemv_run(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void
   if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   if (h->format == QG_FMT_TRELLIS3) return run_trellis(h, h->ws, x, M, y, st);
-  if (M == 1) return run_m1(h, h->ws, nullptr, x, false, y, false, st);
+  if (M == 1 && !invariant(h)) return run_m1(h, h->ws, nullptr, x, false, y, false, st);
   return run_xs(h, h->ws, nullptr, x, nullptr, M, y, false, h->N, st);
 }
 
@@ -964,7 +976,7 @@ qg_status qgemv_run_noalloc(qg_handle h, const uint16_t* x, int32_t M, uint16_t*
   if (s != QG_OK) return s;
   carve(need, reinterpret_cast<uintptr_t>(base), &w);
   if (h->format == QG_FMT_TRELLIS3) return run_trellis(h, w, x, M, y, st);
-  if (M == 1) return run_m1(h, w, nullptr, x, false, y, false, st);
+  if (M == 1 && !invariant(h)) return run_m1(h, w, nullptr, x, false, y, false, st);
   return run_xs(h, w, nullptr, x, nullptr, M, y, false, h->N, st);
 }
 
@@ -980,7 +992,7 @@ qg_status qgemv_run_batch(int32_t n, const qg_handle* hs, const uint16_t* const*
     if (!aligned16(xs[i]) || !aligned16(ys[i])) return fail(QG_ERR_INVALID_ARG, "x and y of entry %d must be 16-byte aligned", i);
     for (int k = 0; k < i; ++k)
       if (hs[k] == hs[i]) return fail(QG_ERR_INVALID_ARG, "entries %d and %d share a handle (and its workspace)", k, i);
-    if (hs[i]->format != QG_FMT_UNIFORM || hs[i]->device != hs[0]->device) one_launch = false;
+    if (hs[i]->format != QG_FMT_UNIFORM || hs[i]->device != hs[0]->device || invariant(hs[i])) one_launch = false;
   }
   hipStream_t st = (hipStream_t)stream;
   if (one_launch) return run_batch_m1(n, hs, xs, ys, st);
@@ -1002,8 +1014,10 @@ qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t*
   if (down->K != gate->N) return fail(QG_ERR_INVALID_ARG, "down K (%d) != gate N (%d)", down->K, gate->N);
   if (M < 1 || M > gate->max_M || M > down->max_M) return fail(QG_ERR_INVALID_ARG, "M = %d out of range", M);
   if (!aligned16(x) || !aligned16(out)) return fail(QG_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+  if (invariant(gate) != invariant(up) || invariant(gate) != invariant(down))
+    return fail(QG_ERR_INVALID_ARG, "gate, up and down must agree on QG_FLAG_BATCH_INVARIANT");
   hipStream_t st = (hipStream_t)stream;
-  if (M == 1) {
+  if (M == 1 && !invariant(gate)) {
     const qg_status s = run_m1(gate, gate->ws, up, x, false, gate->h32, true, st);
     if (s != QG_OK) return s;
     return run_m1(down, down->ws, nullptr, gate->h32, true, out, false, st);

@@ -94,7 +94,19 @@ typedef enum {
 typedef enum { QG_FMT_UNIFORM = 0, QG_FMT_TRELLIS3 = 1 } qg_format;
 
 enum {
-  QG_FLAG_X_PREROTATED = 1u << 0 /* TRELLIS3: x already rotated, skip the Walsh-Hadamard step */
+  QG_FLAG_X_PREROTATED = 1u << 0, /* TRELLIS3: x already rotated, skip the Walsh-Hadamard step */
+  /* UNIFORM only: batch-invariant rows.  Row m of a run (or qmlp_run) of M
+   * rows is bit-identical to a run of that row alone, for every M in
+   * [1, max_M]: every row count takes the verify GEMM with one launch plan
+   * (K slices, tile grouping, hand-over) fixed at create from max_M, so no
+   * row's arithmetic depends on how many rows ride along.  Speculative
+   * verification then accepts exactly the tokens that one-row decoding would
+   * produce ("Qwen3.8-27B on a 16 GB RX 9070 XT", "What we added on top of
+   * upstream": verify batches of up to 32 rows on the fast path, with the
+   * output of plain decoding).  Costs speed at M = 1 (the verify GEMM
+   * instead of the GEMV); qgemv_run_batch runs such handles entry by entry.
+   * Other formats: QG_ERR_UNSUPPORTED at create. */
+  QG_FLAG_BATCH_INVARIANT = 1u << 1
 };
 
 /* Pins (qg_weight_desc.pins): force a kernel or hand-over that the built-in

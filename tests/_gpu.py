@@ -36,7 +36,8 @@ def dev_f16(a: np.ndarray) -> torch.Tensor:
 class Uniform:
     """A seeded uniform-code (or per-column width) matrix with its handle."""
 
-    def __init__(self, N, K, bits=3, col_bits=None, cfg_id=50, tid=0, max_M=32, pins=0, launch=None):
+    def __init__(self, N, K, bits=3, col_bits=None, cfg_id=50, tid=0, max_M=32, pins=0, launch=None,
+                 batch_invariant=False):
         self.N, self.K = N, K
         self.bits = bits
         self.col_bits = col_bits
@@ -48,12 +49,12 @@ class Uniform:
         self.dw = dev_words(self.words)
         self.ds = dev_f16(self.scales)
         self.lin = Q.QLinear(self.dw, self.ds, K, N, bits=bits, col_bits=col_bits, max_M=max_M, pins=pins,
-                             launch=launch)
+                             launch=launch, batch_invariant=batch_invariant)
 
-    def relinked(self, pins=0, launch=None, max_M=32):
+    def relinked(self, pins=0, launch=None, max_M=32, batch_invariant=False):
         """A second handle over the same device bytes, with other pins / launch overrides."""
         return Q.QLinear(self.dw, self.ds, self.K, self.N, bits=self.bits, col_bits=self.col_bits, max_M=max_M,
-                         pins=pins, launch=launch)
+                         pins=pins, launch=launch, batch_invariant=batch_invariant)
 
     def codes(self, rows=None):
         if self.col_bits is None:
