@@ -20,11 +20,11 @@
 // behind them, so staging x overlaps the first code fetches; no wave waits for
 // another.
 //
-// The nch partials of one tile meet in a per-column 64-bit word: each wave
-// adds (round(v * 2^28) << 6) + 1 (v clamped to +-2^23) with one integer
-// atomic.  Integer addition is exact and commutative, so the total is the same
-// whatever the order of arrival (bit-identical results), and the low 6 bits
-// count the arrivals: the wave that brings the count to nch converts the sum
+// The nch partials of one tile meet in a per-column 64-bit fixed-point word
+// (fx_word, qg_common.h): each wave adds its partial with one integer atomic.
+// Integer addition is exact and commutative, so the total is the same
+// whatever the order of arrival (bit-identical results), and the word's low 6
+// bits count the arrivals: the wave that brings the count to nch converts the sum
 // to fp16, stores it and re-arms the word to 0 for the next launch.  With
 // nch = 1 the sum is stored directly.  For the gate/up pair every wave adds its
 // up partial, waits for that atomic to return, and only then adds its gate
