@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the MI355X
 
 
 def parse():
@@ -514,6 +515,37 @@ def main():
                 t.close()
             del tl
         result["trellis"] = tres
+
+    # ---------------- prefill route: dequantise to fp16, then a plain fp16 GEMM ----------------
+    # gate/up shape; each call reads its codes from HBM (weight copies in
+    # rotation); beside it the fp16 GEMM alone on the weights the last call
+    # dequantised (what the route costs over a dense fp16 model)
+    if not args.quick:
+        ig = 4
+        N, K = shapes[ig]["N"], shapes[ig]["K"]
+        full = lins[0][ig].prefill_workspace()[1]
+        wsb = torch.empty(full, dtype=torch.uint8, device=dev)
+        wf = wsb[32 << 20:(32 << 20) + N * K * 2].view(torch.float16).view(N, K)
+        pres = {"K": K, "N": N, "weight_bytes": lins[0][ig].weight_bytes(), "copies": R}
+        for M in (64, 256, 1024, 2048):
+            xp = df16(S.activations(M, K, cfg_id=S.CFG_DECODE, tensor_id=S.T_X + 1000 + M))
+            yp = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+            def f(xp=xp, yp=yp):
+                for r in range(R):
+                    lins[r][ig].run_prefill(xp, out=yp, workspace=wsb)
+            us = graph_us(capture(f), R, reps=3, trials=3)
+
+            def fg(xp=xp, yp=yp):
+                torch.mm(xp, wf.t(), out=yp)
+            gus = graph_us(capture(fg), 1, reps=10, trials=3)
+            tf = 2.0 * M * N * K / us / 1e6
+            pres[f"M{M}"] = {"us": round(us, 3), "TFLOPs": round(tf, 1),
+                             "pct_fp16_mfma_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1),
+                             "fp16_gemm_alone_us": round(gus, 3), "route_over_gemm": round(us / gus, 3)}
+            log("prefill", M, pres[f"M{M}"])
+        result["prefill_gateup"] = pres
+        del wsb, wf
 
     # ---------------- CPU oracle on a bounded sample ----------------
     if not args.no_cpu:

@@ -76,8 +76,10 @@ def lib() -> ctypes.CDLL:
     L.qgemv_debug_dequant.argtypes = [vp, vp, u16p, vp]
     L.qgemv_debug_operand.argtypes = [vp, vp, vp, vp, vp]
     L.qgemv_debug_trellis.argtypes = [vp, vp, vp]
+    L.qgemv_run_prefill.argtypes = [vp, vp, i32, vp, vp, ctypes.c_size_t, vp]
+    L.qgemv_prefill_workspace.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     for f in ("qgemv_create", "qgemv_run", "qmlp_run", "qgemv_destroy", "qgemv_weight_bytes", "qg_stream_read",
-              "qgemv_run_batch", "qgemv_run_noalloc",
+              "qgemv_run_batch", "qgemv_run_noalloc", "qgemv_run_prefill", "qgemv_prefill_workspace",
               "qgemv_debug_unpack", "qgemv_debug_dequant", "qgemv_debug_operand", "qgemv_debug_trellis"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -157,6 +159,25 @@ class QLinear:
         return out
 
     __call__ = run
+
+    def prefill_workspace(self):
+        """(least, full) workspace bytes of run_prefill."""
+        lo, full = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(lib().qgemv_prefill_workspace(self._h, ctypes.byref(lo), ctypes.byref(full)))
+        return int(lo.value), int(full.value)
+
+    def run_prefill(self, x, out=None, workspace=None, stream=None):
+        """y = x W^T for any row count through the dequantise-then-fp16-GEMM route.
+        workspace: a CUDA uint8 tensor (default: the full size, allocated here)."""
+        import torch
+        M = x.shape[0]
+        if out is None:
+            out = torch.empty((M, self.N), dtype=torch.float16, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(self.prefill_workspace()[1], dtype=torch.uint8, device=x.device)
+        nbytes = int(workspace.numel() * workspace.element_size())
+        _check(lib().qgemv_run_prefill(self._h, _ptr(x), int(M), _ptr(out), _ptr(workspace), nbytes, _stream(stream)))
+        return out
 
     def weight_bytes(self) -> int:
         b = ctypes.c_int64()

@@ -47,7 +47,8 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         sys.stderr.write(f"--- {s}\n{r.stdout}{r.stderr}")
     if bad:
         raise RuntimeError("hipcc failed building libqgemv.so")
-    r = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", OUT + ".tmp", *objs], verbose)
+    r = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", OUT + ".tmp", *objs,
+              "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"], verbose)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed linking libqgemv.so")

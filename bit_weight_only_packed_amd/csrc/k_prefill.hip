@@ -1,0 +1,156 @@
+// k_prefill.hip -- the prefill route ("The Rock8", per-format hipBLASLt routes:
+// dequantise, then a plain fp16 GEMM): the dequantisation launcher and the GEMM
+// through hipBLASLt, one library handle per device (created on the first
+// prefill call there) and one matmul plan per problem shape (cached).
+#include <hipblaslt/hipblaslt.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "qg_launch.h"
+#include "qg_prefill.h"
+
+namespace qg {
+
+hipError_t launch_dequant_f16(const SegDev& sg, const int32_t* col_map, int G, int G4, int K, int tl0, int ntl, int n0,
+                              int n1, uint16_t* out, hipStream_t st) {
+  const int64_t n = (int64_t)ntl * G4 * 64;
+  if (n <= 0) return hipSuccess;
+  k_dequant_f16<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(sg, col_map, G, G4, K, tl0, ntl, n0, n1, out);
+  return hipGetLastError();
+}
+
+namespace {
+
+struct LtPlan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+  size_t ws = 0;
+};
+
+constexpr int kMaxLtDevices = 64;
+std::mutex g_lt_mu;
+hipblasLtHandle_t g_lt[kMaxLtDevices] = {};
+std::map<std::tuple<int, int, int, int, int, size_t>, LtPlan> g_lt_plans;  // (device, rows, M, K, ldc, ws cap)
+
+const char* lt_err(hipblasStatus_t s) {
+  switch (s) {
+    case HIPBLAS_STATUS_NOT_INITIALIZED: return "hipBLASLt not initialised";
+    case HIPBLAS_STATUS_ALLOC_FAILED: return "hipBLASLt allocation failed";
+    case HIPBLAS_STATUS_INVALID_VALUE: return "hipBLASLt invalid value";
+    case HIPBLAS_STATUS_NOT_SUPPORTED: return "hipBLASLt: problem not supported";
+    case HIPBLAS_STATUS_EXECUTION_FAILED: return "hipBLASLt execution failed";
+    default: return "hipBLASLt error";
+  }
+}
+
+}  // namespace
+
+// D (column-major, rows x M, leading dimension ldc) = W x^T: W row-major
+// [rows][K] (to hipBLASLt a column-major K x rows matrix, taken transposed), x
+// row-major [M][K] (a column-major K x M matrix).  fp16 in and out, fp32
+// accumulation and scaling.  Returns 0, or sets *err and returns nonzero.
+int gemm_f16_wxt(int dev, const uint16_t* w, int rows, const uint16_t* x, int M, int K, uint16_t* d, int ldc,
+                 void* ws, size_t ws_bytes, hipStream_t st, const char** err) {
+  if (dev < 0 || dev >= kMaxLtDevices) {
+    *err = "device index out of range";
+    return 1;
+  }
+  LtPlan plan;
+  hipblasLtHandle_t lt = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_lt_mu);
+    if (!g_lt[dev]) {
+      const hipblasStatus_t s = hipblasLtCreate(&g_lt[dev]);
+      if (s != HIPBLAS_STATUS_SUCCESS) {
+        g_lt[dev] = nullptr;
+        *err = lt_err(s);
+        return 1;
+      }
+    }
+    lt = g_lt[dev];
+    const auto key = std::make_tuple(dev, rows, M, K, ldc, ws_bytes);
+    auto it = g_lt_plans.find(key);
+    if (it == g_lt_plans.end()) {
+      LtPlan p;
+      hipblasStatus_t s = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F);
+      const int32_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
+      if (s == HIPBLAS_STATUS_SUCCESS)
+        s = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT));
+      if (s == HIPBLAS_STATUS_SUCCESS)
+        s = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN));
+      if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&p.a, HIP_R_16F, (uint64_t)K, (uint64_t)rows, K);
+      if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&p.b, HIP_R_16F, (uint64_t)K, (uint64_t)M, K);
+      if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&p.c, HIP_R_16F, (uint64_t)rows, (uint64_t)M, ldc);
+      hipblasLtMatmulPreference_t pref = nullptr;
+      if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatmulPreferenceCreate(&pref);
+      const uint64_t cap = ws_bytes;
+      if (s == HIPBLAS_STATUS_SUCCESS)
+        s = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof(cap));
+      hipblasLtMatmulHeuristicResult_t res[8];
+      int got = 0;
+      if (s == HIPBLAS_STATUS_SUCCESS)
+        s = hipblasLtMatmulAlgoGetHeuristic(lt, p.desc, p.a, p.b, p.c, p.c, pref, 8, res, &got);
+      if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+      int pick = -1;
+      for (int i = 0; i < got && pick < 0; ++i)
+        if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= ws_bytes) pick = i;
+      // several candidates and a stream that is not being captured: time each
+      // on this very problem (the output is overwritten by the real run) and
+      // keep the fastest
+      hipStreamCaptureStatus cap_st = hipStreamCaptureStatusNone;
+      if (s == HIPBLAS_STATUS_SUCCESS && pick >= 0 && got > 1 && hipStreamIsCapturing(st, &cap_st) == hipSuccess &&
+          cap_st == hipStreamCaptureStatusNone) {
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+          const float alpha = 1.0f, beta = 0.0f;
+          float best = 1e30f;
+          for (int i = 0; i < got; ++i) {
+            if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > ws_bytes) continue;
+            auto run = [&]() {
+              return hipblasLtMatmul(lt, p.desc, &alpha, w, p.a, x, p.b, &beta, d, p.c, d, p.c, &res[i].algo, ws,
+                                     res[i].workspaceSize, st);
+            };
+            if (run() != HIPBLAS_STATUS_SUCCESS) continue;
+            hipEventRecord(e0, st);
+            bool ok = true;
+            for (int r = 0; r < 3 && ok; ++r) ok = run() == HIPBLAS_STATUS_SUCCESS;
+            hipEventRecord(e1, st);
+            float ms = 0.0f;
+            if (ok && hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess &&
+                ms < best) {
+              best = ms;
+              pick = i;
+            }
+          }
+        }
+        if (e0) hipEventDestroy(e0);
+        if (e1) hipEventDestroy(e1);
+      }
+      if (s != HIPBLAS_STATUS_SUCCESS || pick < 0) {
+        if (p.a) hipblasLtMatrixLayoutDestroy(p.a);
+        if (p.b) hipblasLtMatrixLayoutDestroy(p.b);
+        if (p.c) hipblasLtMatrixLayoutDestroy(p.c);
+        if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+        *err = s != HIPBLAS_STATUS_SUCCESS ? lt_err(s) : "hipBLASLt found no algorithm for this shape";
+        return 1;
+      }
+      p.algo = res[pick].algo;
+      p.ws = res[pick].workspaceSize;
+      it = g_lt_plans.emplace(key, p).first;
+    }
+    plan = it->second;
+  }
+  const float alpha = 1.0f, beta = 0.0f;
+  const hipblasStatus_t s = hipblasLtMatmul(lt, plan.desc, &alpha, w, plan.a, x, plan.b, &beta, d, plan.c, d, plan.c,
+                                            &plan.algo, ws, plan.ws, st);
+  if (s != HIPBLAS_STATUS_SUCCESS) {
+    *err = lt_err(s);
+    return 1;
+  }
+  return 0;
+}
+
+}  // namespace qg

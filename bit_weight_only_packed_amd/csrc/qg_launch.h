@@ -45,4 +45,12 @@ hipError_t launch_h_to_f16(const float* h, uint16_t* x16, float* xf, int M, int 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int cus, hipStream_t st);
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);  // bytes: a multiple of 16
 
+// prefill route (k_prefill.hip): fp16 weights of output columns [n0, n1) from
+// tiles [tl0, tl0 + ntl) of a segment into out [n - n0][K]; and the fp16 GEMM
+// D (column-major rows x M, ldc) = W x^T through hipBLASLt (0, or *err set)
+hipError_t launch_dequant_f16(const SegDev& sg, const int32_t* col_map, int G, int G4, int K, int tl0, int ntl, int n0,
+                              int n1, uint16_t* out, hipStream_t st);
+int gemm_f16_wxt(int dev, const uint16_t* w, int rows, const uint16_t* x, int M, int K, uint16_t* d, int ldc,
+                 void* ws, size_t ws_bytes, hipStream_t st, const char** err);
+
 }  // namespace qg

@@ -1029,6 +1029,63 @@ qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t*
   return run_xs(down, down->ws, nullptr, gate->h16, gate->hf, M, out, false, down->N, st);
 }
 
+// ---- prefill route: dequantise to fp16 in column chunks, then hipBLASLt ----------
+namespace {
+constexpr size_t kPrefillGemmWs = (size_t)32 << 20;  // hipBLASLt workspace at the front of the caller's
+}
+
+qg_status qgemv_prefill_workspace(qg_handle h, size_t* min_bytes, size_t* full_bytes) {
+  g_err.clear();
+  if (!h || !min_bytes || !full_bytes) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  if (h->format != QG_FMT_UNIFORM) return fail(QG_ERR_UNSUPPORTED, "the prefill route takes uniform-code handles");
+  const size_t row = (size_t)h->K * sizeof(uint16_t);
+  *full_bytes = kPrefillGemmWs + (size_t)h->N * row;
+  *min_bytes = h->segs.size() == 1 ? kPrefillGemmWs + 16 * row : *full_bytes;
+  return QG_OK;
+}
+
+qg_status qgemv_run_prefill(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  g_err.clear();
+  if (!h || !x || !y || !workspace) return fail(QG_ERR_INVALID_ARG, "NULL argument");
+  if (M < 1) return fail(QG_ERR_INVALID_ARG, "M = %d is not positive", M);
+  if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(QG_ERR_INVALID_ARG, "the workspace must be 256-byte aligned");
+  size_t min_b = 0, full_b = 0;
+  qg_status s = qgemv_prefill_workspace(h, &min_b, &full_b);
+  if (s != QG_OK) return s;
+  if (ws_bytes < min_b)
+    return fail(QG_ERR_INVALID_ARG, "the prefill workspace needs at least %zu bytes (got %zu)", min_b, ws_bytes);
+  int dev = -1;
+  QG_HIP(hipGetDevice(&dev));
+  if (dev != h->device) return fail(QG_ERR_INVALID_ARG, "the handle lives on device %d, the current one is %d", h->device, dev);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t row = (size_t)h->K * sizeof(uint16_t);
+  const int nc = (int)std::min<size_t>((size_t)h->N, (ws_bytes - kPrefillGemmWs) / row) / 16 * 16;
+  uint16_t* wbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kPrefillGemmWs);
+  for (int n0 = 0; n0 < h->N; n0 += nc) {
+    const int n1 = std::min(h->N, n0 + nc);
+    if (h->segs.size() == 1) {  // one width: column n is tile n / 16, lane n % 16
+      const HostSeg& g = h->segs[0];
+      const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0};
+      QG_HIP(launch_dequant_f16(sd, h->col_map, h->G, h->G4, h->K, n0 / 16, (n1 - n0) / 16, n0, n1, wbuf, st));
+    } else {  // several widths (one chunk): every segment's columns land at their own rows
+      for (const auto& g : h->segs) {
+        const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0};
+        QG_HIP(launch_dequant_f16(sd, h->col_map, h->G, h->G4, h->K, 0, g.tiles, n0, n1, wbuf, st));
+      }
+    }
+    const char* err = nullptr;
+    if (gemm_f16_wxt(dev, wbuf, n1 - n0, x, M, h->K, y + n0, h->N, workspace, kPrefillGemmWs, st, &err) != 0)
+      return fail(QG_ERR_DEVICE, "prefill GEMM (%d x %d x %d): %s", M, n1 - n0, h->K, err);
+  }
+  if (h->debug_sync) {
+    const hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(QG_ERR_DEVICE, "prefill failed: %s", hipGetErrorString(e));
+  }
+  return QG_OK;
+}
+
 qg_status qg_stream_read(const void* buf, int64_t bytes, void* stream) {
   g_err.clear();
   if (!buf || bytes <= 0 || bytes % 16 || !aligned16(buf))

@@ -223,6 +223,29 @@ qg_status qgemv_run_noalloc(qg_handle h, const uint16_t* x, int32_t M, uint16_t*
 qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t* x, int32_t M, uint16_t* out,
                    void* stream);
 
+/* Prefill-size products (any M >= 1; the route pays off from tens of rows up):
+ * y = x * W^T by the route the pages give for prompt processing ("The Rock8",
+ * "Per-format hipBLASLt routes" and the route-crossover paragraph): the
+ * weights are dequantised to fp16 -- each w = (c - o) * s rounded once (RNE)
+ * -- and multiplied by a plain fp16 GEMM with fp32 accumulation (hipBLASLt).
+ * x: device fp16 [M][K]; y: device fp16 [M][N]; both 16-byte aligned.
+ * workspace: device, 256-byte aligned, ws_bytes long, caller-owned: its first
+ * 32 MiB are the GEMM's workspace, the rest holds fp16 weight rows of a chunk
+ * of output columns (the whole matrix when it fits; one width per handle can
+ * be cut into chunks of 16-column multiples, several widths need the whole
+ * matrix).  qgemv_prefill_workspace gives the least and the full size.
+ * Enqueues on `stream` and returns; allocates no device memory.  The first
+ * call on a device creates the library's hipBLASLt handle, and the first call
+ * for a problem shape plans it (host work; warm a shape before capturing it).
+ * UNIFORM handles only (QG_ERR_UNSUPPORTED otherwise); errors of the GEMM
+ * return QG_ERR_DEVICE with hipBLASLt's reason. */
+qg_status qgemv_run_prefill(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* Workspace sizes of qgemv_run_prefill (host out-pointers): the least it
+ * accepts and the size that holds the whole matrix's fp16 weights. */
+qg_status qgemv_prefill_workspace(qg_handle h, size_t* min_bytes, size_t* full_bytes);
+
 /* Free everything the handle owns (NULL is accepted). */
 qg_status qgemv_destroy(qg_handle h);
 
