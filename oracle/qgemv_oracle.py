@@ -99,13 +99,26 @@ def unpack_mixed(words: np.ndarray, col_bits: np.ndarray, K: int, rows=None) -> 
     return out
 
 
+def scale_group(K: int, scales: np.ndarray, N: int) -> int:
+    """The scale group size gs of an [N][K/gs] scale array: 128, or 64 / 32
+    ("The Rock8", dormant-capabilities table: int4 weight-only at group 128, 64
+    and 32; one fp16 scale per gs consecutive k of a row)."""
+    per_row = np.asarray(scales).size // N
+    assert per_row * N == np.asarray(scales).size and K % per_row == 0
+    gs = K // per_row
+    assert gs in (32, 64, 128), gs
+    return gs
+
+
 def dequant_uniform(codes: np.ndarray, scales: np.ndarray, bits) -> np.ndarray:
-    """w[n][k] = (c[n][k] - o_b) * s[n][k//128] in fp64 (exact).
+    """w[n][k] = (c[n][k] - o_b) * s[n][k // gs] in fp64 (exact); gs is the
+    scale group the scale array's shape gives (128, 64 or 32).
 
     ``bits`` is an int (all rows) or an array of per-row widths."""
     codes = np.asarray(codes, dtype=np.float64)
     N, K = codes.shape
-    s = np.repeat(np.asarray(scales, dtype=np.float64).reshape(N, K // GROUP), GROUP, axis=1)
+    gs = scale_group(K, scales, N)
+    s = np.repeat(np.asarray(scales, dtype=np.float64).reshape(N, K // gs), gs, axis=1)
     if np.ndim(bits) == 0:
         o = code_offset(int(bits))
     else:
@@ -179,7 +192,7 @@ def gemv_uniform_rows(x, words, scales, N: int, K: int, bits: int, rows) -> np.n
     words = np.asarray(words, dtype=np.uint32).reshape(N, wpr)
     rows = np.asarray(rows)
     codes = unpack_uniform(words[rows].reshape(-1), len(rows), K, bits)
-    s = np.asarray(scales).reshape(N, G)[rows]
+    s = np.asarray(scales).reshape(N, -1)[rows]
     return matmul(x, dequant_uniform(codes, s, bits))
 
 
@@ -188,7 +201,7 @@ def gemv_mixed(x, words, scales, col_bits, K: int, rows=None) -> np.ndarray:
     N = len(col_bits)
     rows = np.arange(N) if rows is None else np.asarray(rows)
     codes = unpack_mixed(words, col_bits, K, rows)
-    s = np.asarray(scales).reshape(N, K // GROUP)[rows]
+    s = np.asarray(scales).reshape(N, -1)[rows]
     return matmul(x, dequant_uniform(codes, s, np.asarray(col_bits)[rows]))
 
 

@@ -37,11 +37,11 @@ def activations(M: int, K: int, *, seed: int = 0, cfg_id: int = 0, tensor_id: in
 
 
 def scales(N: int, K: int, *, seed: int = 0, cfg_id: int = 0, tensor_id: int = T_SCALE,
-           sigma: float = 0.02, floor: float = 1e-3) -> np.ndarray:
-    """fp16 per-group scales s[N][K/128] = fp16(|N(0, sigma)| + floor)."""
-    assert K % GROUP == 0
+           sigma: float = 0.02, floor: float = 1e-3, group: int = GROUP) -> np.ndarray:
+    """fp16 per-group scales s[N][K/group] = fp16(|N(0, sigma)| + floor)."""
+    assert K % GROUP == 0 and group in (32, 64, 128)
     r = _rng(seed, cfg_id, tensor_id)
-    v = np.abs(r.standard_normal((N, K // GROUP))) * sigma + floor
+    v = np.abs(r.standard_normal((N, K // group))) * sigma + floor
     return v.astype(np.float16)
 
 

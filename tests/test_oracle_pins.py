@@ -167,6 +167,60 @@ def test_dequant_group_index_and_rows():
             assert Fraction(w[n, k]) == want
 
 
+@pytest.mark.parametrize("gs", [64, 32])
+def test_small_scale_groups_reduce_to_group_128(gs):
+    """Scales of 64 or 32 that repeat one value over each 128 give exactly the
+    group-128 weights (the pinned case above)."""
+    N, K, b = 4, 768, 3
+    rng = np.random.default_rng(gs)
+    codes = rng.integers(0, 8, size=(N, K))
+    s128 = (rng.random((N, K // 128)) + 0.25).astype(np.float16)
+    small = np.repeat(s128, 128 // gs, axis=1)
+    assert small.shape == (N, K // gs)
+    np.testing.assert_array_equal(O.dequant_uniform(codes, small, b), O.dequant_uniform(codes, s128, b))
+
+
+@pytest.mark.parametrize("gs", [64, 32])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_small_scale_groups_one_scale_moves_one_span(gs, bits):
+    """Doubling one scale of a row changes exactly that row's weights in one
+    span of gs consecutive k, and doubles them (every c - o is non-zero)."""
+    N, K = 3, 512
+    codes = np.random.default_rng(7).integers(0, 1 << bits, size=(N, K))
+    ones = np.ones((N, K // gs), dtype=np.float16)
+    base = O.dequant_uniform(codes, ones, bits)
+    for n0, i in ((0, 0), (2, K // gs - 1), (1, 5)):
+        s = ones.copy()
+        s[n0, i] = 2.0
+        w = O.dequant_uniform(codes, s, bits)
+        changed = np.argwhere(w != base)
+        assert set(changed[:, 0]) == {n0}
+        assert sorted(changed[:, 1]) == list(range(i * gs, (i + 1) * gs))
+        np.testing.assert_array_equal(w[n0, i * gs:(i + 1) * gs], 2 * base[n0, i * gs:(i + 1) * gs])
+
+
+@pytest.mark.parametrize("gs", [64, 32])
+def test_small_scale_groups_brute_force(gs):
+    """y with scale groups of 64 or 32 against exact rationals, summing span by
+    span over the scale groups."""
+    M, N, K, b = 2, 3, 256, 3
+    x = S.activations(M, K, cfg_id=98, tensor_id=gs)
+    s = S.scales(N, K, cfg_id=98, tensor_id=gs + 1, group=gs)
+    w = S.uniform_code_words(N, K, b, cfg_id=98, tensor_id=gs + 2)
+    y = O.gemv_uniform(x, w, s, N, K, b)
+    ww = np.asarray(w).reshape(N, K // 128, 4 * b)
+    o = Fraction(7, 2)
+    for m in range(M):
+        for n in range(N):
+            cs = [c for g in range(K // 128) for c in bigint_unpack_group(ww[n, g], b)]
+            acc = Fraction(0)
+            for i in range(K // gs):
+                sc = Fraction(float(s[n, i]))
+                for k in range(i * gs, (i + 1) * gs):
+                    acc += Fraction(float(x[m, k])) * (cs[k] - o) * sc
+            assert abs(y[m, n] - float(acc)) <= 1e-12 * max(1.0, abs(float(acc)))
+
+
 # ---------------------------------------------------------------------------
 # contraction: brute force with exact rationals
 # ---------------------------------------------------------------------------
