@@ -516,6 +516,36 @@ def main():
             del tl
         result["trellis"] = tres
 
+    # ---------------- W4A16 at scale groups 128, 64 and 32 (gate/up shape) ----------------
+    if not args.quick:
+        N, K = shapes[4]["N"], shapes[4]["K"]
+        w4 = S.uniform_code_words(N, K, 4, cfg_id=S.CFG_DECODE, tensor_id=S.T_CODES + 500)
+        fres = {}
+        for gs in (128, 64, 32):
+            sc = S.scales(N, K, cfg_id=S.CFG_DECODE, tensor_id=S.T_SCALE + 500 + gs, group=gs)
+            wb = w4.nbytes + sc.nbytes
+            Rf = int(np.ceil((1 << 30) / wb))
+            dwf, dsf = dw(w4), df16(sc)
+            fl = [Q.QLinear(dwf, dsf, K, N, bits=4, max_M=32, group_size=gs) for _ in range(Rf)]
+            row = {"weight_bytes": wb, "copies": Rf}
+            for M in (1, 8, 32):
+                xf = xk[(M, K)]
+                out = ys[M][:, :N]
+
+                def f(fl=fl, xf=xf, out=out):
+                    for l in fl:
+                        l.run(xf, out=out)
+                us = graph_us(capture(f), Rf, reps=10, trials=3)
+                row[f"us_M{M}"] = round(us, 3)
+                row[f"GBs_M{M}"] = round(wb / us / 1e3, 1)
+            row["ratio_M32_M1"] = round(row["us_M32"] / row["us_M1"], 3)
+            fres[f"g{gs}"] = row
+            log("w4a16", gs, row)
+            for l in fl:
+                l.close()
+            del fl, dwf, dsf
+        result["w4a16_gateup"] = fres
+
     # ---------------- prefill route: dequantise to fp16, then a plain fp16 GEMM ----------------
     # gate/up shape; each call reads its codes from HBM (weight copies in
     # rotation); beside it the fp16 GEMM alone on the weights the last call

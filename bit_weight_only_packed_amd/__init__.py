@@ -119,13 +119,15 @@ class QLinear:
     pins: PIN_* bits; launch: optional {row class 0/1/2: (tiles, waves, splits)}
     launch-geometry overrides (both fixed at create).  batch_invariant: row m of
     an M-row run is bit-identical to running that row alone (uniform codes).
+    group_size: the scale group, 128 (scales [N][K/128]) or, for uniform
+    codes, 64 or 32 (scales [N][K/64] or [N][K/32]).
     """
 
     def __init__(self, codes, scales, K: int, N: int, bits: int = 3, col_bits=None, max_M: int = 32,
                  trellis: bool = False, codebook=None, prerotated: bool = False, stream=None,
-                 pins: int = 0, launch=None, batch_invariant: bool = False):
+                 pins: int = 0, launch=None, batch_invariant: bool = False, group_size: int = GROUP):
         d = _Desc()
-        d.K, d.N, d.group_size = int(K), int(N), GROUP
+        d.K, d.N, d.group_size = int(K), int(N), int(group_size)
         d.format = FMT_TRELLIS3 if trellis else FMT_UNIFORM
         self._cb_host = None
         if not trellis and col_bits is not None:

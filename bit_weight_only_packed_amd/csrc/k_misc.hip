@@ -8,11 +8,11 @@
 namespace qg {
 
 hipError_t launch_repack_uniform(const uint32_t* canon, const int64_t* row_off, const uint16_t* scales,
-                                 const int32_t* cols, int bits, int tiles, int G, int G4, uint32_t* dcodes,
+                                 const int32_t* cols, int bits, int tiles, int G, int G4, int gs, uint32_t* dcodes,
                                  uint16_t* dscales, hipStream_t st) {
   const size_t nslot = (size_t)tiles * G4 * 64;
   k_repack_uniform<<<(unsigned)((nslot + 255) / 256), 256, 0, st>>>(canon, row_off, scales, cols, bits, tiles, G, G4,
-                                                                   dcodes, dscales);
+                                                                   gs, dcodes, dscales);
   return hipGetLastError();
 }
 

@@ -12,10 +12,12 @@ constexpr int MAX_SEG = 3;
 
 struct SegDev {
   const uint32_t* codes;   // device layout, [tiles][G4][bits][64][4] words
-  const uint16_t* scales;  // [tiles][G4][16][4] fp16
+  const uint16_t* scales;  // fp16, [tiles][G4][16][4]; sq: [tiles][G4][4][16][4]
   int bits;                // 2, 3 or 4
   int tiles;               // 16-column tiles in this segment
   int tile0;               // index of the first tile in the handle's padded column space
+  int sq;                  // scale group 64 or 32: one scale per lane quarter (32 weights) and
+                           // group of 128 instead of one per column and group (qg_common.h)
 };
 
 struct WSet {

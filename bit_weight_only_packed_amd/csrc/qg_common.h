@@ -52,9 +52,20 @@ __device__ __forceinline__ void store_y(void* y, size_t i, float v, int yf32) {
   else reinterpret_cast<uint16_t*>(y)[i] = f2h(v);
 }
 
-// scale of group g, column j of tile t (scales layout [tile][G4][16][4])
-__device__ __forceinline__ size_t scale_index(int t, int G4, int g, int j) {
-  return (((size_t)t * G4 + (g >> 2)) * 16 + j) * 4 + (g & 3);
+// Scales of a quad (4 groups of 128) in the device layout.  Group size 128:
+// [16 columns][4 groups], 128 B, one scale per column and group.  Group size
+// 64 or 32 ("sq"): [4 lane quarters][16 columns][4 groups], 512 B: lane l
+// holds weights 32 (l >> 4) .. + 31 of each group of its column, which lie in
+// one scale group (of 64: groups 2g + (l >> 5); of 32: 4g + (l >> 4)), so each
+// lane still meets one scale per group of 128 and loads its 4 with one 8-byte
+// load.
+__host__ __device__ constexpr uint32_t scale_quad_halves(int sq) { return sq ? 256u : 64u; }
+__device__ __forceinline__ uint32_t scale_lane_byte(int sq, uint32_t lane) {
+  return ((sq ? (lane >> 4) << 4 : 0u) + (lane & 15u)) * 8u;
+}
+// scale of group g for column j, lane quarter q of tile t
+__device__ __forceinline__ size_t scale_index(int t, int G4, int g, int j, int q, int sq) {
+  return ((size_t)t * G4 + (g >> 2)) * scale_quad_halves(sq) + ((sq ? 16 * q : 0) + j) * 4 + (g & 3);
 }
 
 // ---------------------------------------------------------------------------

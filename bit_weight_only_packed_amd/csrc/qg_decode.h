@@ -197,6 +197,23 @@ __device__ __forceinline__ void decode_group_off1(const uint32_t (&w)[4 * B], in
   decode_off1<B>(g, r);
 }
 
+// MFMA operand with the scale inside (scale groups of 64 or 32, where one MFMA
+// spans lanes of four different scales): each pair at offset 1 under the
+// exponent of 1024 is the exact fp16 pair 1024 + 2c; one exact packed
+// subtraction of 1024 + 2 o leaves 2 (c - o) (|.| <= 15), and one packed
+// multiplication by the lane's scale pair s2 = (s, s) rounds 2 (c - o) s once
+// to fp16 (RNE).  The MFMA chain then yields 2 y, halved on output.
+template <int B>
+__device__ __forceinline__ void decode_group_scaled(const uint32_t (&w)[4 * B], int gi, uint32_t s2, uint32_t (&r)[16]) {
+  decode_group_off1<B>(w, gi, r);
+  constexpr uint32_t kExp = 0x64006400u;  // fp16 1024 in both halves
+  constexpr uint32_t kOff = (uint32_t)(0x8000u | 0x6400u | ((1u << B) - 1u));  // fp16 -(1024 + 2 o)
+  const h2_t off = as_h2(kOff | (kOff << 16));
+  const h2_t sc = as_h2(s2);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = __builtin_bit_cast(uint32_t, (as_h2(r[i] | kExp) + off) * sc);
+}
+
 template <int B>
 __device__ __forceinline__ void decode_group_classes(const uint32_t (&w)[4 * B], int gi, uint32_t (&r)[16]) {
   uint32_t g[B];

@@ -59,11 +59,14 @@ __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, 
   uint2 sc[NQ];
   {
     const size_t qoff = (size_t)tile * G4 + qb;
+    const int sq = __builtin_amdgcn_readfirstlane(sd.sq);
+    const uint32_t sqb = scale_quad_halves(sq) * 2u;  // scale bytes per quad
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(uniform_ptr(sd.codes) + qoff * (B * 256), (uint32_t)nvalid * (B * 1024u));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(sd.scales) + qoff * 64, (uint32_t)nvalid * 128u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(sd.scales) + qoff * scale_quad_halves(sq), (uint32_t)nvalid * sqb);
+    const uint32_t slane = scale_lane_byte(sq, (uint32_t)lane);
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)(lane & 15) * 8u, (uint32_t)u * 128u, 0);
+      const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, slane, (uint32_t)u * sqb, 0);
       sc[u] = make_uint2(v.x, v.y);
       buffer_quad<B>(rc, (uint32_t)lane, u, cw[u]);
     }

@@ -18,9 +18,10 @@ hipError_t launch_gemv_sk(const SkArgs& a, bool dual, int NW, size_t lds, unsign
 hipError_t m1_allow_lds();  // lets the M = 1 kernels take more than 64 KiB of dynamic LDS
 
 // verify GEMM (k_xs1.hip: MT = 1, k_xs2.hip: MT = 2)
-hipError_t launch_gemm_xs1(const XsArgs& a, int T, bool dual, bool xsc, int NQ, int bf, int NW, size_t lds,
+// sq: per-lane-quarter scales (scale groups of 64 or 32)
+hipError_t launch_gemm_xs1(const XsArgs& a, int T, bool dual, bool xsc, int NQ, int bf, bool sq, int NW, size_t lds,
                            unsigned grid, hipStream_t st);
-hipError_t launch_gemm_xs2(const XsArgs& a, int T, bool dual, bool xsc, int NQ, int bf, int NW, size_t lds,
+hipError_t launch_gemm_xs2(const XsArgs& a, int T, bool dual, bool xsc, int NQ, int bf, bool sq, int NW, size_t lds,
                            unsigned grid, hipStream_t st);
 hipError_t xs1_allow_lds();
 hipError_t xs2_allow_lds();
@@ -36,7 +37,7 @@ hipError_t launch_debug_trellis(const uint32_t* codes, const uint16_t* scales, c
 
 // create-time, checking and measurement kernels (k_misc.hip)
 hipError_t launch_repack_uniform(const uint32_t* canon, const int64_t* row_off, const uint16_t* scales,
-                                 const int32_t* cols, int bits, int tiles, int G, int G4, uint32_t* dcodes,
+                                 const int32_t* cols, int bits, int tiles, int G, int G4, int gs, uint32_t* dcodes,
                                  uint16_t* dscales, hipStream_t st);
 // mode 0: the GEMV class decode; mode 1: the verify GEMM's operand decode
 hipError_t launch_debug_uniform(const SegDev& sg, const int32_t* col_map, int G, int G4, int K, int mode,

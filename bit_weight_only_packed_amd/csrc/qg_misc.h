@@ -12,9 +12,10 @@ namespace qg {
 // create-time re-layout: canonical stream -> device layout (one thread per
 // tile, quad and lane)
 // ---------------------------------------------------------------------------
+// gs: the scale group size (128, 64 or 32; scales_in is [N][K / gs])
 __global__ void k_repack_uniform(const uint32_t* __restrict__ canon, const int64_t* __restrict__ row_off,
                                  const uint16_t* __restrict__ scales_in, const int32_t* __restrict__ cols,
-                                 int bits, int tiles, int G, int G4, uint32_t* __restrict__ dcodes,
+                                 int bits, int tiles, int G, int G4, int gs, uint32_t* __restrict__ dcodes,
                                  uint16_t* __restrict__ dscales) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)tiles * G4 * 64;
@@ -56,10 +57,13 @@ __global__ void k_repack_uniform(const uint32_t* __restrict__ canon, const int64
   uint4* dst = reinterpret_cast<uint4*>(dcodes);
   for (int p = 0; p < bits; ++p)
     dst[((size_t)tq * bits + p) * 64 + lane] = make_uint4(out[4 * p], out[4 * p + 1], out[4 * p + 2], out[4 * p + 3]);
-  if (q == 0) {
+  const int sq = gs < 128;
+  if (sq || q == 0) {
+    const int gpr = G * (128 / gs);  // scales per row
     for (int gi = 0; gi < 4; ++gi) {
       const int g = 4 * qu + gi;
-      dscales[((size_t)tq * 16 + j) * 4 + gi] = (n >= 0 && g < G) ? scales_in[(int64_t)n * G + g] : (uint16_t)0;
+      const int sg = (g * 128 + 32 * q) / gs;  // the scale group of this lane's 32 weights
+      dscales[scale_index(t, G4, g, j, q, sq)] = (n >= 0 && g < G) ? scales_in[(int64_t)n * gpr + sg] : (uint16_t)0;
     }
   }
 }
@@ -80,7 +84,9 @@ __device__ __forceinline__ void debug_quad(const SegDev& sg, int G4, int tl, int
 // MODE 0: the M = 1 GEMVs' class decode (codes, exact q = c - o and w = q * s).
 // MODE 1: the verify GEMM's MFMA operand decode (codes read back out of the
 // offset-1 operand registers, the operand's fp16 bits, and w rebuilt from the
-// operand value and the kernel's offset constant: (op + ko) * 2^23 * s).
+// operand value and the kernel's offset constant: (op + ko) * 2^23 * s).  With
+// scale groups of 64 or 32 the operand carries the scale: its fp16 bits are
+// 2 (c - o) s rounded once, and w is half its value.
 template <int B, int MODE>
 __device__ __forceinline__ void debug_slot(const SegDev& sg, const int32_t* col_map, int G, int G4, int K,
                                            int64_t gid, int32_t* codes, float* w, uint16_t* q16) {
@@ -93,10 +99,12 @@ __device__ __forceinline__ void debug_slot(const SegDev& sg, const int32_t* col_
   if (n < 0) return;
   uint32_t cw[4 * B];
   debug_quad<B>(sg, G4, tl, g, lane, cw);
-  uint32_t r[16];
+  uint32_t r[16], rs[16];
+  const uint16_t s16 = sg.scales[scale_index(tl, G4, g, j, q, sg.sq)];
   if constexpr (MODE == 0) decode_group_classes<B>(cw, g & 3, r);
   else decode_group_off1<B>(cw, g & 3, r);
-  const float s = h2f(sg.scales[scale_index(tl, G4, g, j)]);
+  if (MODE == 1 && sg.sq) decode_group_scaled<B>(cw, g & 3, (uint32_t)s16 | ((uint32_t)s16 << 16), rs);
+  const float s = h2f(s16);
   const float o = 0.5f * (float)((1 << B) - 1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -111,6 +119,10 @@ __device__ __forceinline__ void debug_slot(const SegDev& sg, const int32_t* col_
         const float qv = (float)c - o;                 // exact
         if (w) w[at] = qv * s;                         // exact in fp32
         if (q16) q16[at] = f2h(qv);
+      } else if (sg.sq) {
+        const uint16_t op = (uint16_t)(rs[i] >> (16 * h));  // fp16 bits of 2 (c - o) s, rounded once
+        if (q16) q16[at] = op;
+        if (w) w[at] = 0.5f * h2f(op);
       } else {
         const uint16_t op = (uint16_t)(r[i] >> (16 * h));  // the operand element: fp16 bits of c * 2^-23
         if (q16) q16[at] = op;

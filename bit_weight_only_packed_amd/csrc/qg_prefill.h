@@ -26,7 +26,7 @@ __device__ __forceinline__ void dq_quad(const SegDev& sg, const int32_t* col_map
     const uint4 v = src[p * 64];
     cw[4 * p] = v.x; cw[4 * p + 1] = v.y; cw[4 * p + 2] = v.z; cw[4 * p + 3] = v.w;
   }
-  const uint2 sw = *reinterpret_cast<const uint2*>(sg.scales + (tq * 16 + j) * 4);
+  const uint2 sw = *reinterpret_cast<const uint2*>(sg.scales + scale_index(tl, G4, 4 * qu, j, q, sg.sq));
   const float o = 0.5f * (float)((1 << B) - 1);
   uint16_t* row = out + (size_t)(n - n0) * K + 32 * q;
 #pragma unroll

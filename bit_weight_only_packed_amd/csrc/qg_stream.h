@@ -49,6 +49,7 @@ template <int ND>
 struct SkPtrs {
   const uint32_t* codes[ND];
   const uint16_t* scales[ND];
+  int sq;  // the scale layout (qg_common.h), the same for both matrices
 };
 
 // unit u (segment-local: tile u / G4, quad u % G4) of the segment's matrices
@@ -57,8 +58,9 @@ __device__ __forceinline__ void sk_load(const SkPtrs<ND>& p, SkUnit<B, ND>& c, i
   const uint32_t uc = live ? (uint32_t)u : 0u;
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scales[d] + (size_t)uc * 64, live ? 128u : 0u);
-    const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)(lane & 15) * 8u, 0, 0);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(p.scales[d] + (size_t)uc * scale_quad_halves(p.sq), live ? scale_quad_halves(p.sq) * 2u : 0u);
+    const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, scale_lane_byte(p.sq, (uint32_t)lane), 0, 0);
     c.sc[d] = make_uint2(v.x, v.y);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes[d] + (size_t)uc * (B * 256), live ? B * 1024u : 0u);
     buffer_quad<B>(rc, (uint32_t)lane, 0, c.cw[d]);
@@ -81,6 +83,7 @@ __device__ __forceinline__ void sk_prime(SkPipe<B, ND>& pp, const SegDev (&sd)[2
     pp.ptr.codes[d] = uniform_ptr(sd[d].codes);
     pp.ptr.scales[d] = uniform_ptr(sd[d].scales);
   }
+  pp.ptr.sq = __builtin_amdgcn_readfirstlane(sd[0].sq);
 #pragma unroll
   for (int i = 0; i < SK_PD; ++i) sk_load<B, ND>(pp.ptr, pp.c[i], u0 + i, u0 + i < u1, lane);
 }

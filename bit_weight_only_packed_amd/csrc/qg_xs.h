@@ -23,6 +23,11 @@
 // (the fp32 intermediate rounded once with a block exponent, qg_misc.h), and
 // multiplies each row's chain by that row and group's 2^-e as well.
 //
+// Scale groups of 64 or 32 (SQ): one MFMA spans lanes of four different scales,
+// so the scale goes into the B operand instead (decode_group_scaled: 2 (c - o)
+// s rounded once to fp16); the chains then need no offset term and no group
+// sums, run on across groups, and yield 2 y.
+//
 // K slices meet in one of two ways, both independent of the order of arrival.
 // Few outputs: in fixed-point words (see fx_word), one integer atomic per
 // output and slice, whose returned count tells the last slice to store the
@@ -49,9 +54,10 @@ template <int B, int T, int ND> constexpr int xs_loads() { return ND * T * (B + 
 
 // the code and scale loads of unit (tile group tg, quad q); a dead unit (or a
 // tile past the segment) loads through an empty range: zeros, no memory access
-template <int B, int T, int ND>
+template <int B, int T, int ND, bool SQ>
 __device__ __forceinline__ void xs_load(XsUnit<B, T, ND>& c, const SegDev (&sd)[2], int tg, int q, bool live, int G4,
                                         uint32_t lane) {
+  constexpr int sq = SQ ? 1 : 0;
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -60,16 +66,17 @@ __device__ __forceinline__ void xs_load(XsUnit<B, T, ND>& c, const SegDev (&sd)[
       const bool ok = live && tile < sd[d].tiles;
       const size_t qb = ok ? (size_t)tile * G4 + q : 0;
       const __amdgpu_buffer_rsrc_t rc = make_rsrc(uniform_ptr(sd[d].codes) + qb * (B * 256), ok ? B * 1024u : 0u);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(sd[d].scales) + qb * 64, ok ? 128u : 0u);
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(uniform_ptr(sd[d].scales) + qb * scale_quad_halves(sq), ok ? scale_quad_halves(sq) * 2u : 0u);
       buffer_quad<B>(rc, lane, 0, c.cw[d][t]);
-      const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, (lane & 15u) * 8u, 0, 0);
+      const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, scale_lane_byte(sq, lane), 0, 0);
       c.sc[d][t] = make_uint2(v.x, v.y);
     }
 }
 
 // one unit: groups gl0 .. gl0 + ngr - 1 of the slice against the unit's tiles;
 // xa[mt][v]: this lane's A-fragment address of group 0 (add 256 per group)
-template <int B, int T, int MT, int ND, bool XSC>
+template <int B, int T, int MT, int ND, bool XSC, bool SQ>
 __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* const (&xa)[MT][4], const float* xsum,
                                         const float* xfac, int gl0, int ngr, int lane, f4_t (&R)[ND][T][MT]) {
   const int kq = lane >> 4;
@@ -85,8 +92,33 @@ __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* c
 #pragma unroll
       for (int v = 0; v < 4; ++v) A[mt][v] = *reinterpret_cast<const h8_t*>(xa[mt][v] + gl * 256);
       // chain start: rows 16 mt + 4 kq + e (sums past M are never stored either)
-      C0[mt] = *reinterpret_cast<const f4_t*>(xsum + gl * (16 * MT) + 16 * mt + 4 * kq) * ko;
+      if constexpr (!SQ) C0[mt] = *reinterpret_cast<const f4_t*>(xsum + gl * (16 * MT) + 16 * mt + 4 * kq) * ko;
       if constexpr (XSC) F[mt] = *reinterpret_cast<const f4_t*>(xfac + gl * (16 * MT) + 16 * mt + 4 * kq);
+    }
+    if constexpr (SQ) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint32_t sw = (gi < 2) ? c.sc[d][t].x : c.sc[d][t].y;
+          const uint32_t sh = (gi & 1) ? (sw >> 16) : (sw & 0xFFFFu);
+          uint32_t r[16];
+          decode_group_scaled<B>(c.cw[d][t], gi, sh | (sh << 16), r);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            f4_t cc = XSC ? f4_t{0.0f, 0.0f, 0.0f, 0.0f} : R[d][t][mt];  // without factors: one chain throughout
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              cc = mfma16(A[mt][v], as_h8(r[4 * v], r[4 * v + 1], r[4 * v + 2], r[4 * v + 3]), cc);
+            if constexpr (XSC) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) R[d][t][mt][e] = __builtin_fmaf(F[mt][e], cc[e], R[d][t][mt][e]);
+            } else {
+              R[d][t][mt] = cc;
+            }
+          }
+        }
+      continue;
     }
 #pragma unroll
     for (int d = 0; d < ND; ++d)
@@ -109,9 +141,10 @@ __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* c
   }
 }
 
-template <int B, int T, int MT, int ND, int NQ, bool XSC>
+template <int B, int T, int MT, int ND, int NQ, bool XSC, bool SQ>
 __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], int s, int q0, int nq, int tgb, int tge,
                                         int tgbase, char* smem) {
+  constexpr float kOut = SQ ? 0.5f : 8388608.0f;  // the chains' unit: 2 y (SQ) or 2^-23 y
   const int lane = threadIdx.x & 63;
   const int NW = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -169,7 +202,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
   XsUnit<B, T, ND> c[XS_PD];
 #pragma unroll
   for (int i = 0; i < XS_PD; ++i) {
-    xs_load<B, T, ND>(c[i], sd, tg, q0 + i, mine && i < nq, G4, (uint32_t)lane);
+    xs_load<B, T, ND, SQ>(c[i], sd, tg, q0 + i, mine && i < nq, G4, (uint32_t)lane);
     __builtin_amdgcn_sched_barrier(0);  // unit by unit, in order of use
   }
   {
@@ -190,7 +223,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
   // hit 16 bank groups); the order depends on the group only, never on the
   // row's place in the batch (the row swizzle is undone on the address), so a
   // row's sums round the same at every row count
-  {
+  if constexpr (!SQ) {
     const uint32_t ones = 0x3C003C00u;
     const int gl = lane & 31;
     for (int mb = 2 * wave; mb < M; mb += 2 * NW) {
@@ -241,9 +274,9 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
   // it the wait for that unit's codes)
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    if (i < nq) xs_unit<B, T, MT, ND, XSC>(c[i % XS_PD], xa, xsum, xfac, 4 * i, min(4, G - 4 * (q0 + i)), lane, R);
+    if (i < nq) xs_unit<B, T, MT, ND, XSC, SQ>(c[i % XS_PD], xa, xsum, xfac, 4 * i, min(4, G - 4 * (q0 + i)), lane, R);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + XS_PD < NQ) xs_load<B, T, ND>(c[i % XS_PD], sd, tg, q0 + i + XS_PD, i + XS_PD < nq, G4, (uint32_t)lane);
+    if (i + XS_PD < NQ) xs_load<B, T, ND, SQ>(c[i % XS_PD], sd, tg, q0 + i + XS_PD, i + XS_PD < nq, G4, (uint32_t)lane);
     __builtin_amdgcn_sched_barrier(0);
   }
   // ---- results: stored directly (one slice), or added to the fixed-point
@@ -263,8 +296,8 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
         for (int e = 0; e < 4; ++e) {
           const int m = 16 * mt + 4 * mq + e;
           if (m >= M) continue;
-          const float v0 = R[0][t][mt][e] * 8388608.0f;  // 2^23
-          const float v1 = R[ND - 1][t][mt][e] * 8388608.0f;
+          const float v0 = R[0][t][mt][e] * kOut;
+          const float v1 = R[ND - 1][t][mt][e] * kOut;
           store_y(a.y, (size_t)m * a.ldy + n, ND == 2 ? silu_mul(v0, v1) : v0, a.yf32);
         }
     }
@@ -290,7 +323,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
             const int m = 16 * mt + 4 * mq + e;
             const int pc = 16 * (sd[0].tile0 + tg * T + t) + j;
             if ((t == 0 ? live0 : live1) && m < M)
-              fx_add(W + up_off + (size_t)m * a.NP + pc, fx_word(R[1][t][mt][e] * 8388608.0f));
+              fx_add(W + up_off + (size_t)m * a.NP + pc, fx_word(R[1][t][mt][e] * kOut));
           }
       __builtin_amdgcn_s_waitcnt(0);
     }
@@ -300,7 +333,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ag[t][mt][e] = fx_word(R[0][t][mt][e] * 8388608.0f);
+        for (int e = 0; e < 4; ++e) ag[t][mt][e] = fx_word(R[0][t][mt][e] * kOut);
     unsigned long long* const wl = W + (size_t)(4 * mq) * a.NP + 16 * (sd[0].tile0 + tg * T) + j;
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -352,7 +385,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
         if (m >= M) continue;
 #pragma unroll
         for (int d = 0; d < ND; ++d)
-          st_partial(a.partial + ((size_t)(d * S + s) * M + m) * a.NP + pc, R[d][t][mt][e] * 8388608.0f);  // 2^23
+          st_partial(a.partial + ((size_t)(d * S + s) * M + m) * a.NP + pc, R[d][t][mt][e] * kOut);
       }
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
@@ -426,7 +459,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
 }
 
 // NQ: the most quads a slice may have (the kernel is straight-line code over them)
-template <int T, int MT, bool DUAL, int BF, int NQ, bool XSC>
+template <int T, int MT, bool DUAL, int BF, int NQ, bool XSC, bool SQ>
 __global__ __launch_bounds__(512) void k_gemm_xs(XsArgs a) {
   static_assert(!(DUAL && XSC), "the fused gate/up pass reads plain fp16 x");
   extern __shared__ __align__(16) char smem[];
@@ -444,10 +477,10 @@ __global__ __launch_bounds__(512) void k_gemm_xs(XsArgs a) {
   const int q0 = (int)((int64_t)s * G4 / S), q1 = (int)((int64_t)(s + 1) * G4 / S);
   const int bits = sd[0].bits;
   if (BF == 2 || (BF == 0 && bits == 2))
-    xs_body<2, T, MT, ND, NQ, XSC>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
+    xs_body<2, T, MT, ND, NQ, XSC, SQ>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
   else if (BF == 3 || (BF == 0 && bits == 3))
-    xs_body<3, T, MT, ND, NQ, XSC>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
-  else xs_body<4, T, MT, ND, NQ, XSC>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
+    xs_body<3, T, MT, ND, NQ, XSC, SQ>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
+  else xs_body<4, T, MT, ND, NQ, XSC, SQ>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
 }
 
 }  // namespace qg

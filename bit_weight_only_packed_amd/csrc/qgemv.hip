@@ -60,6 +60,7 @@ struct Work {
 
 struct HostSeg {
   int bits, tiles, tile0, ncols;
+  int sq = 0;  // scale group 64 or 32 (per-lane-quarter scale layout)
   uint32_t* codes = nullptr;
   uint16_t* scales = nullptr;
 };
@@ -72,6 +73,7 @@ int mclass(int M) { return M <= 1 ? 0 : (M <= 16 ? 1 : 2); }
 
 struct qg_plan {
   int K = 0, N = 0, G = 0, G4 = 0, format = 0, max_M = 0;
+  int group_size = QG_GROUP;      // scale group: 128, or 64 / 32 (uniform codes)
   uint32_t flags = 0, pins = 0;
   bool debug_sync = false;        // QG_DEBUG_SYNC set at create: synchronise and check after each run
   int device = 0;
@@ -114,7 +116,7 @@ WSet wset_of(const qg_plan* h) {
   w.nseg = (int)h->segs.size();
   for (int i = 0; i < w.nseg; ++i) {
     const HostSeg& s = h->segs[i];
-    w.seg[i] = SegDev{s.codes, s.scales, s.bits, s.tiles, s.tile0};
+    w.seg[i] = SegDev{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq};
   }
   w.col_map = h->col_map;
   return w;
@@ -524,7 +526,9 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
     row_off[n] = acc;
     acc += (int64_t)h->col_bits[n] * K / 32;
   }
-  h->weight_bytes = acc * 4 + (int64_t)N * G * 2;
+  const int gs = d->group_size, sq = gs < QG_GROUP ? 1 : 0;
+  h->group_size = gs;
+  h->weight_bytes = acc * 4 + (int64_t)N * (K / gs) * 2;
   // widest codes first: their workgroups (the longest) are dispatched first,
   // so the tail of a launch is the lighter widths'
   int tile0 = 0;
@@ -535,6 +539,7 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
     if (cols.empty()) continue;
     HostSeg s;
     s.bits = b;
+    s.sq = sq;
     s.ncols = (int)cols.size();
     s.tiles = (s.ncols + 15) / 16;
     s.tile0 = tile0;
@@ -553,13 +558,13 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
     if (e != hipSuccess) break;
     const size_t nslot = (size_t)s.tiles * G4 * 64;
     if (hipMalloc(&s.codes, nslot * s.bits * 4 * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc(&s.scales, nslot * sizeof(uint16_t)) != hipSuccess) {
+        hipMalloc(&s.scales, nslot * (sq ? 4 : 1) * sizeof(uint16_t)) != hipSuccess) {
       hipStreamSynchronize(st);
       hipFree(d_off);
       return fail(QG_ERR_OOM, "device allocation for the weight layout failed");
     }
     e = launch_repack_uniform((const uint32_t*)d->codes, d_off, d->scales, h->col_map + 16 * s.tile0, s.bits, s.tiles,
-                              G, G4, s.codes, s.scales, st);
+                              G, G4, gs, s.codes, s.scales, st);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   hipFree(d_off);
@@ -686,8 +691,9 @@ qg_status run_xs(const qg_plan* h, const Work& w, const qg_plan* h2, const uint1
     a.tg_prefix[i] = p.tg_prefix[i];
   }
   const int bf = single_bits(h);
-  const hipError_t e = p.MT == 1 ? launch_gemm_xs1(a, p.T, dual, xsc, p.NQ, bf, p.NW, p.lds, p.grid, st)
-                                 : launch_gemm_xs2(a, p.T, dual, xsc, p.NQ, bf, p.NW, p.lds, p.grid, st);
+  const bool sq = h->group_size < QG_GROUP;
+  const hipError_t e = p.MT == 1 ? launch_gemm_xs1(a, p.T, dual, xsc, p.NQ, bf, sq, p.NW, p.lds, p.grid, st)
+                                 : launch_gemm_xs2(a, p.T, dual, xsc, p.NQ, bf, sq, p.NW, p.lds, p.grid, st);
   return after_launch(h, e, st);
 }
 
@@ -868,7 +874,8 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   if (!out) return fail(QG_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (!d) return fail(QG_ERR_INVALID_ARG, "desc is NULL");
-  if (d->group_size != QG_GROUP) return fail(QG_ERR_INVALID_ARG, "group_size must be 128 (got %d)", d->group_size);
+  if (d->group_size != QG_GROUP && !(d->format == QG_FMT_UNIFORM && (d->group_size == 64 || d->group_size == 32)))
+    return fail(QG_ERR_INVALID_ARG, "group_size must be 128 (uniform codes: 128, 64 or 32; got %d)", d->group_size);
   if (d->K <= 0 || d->K % QG_GROUP) return fail(QG_ERR_INVALID_ARG, "K = %d is not a positive multiple of 128", d->K);
   if (d->N <= 0 || d->N % 16) return fail(QG_ERR_INVALID_ARG, "N = %d is not a positive multiple of 16", d->N);
   if (max_M < 1 || max_M > QG_MAX_M) return fail(QG_ERR_INVALID_ARG, "max_M = %d is not in [1, 32]", max_M);
@@ -1011,6 +1018,7 @@ qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t*
     return fail(QG_ERR_UNSUPPORTED, "the fused MLP takes uniform-code handles");
   if (gate->K != up->K || gate->N != up->N) return fail(QG_ERR_INVALID_ARG, "gate and up shapes differ");
   if (gate->col_bits != up->col_bits) return fail(QG_ERR_INVALID_ARG, "gate and up need the same per-column widths");
+  if (gate->group_size != up->group_size) return fail(QG_ERR_INVALID_ARG, "gate and up need the same scale group size");
   if (down->K != gate->N) return fail(QG_ERR_INVALID_ARG, "down K (%d) != gate N (%d)", down->K, gate->N);
   if (M < 1 || M > gate->max_M || M > down->max_M) return fail(QG_ERR_INVALID_ARG, "M = %d out of range", M);
   if (!aligned16(x) || !aligned16(out)) return fail(QG_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
@@ -1067,11 +1075,11 @@ qg_status qgemv_run_prefill(qg_handle h, const uint16_t* x, int32_t M, uint16_t*
     const int n1 = std::min(h->N, n0 + nc);
     if (h->segs.size() == 1) {  // one width: column n is tile n / 16, lane n % 16
       const HostSeg& g = h->segs[0];
-      const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0};
+      const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0, g.sq};
       QG_HIP(launch_dequant_f16(sd, h->col_map, h->G, h->G4, h->K, n0 / 16, (n1 - n0) / 16, n0, n1, wbuf, st));
     } else {  // several widths (one chunk): every segment's columns land at their own rows
       for (const auto& g : h->segs) {
-        const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0};
+        const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0, g.sq};
         QG_HIP(launch_dequant_f16(sd, h->col_map, h->G, h->G4, h->K, 0, g.tiles, n0, n1, wbuf, st));
       }
     }
@@ -1102,7 +1110,7 @@ qg_status qgemv_debug_unpack(qg_handle h, int32_t* codes, void* stream) {
   if (!h || !codes) return fail(QG_ERR_INVALID_ARG, "NULL argument");
   if (h->format != QG_FMT_UNIFORM) return fail(QG_ERR_INVALID_ARG, "debug_unpack takes a uniform-code handle");
   for (const auto& s : h->segs) {
-    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0};
+    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq};
     QG_HIP(launch_debug_uniform(sd, h->col_map, h->G, h->G4, h->K, 0, codes, nullptr, nullptr, (hipStream_t)stream));
   }
   return QG_OK;
@@ -1117,7 +1125,7 @@ qg_status qgemv_debug_dequant(qg_handle h, float* w, uint16_t* q16, void* stream
     return QG_OK;
   }
   for (const auto& s : h->segs) {
-    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0};
+    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq};
     QG_HIP(launch_debug_uniform(sd, h->col_map, h->G, h->G4, h->K, 0, nullptr, w, q16, st));
   }
   return QG_OK;
@@ -1128,7 +1136,7 @@ qg_status qgemv_debug_operand(qg_handle h, int32_t* codes, uint16_t* b16, float*
   if (!h || (!codes && !b16 && !w)) return fail(QG_ERR_INVALID_ARG, "NULL argument");
   if (h->format != QG_FMT_UNIFORM) return fail(QG_ERR_INVALID_ARG, "debug_operand takes a uniform-code handle");
   for (const auto& s : h->segs) {
-    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0};
+    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq};
     QG_HIP(launch_debug_uniform(sd, h->col_map, h->G, h->G4, h->K, 1, codes, w, b16, (hipStream_t)stream));
   }
   return QG_OK;

@@ -143,12 +143,17 @@ typedef struct {
 typedef struct {
   int32_t K;                /* in-features; multiple of 128                                   */
   int32_t N;                /* out-features; multiple of 16                                   */
-  int32_t group_size;       /* must be 128                                                    */
+  int32_t group_size;       /* scale group: 128; UNIFORM also 64 or 32 (W4A16 g64 / g32 --
+                               "The Rock8", dormant-capabilities table: int4 weight-only
+                               at group 128, 64 and 32)                                       */
   int32_t format;           /* qg_format                                                      */
   int32_t bits;             /* UNIFORM: 2, 3 or 4 for every column, or 0 = per-column widths  */
   const uint8_t* col_bits;  /* host, N entries in {2,3,4}; read iff format UNIFORM and bits 0 */
   const void* codes;        /* device, canonical packed layout above; 16-byte aligned          */
-  const uint16_t* scales;   /* device, fp16 bits [N][K/128]; 16-byte aligned                   */
+  const uint16_t* scales;   /* device, fp16 bits [N][K/group_size]; 16-byte aligned. With
+                               groups of 64 or 32 the verify GEMM (2..32 rows) folds each
+                               scale into its fp16 operand, 2 (c - o) s rounded once, so
+                               scales beyond 4096 would overflow there                        */
   const uint16_t* codebook; /* device, fp16 bits [65536]; TRELLIS3 only                        */
   uint32_t flags;           /* QG_FLAG_*                                                       */
   uint32_t pins;            /* QG_PIN_*, 0 = built-in choices                                  */

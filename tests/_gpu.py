@@ -37,7 +37,7 @@ class Uniform:
     """A seeded uniform-code (or per-column width) matrix with its handle."""
 
     def __init__(self, N, K, bits=3, col_bits=None, cfg_id=50, tid=0, max_M=32, pins=0, launch=None,
-                 batch_invariant=False):
+                 batch_invariant=False, group_size=128):
         self.N, self.K = N, K
         self.bits = bits
         self.col_bits = col_bits
@@ -45,16 +45,17 @@ class Uniform:
             self.words = S.uniform_code_words(N, K, bits, cfg_id=cfg_id, tensor_id=S.T_CODES + 10 * tid)
         else:
             self.words = S.mixed_code_words(col_bits, K, cfg_id=cfg_id, tensor_id=S.T_CODES + 10 * tid)
-        self.scales = S.scales(N, K, cfg_id=cfg_id, tensor_id=S.T_SCALE + 10 * tid)
+        self.group_size = group_size
+        self.scales = S.scales(N, K, cfg_id=cfg_id, tensor_id=S.T_SCALE + 10 * tid, group=group_size)
         self.dw = dev_words(self.words)
         self.ds = dev_f16(self.scales)
         self.lin = Q.QLinear(self.dw, self.ds, K, N, bits=bits, col_bits=col_bits, max_M=max_M, pins=pins,
-                             launch=launch, batch_invariant=batch_invariant)
+                             launch=launch, batch_invariant=batch_invariant, group_size=group_size)
 
     def relinked(self, pins=0, launch=None, max_M=32, batch_invariant=False):
         """A second handle over the same device bytes, with other pins / launch overrides."""
         return Q.QLinear(self.dw, self.ds, self.K, self.N, bits=self.bits, col_bits=self.col_bits, max_M=max_M,
-                         pins=pins, launch=launch, batch_invariant=batch_invariant)
+                         pins=pins, launch=launch, batch_invariant=batch_invariant, group_size=self.group_size)
 
     def codes(self, rows=None):
         if self.col_bits is None:

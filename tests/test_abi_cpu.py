@@ -37,7 +37,8 @@ def _desc(**kw):
 
 
 @pytest.mark.parametrize("kw,frag", [
-    (dict(K=500), "K"), (dict(K=0), "K"), (dict(N=20), "N"), (dict(group_size=64), "group_size"),
+    (dict(K=500), "K"), (dict(K=0), "K"), (dict(N=20), "N"), (dict(group_size=16), "group_size"),
+    (dict(group_size=96), "group_size"), (dict(format=1, group_size=64), "group_size"),
     (dict(codes=0), "codes"), (dict(scales=0x200004), "aligned"), (dict(format=7), "format"),
     (dict(format=1, codebook=None), "codebook"),
 ])
