@@ -34,6 +34,13 @@ bit layout, so the conventions below are this library's, stated once here:
 * Rotation: normalised 128-point Walsh-Hadamard transform of x per 128-group,
   Sylvester (natural) order, H[i][j] = (-1)**popcount(i & j) / sqrt(128).
 * MLP: out = down(SiLU(gate(x)) * up(x)), SiLU(z) = z / (1 + exp(-z)).
+* MXFP4 ("The Rock8", format table, MXFP4 row: blocks of 32 elements in 17
+  bytes, OCP E2M1 leaves -- 2 exponent bits, 1 mantissa bit -- nibble-packed,
+  and one UE8M0 scale byte per block, value 2**(e - 127)): element codes in the
+  4-bit canonical stream above, scales uint8 [N][K/32];
+  w = e2m1(c) * 2**(e - 127).  E2M1 read as a binary float with exponent bias
+  1: sign bit 3, exponent bits 2..1, mantissa bit 0; exponent 0 is subnormal
+  (0.5 * m).  E8M0 = 255 is NaN.
 
 All floating point is fp64 and no intermediate is rounded.  Dequantised weights
 are exact (fp16 scale times a code offset has at most 15 significant bits), and
@@ -169,6 +176,46 @@ def rotate(x: np.ndarray) -> np.ndarray:
     H = hadamard128()
     xg = x.reshape(M, K // GROUP, GROUP)
     return np.einsum("ji,mgi->mgj", H, xg).reshape(M, K)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4: E2M1 elements, UE8M0 block scales (blocks of 32 along k)
+# ---------------------------------------------------------------------------
+MX_BLOCK = 32
+
+
+def e2m1_value(code: int) -> float:
+    """An E2M1 element: sign bit 3, two exponent bits (bias 1), one mantissa bit."""
+    code = int(code)
+    sign = -1.0 if (code >> 3) & 1 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    if e == 0:
+        return sign * 0.5 * m                      # subnormal: 2^(1-1) * (0 + m/2)
+    return sign * 2.0 ** (e - 1) * (1.0 + 0.5 * m)
+
+
+def e8m0_value(e: int) -> float:
+    """A UE8M0 scale byte: 2^(e - 127); 255 is NaN."""
+    e = int(e)
+    return float("nan") if e == 255 else 2.0 ** (e - 127)
+
+
+def dequant_mxfp4(codes: np.ndarray, e8: np.ndarray) -> np.ndarray:
+    """w[n][k] = e2m1(c[n][k]) * 2^(e8[n][k // 32] - 127) in fp64 (exact)."""
+    codes = np.asarray(codes, dtype=np.int64)
+    N, K = codes.shape
+    lut = np.array([e2m1_value(c) for c in range(16)])
+    sc = np.array([e8m0_value(e) for e in range(256)])
+    s = np.repeat(sc[np.asarray(e8, dtype=np.int64).reshape(N, K // MX_BLOCK)], MX_BLOCK, axis=1)
+    return lut[codes] * s
+
+
+def gemv_mxfp4(x, words, e8, N: int, K: int, rows=None) -> np.ndarray:
+    """y = x * dequant(W)^T for MXFP4 weights (optionally some output columns)."""
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    words = np.asarray(words, dtype=np.uint32).reshape(N, -1)
+    codes = unpack_uniform(words[rows].reshape(-1), len(rows), K, 4)
+    return matmul(x, dequant_mxfp4(codes, np.asarray(e8).reshape(N, -1)[rows]))
 
 
 # ---------------------------------------------------------------------------

@@ -45,6 +45,15 @@ def scales(N: int, K: int, *, seed: int = 0, cfg_id: int = 0, tensor_id: int = T
     return v.astype(np.float16)
 
 
+def mx_scales(N: int, K: int, *, seed: int = 0, cfg_id: int = 0, tensor_id: int = T_SCALE, lo: int = 116,
+              hi: int = 124) -> np.ndarray:
+    """UE8M0 block-scale bytes [N][K/32], uniform integers in [lo, hi]
+    (2^-11 .. 2^-3 by default: the magnitudes of LLM weight blocks)."""
+    assert K % 32 == 0 and 0 <= lo <= hi <= 255
+    r = _rng(seed, cfg_id, tensor_id)
+    return r.integers(lo, hi + 1, size=(N, K // 32)).astype(np.uint8)
+
+
 def code_words(n_words: int, *, seed: int = 0, cfg_id: int = 0, tensor_id: int = T_CODES) -> np.ndarray:
     """``n_words`` uniformly random uint32 words (canonical packed code stream)."""
     r = _rng(seed, cfg_id, tensor_id)

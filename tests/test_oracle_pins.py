@@ -222,6 +222,60 @@ def test_small_scale_groups_brute_force(gs):
 
 
 # ---------------------------------------------------------------------------
+# MXFP4 ("The Rock8", format table: E2M1 leaves, 2 exponent / 1 mantissa bit,
+# UE8M0 scale 2^(e-127) per 32 elements, 17 bytes per block)
+# ---------------------------------------------------------------------------
+def test_e2m1_values():
+    vals = [O.e2m1_value(c) for c in range(16)]
+    # eight magnitudes: 0 and 1/2 (exponent 0), then 1, 1.5, 2, 3, 4, 6
+    assert vals[:8] == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(8):
+        assert vals[c | 8] == -vals[c]  # the sign bit only negates (-0 for code 8)
+    assert math.copysign(1.0, vals[8]) == -1.0
+    # a binary float: each exponent step doubles, each mantissa step adds half the
+    # exponent's unit, the subnormal step equals the first normal's unit
+    for e in (1, 2):
+        assert vals[2 * e + 2] == 2 * vals[2 * e]
+    assert vals[1] == vals[3] - vals[2]
+    # 2 exponent bits and 1 mantissa bit leave 4 bits per element: 32 elements in
+    # 16 bytes plus the scale byte = the format's 17-byte block
+    assert 32 * 4 // 8 + 1 == 17
+
+
+def test_e8m0_values():
+    assert O.e8m0_value(127) == 1.0 and O.e8m0_value(128) == 2.0 and O.e8m0_value(126) == 0.5
+    assert O.e8m0_value(0) == 2.0 ** -127 and O.e8m0_value(254) == 2.0 ** 127
+    assert math.isnan(O.e8m0_value(255))
+
+
+def test_mxfp4_dequant_blocks_and_brute_force():
+    """Each scale byte covers exactly 32 consecutive k of its row; products
+    against exact rationals."""
+    N, K, M = 3, 256, 2
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, size=(N, K))
+    e8 = rng.integers(120, 130, size=(N, K // 32)).astype(np.uint8)
+    w = O.dequant_mxfp4(codes, e8)
+    base = O.dequant_mxfp4(codes, np.full_like(e8, 127))
+    for n0, i in ((0, 0), (2, 7), (1, 3)):
+        e2 = np.full_like(e8, 127)
+        e2[n0, i] = 128
+        changed = np.argwhere(O.dequant_mxfp4(codes, e2) != base)
+        nz = [k for k in range(i * 32, (i + 1) * 32) if codes[n0, k] & 7]
+        assert sorted(changed[:, 1]) == nz and set(changed[:, 0]) <= {n0}
+    words = O.pack_uniform(codes, 4)
+    x = S.activations(M, K, cfg_id=99)
+    y = O.gemv_mxfp4(x, words, e8, N, K)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(x[m, k])) * Fraction(O.e2m1_value(codes[n, k])) * Fraction(2) ** (int(e8[n, k // 32]) - 127)
+            assert abs(y[m, n] - float(acc)) <= 1e-12 * max(1.0, abs(float(acc)))
+    assert np.all(w == base * np.repeat(2.0 ** (e8.astype(np.float64) - 127), 32, axis=1))
+
+
+# ---------------------------------------------------------------------------
 # contraction: brute force with exact rationals
 # ---------------------------------------------------------------------------
 def brute_gemv(x16, words, s16, N, K, bits):
