@@ -16,6 +16,13 @@ hipError_t launch_repack_uniform(const uint32_t* canon, const int64_t* row_off, 
   return hipGetLastError();
 }
 
+hipError_t launch_repack_mx_scales(const uint8_t* e8, const int32_t* cols, int tiles, int G, int G4, uint16_t* dscales,
+                                   hipStream_t st) {
+  const size_t nslot = (size_t)tiles * G4 * 64;
+  k_repack_mx_scales<<<(unsigned)((nslot + 255) / 256), 256, 0, st>>>(e8, cols, tiles, G, G4, dscales);
+  return hipGetLastError();
+}
+
 hipError_t launch_debug_uniform(const SegDev& sg, const int32_t* col_map, int G, int G4, int K, int mode,
                                 int32_t* codes, float* w, uint16_t* q16, hipStream_t st) {
   const int64_t n = (int64_t)sg.tiles * G * 64;

@@ -19,6 +19,10 @@ void l(const XsArgs& a, int NW, size_t lds, unsigned grid, hipStream_t st) {
 // per-quarter scales (SQ) are compiled for the width-generic body only
 template <int MT, int T, bool DUAL, int NQ, bool XSC>
 void l_b(const XsArgs& a, int bf, bool sq, int NW, size_t lds, unsigned grid, hipStream_t st) {
+  if (bf == 5) {  // MXFP4: one matrix, fp16 x
+    if constexpr (!DUAL && !XSC) l<MT, T, DUAL, 5, NQ, XSC, false>(a, NW, lds, grid, st);
+    return;
+  }
   if (sq) {
     l<MT, T, DUAL, 0, NQ, XSC, true>(a, NW, lds, grid, st);
     return;
@@ -85,7 +89,8 @@ template <int MT>
 hipError_t allow() {
   hipError_t e = hipSuccess;
   const hipError_t r[] = {allow_b<MT, 0, false>(), allow_b<MT, 2, false>(), allow_b<MT, 3, false>(),
-                          allow_b<MT, 4, false>(), allow_b<MT, 0, true>()};
+                          allow_b<MT, 4, false>(), allow_b<MT, 0, true>(), allow_one<MT, 1, false, 5, false, false>(),
+                          allow_one<MT, 2, false, 5, false, false>()};
   for (hipError_t x : r)
     if (x != hipSuccess) e = x;
   return e;

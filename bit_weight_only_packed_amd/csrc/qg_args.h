@@ -18,6 +18,8 @@ struct SegDev {
   int tile0;               // index of the first tile in the handle's padded column space
   int sq;                  // scale group 64 or 32: one scale per lane quarter (32 weights) and
                            // group of 128 instead of one per column and group (qg_common.h)
+  int mx;                  // MXFP4: 4-bit fields are E2M1 elements; the per-quarter scale
+                           // entries hold E8M0 bytes (own exponent | group maximum << 8)
 };
 
 struct WSet {

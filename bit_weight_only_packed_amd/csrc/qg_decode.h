@@ -214,6 +214,32 @@ __device__ __forceinline__ void decode_group_scaled(const uint32_t (&w)[4 * B], 
   for (int i = 0; i < 16; ++i) r[i] = __builtin_bit_cast(uint32_t, (as_h2(r[i] | kExp) + off) * sc);
 }
 
+// MXFP4 elements in the 4-bit layout: each E2M1 nibble (sign, two exponent
+// bits, one mantissa bit) of a pair becomes the fp16 with the sign at bit 15
+// and the three magnitude bits at bits 11..9 -- exponent field e, mantissa m/2,
+// and e = 0 the subnormal m 2^-15 -- which is exactly the element times 2^-14
+__device__ __forceinline__ void decode_group_mx(const uint32_t (&w)[16], int gi, uint32_t (&r)[16]) {
+  uint32_t g[4];
+  quad_group<4>(w, gi, g);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t v = g[i >> 2];
+    const int o = 4 * (i & 3);  // the pair's nibbles sit at bits o and 16 + o
+    const uint32_t mag = (o <= 9 ? v << (9 - o) : v >> (o - 9)) & 0x0E000E00u;
+    r[i] = mag | ((v << (12 - o)) & 0x80008000u);
+  }
+}
+
+// fp32 2^(e - 127) of an E8M0 byte (e = 0: 2^-127; 255: NaN), times 2^k
+// (|k| small; the result clamps to the fp32 range ends)
+__device__ __forceinline__ float e8m0_scale(uint32_t e, int k) {
+  if (e == 255u) return __builtin_nanf("");
+  const int f = (int)e + k;  // biased fp32 exponent of 2^(e - 127 + k)
+  if (f >= 255) return __builtin_bit_cast(float, 0x7F000000u);                // 2^127
+  if (f >= 1) return __builtin_bit_cast(float, (uint32_t)f << 23);
+  return f >= -22 ? __builtin_bit_cast(float, 0x00400000u >> (-f)) : 0.0f;   // subnormal
+}
+
 template <int B>
 __device__ __forceinline__ void decode_group_classes(const uint32_t (&w)[4 * B], int gi, uint32_t (&r)[16]) {
   uint32_t g[B];

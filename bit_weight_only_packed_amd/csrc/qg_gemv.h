@@ -25,7 +25,10 @@ namespace qg {
 // one wave's quads: returns this lane's partial (column j = lane & 15, quarter
 // lane >> 4) over them, scaled back to true units (times 2^24 for the
 // reduction's convention: the caller multiplies nothing more)
-template <int B, int NQ, bool XF>
+// MX: MXFP4 elements (B = 4 layout): decoded to fp16 values of their own
+// (times 2^-14), x staged with its block exponent only, no offset term, and
+// each group's E8M0 scale applied as an exact fp32 power of two.
+template <int B, int NQ, bool XF, bool MX = false>
 __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, int tile, int qw0, int q_end,
                                              char* wsm) {
   // several widths inline one body per width behind a branch: keep the
@@ -74,10 +77,40 @@ __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, 
   // ---- the wave's activations -> its LDS region
   uint4* xl = reinterpret_cast<uint4*>(wsm);
   float* xq = reinterpret_cast<float*>(wsm + (size_t)NQ * 1024);
-  const int e = stage_wave<B, XF, NQ>(xv, xl, xq, lane, nvalid);
-  // ---- compute
   const int q = lane >> 4;
   float R = 0.0f;
+  if constexpr (MX) {
+    static_assert(B == 4 && !XF, "MXFP4 takes fp16 x and the 4-bit layout");
+    const int e = stage_wave_plain<NQ>(xv, xl, lane, nvalid);
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int gl = 4 * u + gi;
+        if (gl >= ngw) break;
+        uint32_t xp[16];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 u4 = xl[gl * 16 + q * 4 + v];
+          xp[4 * v + 0] = u4.x; xp[4 * v + 1] = u4.y; xp[4 * v + 2] = u4.z; xp[4 * v + 3] = u4.w;
+        }
+        uint32_t r[16];
+        decode_group_mx(cw[u], gi, r);
+        float e0 = 0.0f, e1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          e0 = dot2(r[i], xp[i], e0);
+          e1 = dot2(r[i + 1], xp[i + 1], e1);
+        }
+        const uint32_t sw = (gi < 2) ? sc[u].x : sc[u].y;
+        const uint32_t eq = ((gi & 1) ? (sw >> 16) : sw) & 0xFFu;  // the lane's block exponent byte
+        R = __builtin_fmaf(e8m0_scale(eq, 0), e0 + e1, R);
+      }
+    }
+    return R * pow2f(14 - e);  // the products carry 2^(e - 14)
+  }
+  const int e = stage_wave<B, XF, NQ>(xv, xl, xq, lane, nvalid);
+  // ---- compute
 #pragma unroll
   for (int u = 0; u < NQ; ++u) {
 #pragma unroll
@@ -150,7 +183,8 @@ __device__ __forceinline__ void gemv_q_block(const GvArgs& a, int bid, char* sme
   const int qw0 = q_beg + wave * NQ;
   float R;
   const int bits = sd.bits;
-  if (BF == 2 || (BF == 0 && bits == 2)) R = gemv_q_wave<2, NQ, XF>(a, sd, tile, qw0, q_end, wsm);
+  if constexpr (BF == 5) R = gemv_q_wave<4, NQ, XF, true>(a, sd, tile, qw0, q_end, wsm);  // MXFP4
+  else if (BF == 2 || (BF == 0 && bits == 2)) R = gemv_q_wave<2, NQ, XF>(a, sd, tile, qw0, q_end, wsm);
   else if (BF == 3 || (BF == 0 && bits == 3)) R = gemv_q_wave<3, NQ, XF>(a, sd, tile, qw0, q_end, wsm);
   else R = gemv_q_wave<4, NQ, XF>(a, sd, tile, qw0, q_end, wsm);
   {

@@ -39,6 +39,9 @@ hipError_t launch_debug_trellis(const uint32_t* codes, const uint16_t* scales, c
 hipError_t launch_repack_uniform(const uint32_t* canon, const int64_t* row_off, const uint16_t* scales,
                                  const int32_t* cols, int bits, int tiles, int G, int G4, int gs, uint32_t* dcodes,
                                  uint16_t* dscales, hipStream_t st);
+// MXFP4 exponent bytes [N][K/32] -> the per-quarter scale entries (own | group max << 8)
+hipError_t launch_repack_mx_scales(const uint8_t* e8, const int32_t* cols, int tiles, int G, int G4, uint16_t* dscales,
+                                   hipStream_t st);
 // mode 0: the GEMV class decode; mode 1: the verify GEMM's operand decode
 hipError_t launch_debug_uniform(const SegDev& sg, const int32_t* col_map, int G, int G4, int K, int mode,
                                 int32_t* codes, float* w, uint16_t* q16, hipStream_t st);

@@ -58,13 +58,37 @@ __global__ void k_repack_uniform(const uint32_t* __restrict__ canon, const int64
   for (int p = 0; p < bits; ++p)
     dst[((size_t)tq * bits + p) * 64 + lane] = make_uint4(out[4 * p], out[4 * p + 1], out[4 * p + 2], out[4 * p + 3]);
   const int sq = gs < 128;
-  if (sq || q == 0) {
+  if (dscales && (sq || q == 0)) {  // (MXFP4 scales are laid out by k_repack_mx_scales)
     const int gpr = G * (128 / gs);  // scales per row
     for (int gi = 0; gi < 4; ++gi) {
       const int g = 4 * qu + gi;
       const int sg = (g * 128 + 32 * q) / gs;  // the scale group of this lane's 32 weights
       dscales[scale_index(t, G4, g, j, q, sq)] = (n >= 0 && g < G) ? scales_in[(int64_t)n * gpr + sg] : (uint16_t)0;
     }
+  }
+}
+
+// MXFP4 scales: E8M0 bytes [N][K/32] -> the per-quarter layout, each entry the
+// block's own exponent byte | the largest of its 128-group's four << 8.  One
+// thread per (tile, quad, lane); padding (columns or groups) gets 0.
+__global__ void k_repack_mx_scales(const uint8_t* __restrict__ e8, const int32_t* __restrict__ cols, int tiles, int G,
+                                   int G4, uint16_t* __restrict__ dscales) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)tiles * G4 * 64) return;
+  const int lane = (int)(gid & 63);
+  const int64_t tq = gid >> 6;
+  const int qu = (int)(tq % G4), t = (int)(tq / G4);
+  const int j = lane & 15, q = lane >> 4;
+  const int n = cols[16 * t + j];
+  for (int gi = 0; gi < 4; ++gi) {
+    const int g = 4 * qu + gi;
+    uint16_t v = 0;
+    if (n >= 0 && g < G) {
+      const uint8_t* b = e8 + (int64_t)n * (4 * G) + 4 * g;
+      const uint32_t mx = max(max(b[0], b[1]), max(b[2], b[3]));
+      v = (uint16_t)(b[q] | (mx << 8));
+    }
+    dscales[scale_index(t, G4, g, j, q, 1)] = v;
   }
 }
 
@@ -101,6 +125,37 @@ __device__ __forceinline__ void debug_slot(const SegDev& sg, const int32_t* col_
   debug_quad<B>(sg, G4, tl, g, lane, cw);
   uint32_t r[16], rs[16];
   const uint16_t s16 = sg.scales[scale_index(tl, G4, g, j, q, sg.sq)];
+  if constexpr (B == 4) {
+    if (sg.mx) {
+      // MXFP4.  MODE 0: the GEMVs' element decode -- codes (the nibbles), w
+      // exact in fp32 (element * 2^(e - 127)) and q16 the element's fp16 value.
+      // MODE 1: the verify GEMM's operand -- its fp16 bits (element * 2^-14 *
+      // 2^-(e_max - e), rounded once) and w = operand * 2^(e_max - 113).
+      decode_group_mx(cw, g & 3, r);
+      const uint32_t eq = s16 & 0xFFu, emax = (uint32_t)s16 >> 8, de = emax - eq;
+      const uint32_t f = de <= 14u ? (15u - de) << 10 : (de <= 24u ? 1u << (24u - de) : 0u);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t op2 = MODE == 1 ? pk_mul_f16(r[i], f | (f << 16)) : r[i];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = g * 128 + 32 * q + 2 * i + h;
+          const int64_t at = (int64_t)n * K + k;
+          const uint32_t nib = (cw[(g & 3) * 4 + (i >> 2)] >> (16 * h + 4 * (i & 3))) & 15u;
+          if (codes) codes[at] = (int32_t)nib;
+          const uint16_t el = (uint16_t)(op2 >> (16 * h));
+          if constexpr (MODE == 0) {
+            if (q16) q16[at] = f2h(h2f(el) * 16384.0f);            // the element (exact)
+            if (w) w[at] = h2f(el) * 16384.0f * e8m0_scale(eq, 0);  // exact in fp32
+          } else {
+            if (q16) q16[at] = el;
+            if (w) w[at] = h2f(el) * e8m0_scale(emax, 14);
+          }
+        }
+      }
+      return;
+    }
+  }
   if constexpr (MODE == 0) decode_group_classes<B>(cw, g & 3, r);
   else decode_group_off1<B>(cw, g & 3, r);
   if (MODE == 1 && sg.sq) decode_group_scaled<B>(cw, g & 3, (uint32_t)s16 | ((uint32_t)s16 << 16), rs);

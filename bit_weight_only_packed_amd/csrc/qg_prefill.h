@@ -27,6 +27,28 @@ __device__ __forceinline__ void dq_quad(const SegDev& sg, const int32_t* col_map
     cw[4 * p] = v.x; cw[4 * p + 1] = v.y; cw[4 * p + 2] = v.z; cw[4 * p + 3] = v.w;
   }
   const uint2 sw = *reinterpret_cast<const uint2*>(sg.scales + scale_index(tl, G4, 4 * qu, j, q, sg.sq));
+  if constexpr (B == 4) {
+    if (sg.mx) {  // MXFP4: element * 2^(e - 127), rounded once to fp16
+      uint16_t* row = out + (size_t)(n - n0) * K + 32 * q;
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int g = 4 * qu + gi;
+        if (g >= G) break;
+        uint32_t r[16];
+        decode_group_mx(cw, gi, r);
+        const uint32_t s2 = gi < 2 ? sw.x : sw.y;
+        const float s = e8m0_scale(((gi & 1) ? (s2 >> 16) : s2) & 0xFFu, 14);  // also undoes the 2^-14
+        uint32_t h[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          h[i] = (uint32_t)f2h(h2f((uint16_t)r[i]) * s) | ((uint32_t)f2h(h2f((uint16_t)(r[i] >> 16)) * s) << 16);
+        uint4* dst = reinterpret_cast<uint4*>(row + (size_t)g * 128);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dst[v] = make_uint4(h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]);
+      }
+      return;
+    }
+  }
   const float o = 0.5f * (float)((1 << B) - 1);
   uint16_t* row = out + (size_t)(n - n0) * K + 32 * q;
 #pragma unroll

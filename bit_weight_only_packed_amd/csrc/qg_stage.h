@@ -167,4 +167,29 @@ __device__ __forceinline__ int stage_wave(const uint4 (&v)[NU][XIn<XF>::W], uint
   return e;
 }
 
+// MXFP4 staging: the wave's activations times 2^e (the block exponent) into
+// its LDS region, no class factors (the decoded elements are fp16 values of
+// their own) and no quarter sums (E2M1 has no code offset).  Returns e.
+template <int NU>
+__device__ __forceinline__ int stage_wave_plain(const uint4 (&v)[NU][1], uint4* xl, int lane, int nu) {
+  uint32_t mx = 0;
+#pragma unroll
+  for (int r = 0; r < NU; ++r) {
+    if (r >= nu) break;
+    mx = max(mx, maxbits8<false>(v[r]));
+  }
+  const int e = block_exp<false>(wave_max(mx));
+  const uint32_t f = (uint32_t)(15 + e) * 0x04000400u;  // fp16x2 (2^e, 2^e), e in -2..15
+#pragma unroll
+  for (int r = 0; r < NU; ++r) {
+    if (r >= nu) break;
+    xl[lane + 64 * r] = make_uint4(pk_mul_f16(v[r][0].x, f), pk_mul_f16(v[r][0].y, f), pk_mul_f16(v[r][0].z, f),
+                                   pk_mul_f16(v[r][0].w, f));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  return e;
+}
+
 }  // namespace qg

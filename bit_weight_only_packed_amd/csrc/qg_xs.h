@@ -28,6 +28,12 @@
 // s rounded once to fp16); the chains then need no offset term and no group
 // sums, run on across groups, and yield 2 y.
 //
+// MXFP4 (MX): the elements decode to fp16 values of their own (times 2^-14);
+// the four lane quarters of a group carry E8M0 exponents of their own, so each
+// quarter's operand is multiplied by 2^-(e_max - e) (exact while it stays in
+// fp16's range, else rounded once) and the group's chain by 2^(e_max - 113),
+// e_max the largest of the four (kept beside each exponent at create).
+//
 // K slices meet in one of two ways, both independent of the order of arrival.
 // Few outputs: in fixed-point words (see fx_word), one integer atomic per
 // output and slice, whose returned count tells the last slice to store the
@@ -76,7 +82,7 @@ __device__ __forceinline__ void xs_load(XsUnit<B, T, ND>& c, const SegDev (&sd)[
 
 // one unit: groups gl0 .. gl0 + ngr - 1 of the slice against the unit's tiles;
 // xa[mt][v]: this lane's A-fragment address of group 0 (add 256 per group)
-template <int B, int T, int MT, int ND, bool XSC, bool SQ>
+template <int B, int T, int MT, int ND, bool XSC, bool SQ, bool MX>
 __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* const (&xa)[MT][4], const float* xsum,
                                         const float* xfac, int gl0, int ngr, int lane, f4_t (&R)[ND][T][MT]) {
   const int kq = lane >> 4;
@@ -94,6 +100,30 @@ __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* c
       // chain start: rows 16 mt + 4 kq + e (sums past M are never stored either)
       if constexpr (!SQ) C0[mt] = *reinterpret_cast<const f4_t*>(xsum + gl * (16 * MT) + 16 * mt + 4 * kq) * ko;
       if constexpr (XSC) F[mt] = *reinterpret_cast<const f4_t*>(xfac + gl * (16 * MT) + 16 * mt + 4 * kq);
+    }
+    if constexpr (MX) {
+      static_assert(B == 4 && ND == 1 && !XSC, "MXFP4: one matrix, fp16 x");
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t sw = (gi < 2) ? c.sc[0][t].x : c.sc[0][t].y;
+        const uint32_t ent = ((gi & 1) ? (sw >> 16) : sw) & 0xFFFFu;
+        const uint32_t eq = ent & 0xFFu, emax = ent >> 8, de = emax - eq;
+        const uint32_t f = de <= 14u ? (15u - de) << 10 : (de <= 24u ? 1u << (24u - de) : 0u);  // fp16 2^-de
+        uint32_t r[16];
+        decode_group_mx(c.cw[0][t], gi, r);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) r[i] = pk_mul_f16(r[i], f | (f << 16));
+        const float s = e8m0_scale(emax, 14);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f4_t cc = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) cc = mfma16(A[mt][v], as_h8(r[4 * v], r[4 * v + 1], r[4 * v + 2], r[4 * v + 3]), cc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R[0][t][mt][e] = __builtin_fmaf(s, cc[e], R[0][t][mt][e]);
+        }
+      }
+      continue;
     }
     if constexpr (SQ) {
 #pragma unroll
@@ -141,10 +171,10 @@ __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* c
   }
 }
 
-template <int B, int T, int MT, int ND, int NQ, bool XSC, bool SQ>
+template <int B, int T, int MT, int ND, int NQ, bool XSC, bool SQ, bool MX = false>
 __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], int s, int q0, int nq, int tgb, int tge,
                                         int tgbase, char* smem) {
-  constexpr float kOut = SQ ? 0.5f : 8388608.0f;  // the chains' unit: 2 y (SQ) or 2^-23 y
+  constexpr float kOut = MX ? 1.0f : (SQ ? 0.5f : 8388608.0f);  // the chains' unit: y, 2 y (SQ) or 2^-23 y
   const int lane = threadIdx.x & 63;
   const int NW = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -274,7 +304,7 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
   // it the wait for that unit's codes)
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    if (i < nq) xs_unit<B, T, MT, ND, XSC, SQ>(c[i % XS_PD], xa, xsum, xfac, 4 * i, min(4, G - 4 * (q0 + i)), lane, R);
+    if (i < nq) xs_unit<B, T, MT, ND, XSC, SQ, MX>(c[i % XS_PD], xa, xsum, xfac, 4 * i, min(4, G - 4 * (q0 + i)), lane, R);
     __builtin_amdgcn_sched_barrier(0);
     if (i + XS_PD < NQ) xs_load<B, T, ND, SQ>(c[i % XS_PD], sd, tg, q0 + i + XS_PD, i + XS_PD < nq, G4, (uint32_t)lane);
     __builtin_amdgcn_sched_barrier(0);
@@ -476,7 +506,9 @@ __global__ __launch_bounds__(512) void k_gemm_xs(XsArgs a) {
   const int tgb = (pw - a.wg_prefix[si]) * a.GPW, tge = min(tgb + a.GPW, ngr);
   const int q0 = (int)((int64_t)s * G4 / S), q1 = (int)((int64_t)(s + 1) * G4 / S);
   const int bits = sd[0].bits;
-  if (BF == 2 || (BF == 0 && bits == 2))
+  if constexpr (BF == 5) {  // MXFP4 (per-quarter scale entries, the 4-bit layout)
+    if constexpr (!DUAL && !XSC) xs_body<4, T, MT, ND, NQ, XSC, true, true>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
+  } else if (BF == 2 || (BF == 0 && bits == 2))
     xs_body<2, T, MT, ND, NQ, XSC, SQ>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
   else if (BF == 3 || (BF == 0 && bits == 3))
     xs_body<3, T, MT, ND, NQ, XSC, SQ>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);

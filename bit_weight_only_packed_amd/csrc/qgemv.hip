@@ -61,6 +61,7 @@ struct Work {
 struct HostSeg {
   int bits, tiles, tile0, ncols;
   int sq = 0;  // scale group 64 or 32 (per-lane-quarter scale layout)
+  int mx = 0;  // MXFP4 elements
   uint32_t* codes = nullptr;
   uint16_t* scales = nullptr;
 };
@@ -116,13 +117,19 @@ WSet wset_of(const qg_plan* h) {
   w.nseg = (int)h->segs.size();
   for (int i = 0; i < w.nseg; ++i) {
     const HostSeg& s = h->segs[i];
-    w.seg[i] = SegDev{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq};
+    w.seg[i] = SegDev{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq, s.mx};
   }
   w.col_map = h->col_map;
   return w;
 }
 
-int single_bits(const qg_plan* h) { return h->segs.size() == 1 ? h->segs[0].bits : 0; }
+// the kernels' width argument: the single code width, 0 for several, 5 for MXFP4
+int single_bits(const qg_plan* h) {
+  if (h->format == QG_FMT_MXFP4) return 5;
+  return h->segs.size() == 1 ? h->segs[0].bits : 0;
+}
+// uniform codes and MXFP4 share the code layout and the GEMV / verify GEMM
+bool coded(const qg_plan* h) { return h->format == QG_FMT_UNIFORM || h->format == QG_FMT_MXFP4; }
 
 // ---- M = 1 plans -------------------------------------------------------------
 // quads-per-wave counts the per-group GEMV is compiled for
@@ -182,7 +189,7 @@ bool sk_fits(const qg_plan* h) { return h->G4 <= 63 * SK_UPW; }
 // M = 1 kernel choice, measured on the decode shapes: the per-group kernel
 // from 256 tiles up, the per-tile-run kernel for narrower matrices.
 bool use_sk(const qg_plan* h) {
-  if (!sk_fits(h)) return false;
+  if (!sk_fits(h) || h->format == QG_FMT_MXFP4) return false;  // MXFP4: the per-group GEMV only
   if (h->pins & QG_PIN_M1_PERGROUP) return false;
   if (h->pins & QG_PIN_M1_RUNS) return true;
   return h->total_tiles < 256;
@@ -507,7 +514,10 @@ qg_status run_trellis(const qg_plan* h, const Work& w, const uint16_t* x, int M,
 qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   const int N = d->N, K = d->K, G = K / QG_GROUP, G4 = (G + 3) / 4;
   h->col_bits.resize(N);
-  if (d->bits == 0) {
+  const bool mx = d->format == QG_FMT_MXFP4;
+  if (mx) {
+    std::fill(h->col_bits.begin(), h->col_bits.end(), (uint8_t)4);  // E2M1 elements in 4-bit fields
+  } else if (d->bits == 0) {
     if (!d->col_bits) return fail(QG_ERR_INVALID_ARG, "bits == 0 needs col_bits (host, N entries)");
     for (int n = 0; n < N; ++n) {
       const int b = d->col_bits[n];
@@ -528,7 +538,7 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   }
   const int gs = d->group_size, sq = gs < QG_GROUP ? 1 : 0;
   h->group_size = gs;
-  h->weight_bytes = acc * 4 + (int64_t)N * (K / gs) * 2;
+  h->weight_bytes = acc * 4 + (int64_t)N * (K / gs) * (mx ? 1 : 2);  // MXFP4: one exponent byte per block
   // widest codes first: their workgroups (the longest) are dispatched first,
   // so the tail of a launch is the lighter widths'
   int tile0 = 0;
@@ -540,6 +550,7 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
     HostSeg s;
     s.bits = b;
     s.sq = sq;
+    s.mx = mx ? 1 : 0;
     s.ncols = (int)cols.size();
     s.tiles = (s.ncols + 15) / 16;
     s.tile0 = tile0;
@@ -564,7 +575,10 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
       return fail(QG_ERR_OOM, "device allocation for the weight layout failed");
     }
     e = launch_repack_uniform((const uint32_t*)d->codes, d_off, d->scales, h->col_map + 16 * s.tile0, s.bits, s.tiles,
-                              G, G4, gs, s.codes, s.scales, st);
+                              G, G4, gs, s.codes, mx ? nullptr : s.scales, st);
+    if (e == hipSuccess && mx)
+      e = launch_repack_mx_scales(reinterpret_cast<const uint8_t*>(d->scales), h->col_map + 16 * s.tile0, s.tiles, G,
+                                  G4, s.scales, st);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   hipFree(d_off);
@@ -874,19 +888,24 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   if (!out) return fail(QG_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (!d) return fail(QG_ERR_INVALID_ARG, "desc is NULL");
-  if (d->group_size != QG_GROUP && !(d->format == QG_FMT_UNIFORM && (d->group_size == 64 || d->group_size == 32)))
+  if (d->format == QG_FMT_MXFP4) {
+    if (d->group_size != 32) return fail(QG_ERR_INVALID_ARG, "MXFP4: group_size must be 32 (got %d)", d->group_size);
+    if (d->bits != 0 && d->bits != 4) return fail(QG_ERR_INVALID_ARG, "MXFP4: bits must be 0 or 4 (got %d)", d->bits);
+  } else if (d->group_size != QG_GROUP &&
+             !(d->format == QG_FMT_UNIFORM && (d->group_size == 64 || d->group_size == 32))) {
     return fail(QG_ERR_INVALID_ARG, "group_size must be 128 (uniform codes: 128, 64 or 32; got %d)", d->group_size);
+  }
   if (d->K <= 0 || d->K % QG_GROUP) return fail(QG_ERR_INVALID_ARG, "K = %d is not a positive multiple of 128", d->K);
   if (d->N <= 0 || d->N % 16) return fail(QG_ERR_INVALID_ARG, "N = %d is not a positive multiple of 16", d->N);
   if (max_M < 1 || max_M > QG_MAX_M) return fail(QG_ERR_INVALID_ARG, "max_M = %d is not in [1, 32]", max_M);
   if (!d->codes || !d->scales) return fail(QG_ERR_INVALID_ARG, "codes and scales must be device pointers");
   if (!aligned16(d->codes) || !aligned16(d->scales)) return fail(QG_ERR_INVALID_ARG, "codes/scales must be 16-byte aligned");
-  if (d->format != QG_FMT_UNIFORM && d->format != QG_FMT_TRELLIS3)
+  if (d->format != QG_FMT_UNIFORM && d->format != QG_FMT_TRELLIS3 && d->format != QG_FMT_MXFP4)
     return fail(QG_ERR_INVALID_ARG, "unknown format %d", d->format);
   if (d->format == QG_FMT_TRELLIS3) {
     if (!d->codebook || !aligned16(d->codebook)) return fail(QG_ERR_INVALID_ARG, "trellis needs a 16-byte aligned codebook");
   }
-  if ((d->flags & QG_FLAG_BATCH_INVARIANT) && d->format != QG_FMT_UNIFORM)
+  if ((d->flags & QG_FLAG_BATCH_INVARIANT) && d->format == QG_FMT_TRELLIS3)
     return fail(QG_ERR_UNSUPPORTED, "batch-invariant rows are built for uniform-code handles only");
   if ((d->pins & QG_PIN_M1_PERGROUP) && (d->pins & QG_PIN_M1_RUNS))
     return fail(QG_ERR_INVALID_ARG, "pins: one M = 1 kernel at a time");
@@ -921,7 +940,7 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
     return fail(QG_ERR_DEVICE, "cannot query the compute-unit count");
   }
   hipStream_t st = (hipStream_t)stream;
-  s = d->format == QG_FMT_UNIFORM ? create_uniform(h, d, st) : create_trellis(h, d, st);
+  s = d->format == QG_FMT_TRELLIS3 ? create_trellis(h, d, st) : create_uniform(h, d, st);
   if (s == QG_OK) {
     const int nc = std::max(1, h->total_tiles);
     h->ws.ncounters = (size_t)nc;
@@ -929,7 +948,7 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
     else if (hipMemsetAsync(h->ws.counters, 0, nc * sizeof(int), st) != hipSuccess)
       s = fail(QG_ERR_DEVICE, "counter initialisation failed");
   }
-  if (s == QG_OK && h->format == QG_FMT_UNIFORM) {
+  if (s == QG_OK && coded(h)) {
     if (m1_allow_lds() != hipSuccess || xs1_allow_lds() != hipSuccess || xs2_allow_lds() != hipSuccess)
       s = fail(QG_ERR_DEVICE, "cannot raise the LDS limit of the kernels");
   }
@@ -1000,6 +1019,7 @@ qg_status qgemv_run_batch(int32_t n, const qg_handle* hs, const uint16_t* const*
     for (int k = 0; k < i; ++k)
       if (hs[k] == hs[i]) return fail(QG_ERR_INVALID_ARG, "entries %d and %d share a handle (and its workspace)", k, i);
     if (hs[i]->format != QG_FMT_UNIFORM || hs[i]->device != hs[0]->device || invariant(hs[i])) one_launch = false;
+    // (MXFP4 and trellis handles run entry by entry)
   }
   hipStream_t st = (hipStream_t)stream;
   if (one_launch) return run_batch_m1(n, hs, xs, ys, st);
@@ -1045,7 +1065,7 @@ constexpr size_t kPrefillGemmWs = (size_t)32 << 20;  // hipBLASLt workspace at t
 qg_status qgemv_prefill_workspace(qg_handle h, size_t* min_bytes, size_t* full_bytes) {
   g_err.clear();
   if (!h || !min_bytes || !full_bytes) return fail(QG_ERR_INVALID_ARG, "NULL argument");
-  if (h->format != QG_FMT_UNIFORM) return fail(QG_ERR_UNSUPPORTED, "the prefill route takes uniform-code handles");
+  if (!coded(h)) return fail(QG_ERR_UNSUPPORTED, "the prefill route takes uniform-code and MXFP4 handles");
   const size_t row = (size_t)h->K * sizeof(uint16_t);
   *full_bytes = kPrefillGemmWs + (size_t)h->N * row;
   *min_bytes = h->segs.size() == 1 ? kPrefillGemmWs + 16 * row : *full_bytes;
@@ -1075,11 +1095,11 @@ qg_status qgemv_run_prefill(qg_handle h, const uint16_t* x, int32_t M, uint16_t*
     const int n1 = std::min(h->N, n0 + nc);
     if (h->segs.size() == 1) {  // one width: column n is tile n / 16, lane n % 16
       const HostSeg& g = h->segs[0];
-      const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0, g.sq};
+      const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0, g.sq, g.mx};
       QG_HIP(launch_dequant_f16(sd, h->col_map, h->G, h->G4, h->K, n0 / 16, (n1 - n0) / 16, n0, n1, wbuf, st));
     } else {  // several widths (one chunk): every segment's columns land at their own rows
       for (const auto& g : h->segs) {
-        const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0, g.sq};
+        const SegDev sd{g.codes, g.scales, g.bits, g.tiles, g.tile0, g.sq, g.mx};
         QG_HIP(launch_dequant_f16(sd, h->col_map, h->G, h->G4, h->K, 0, g.tiles, n0, n1, wbuf, st));
       }
     }
@@ -1108,9 +1128,9 @@ qg_status qg_stream_read(const void* buf, int64_t bytes, void* stream) {
 qg_status qgemv_debug_unpack(qg_handle h, int32_t* codes, void* stream) {
   g_err.clear();
   if (!h || !codes) return fail(QG_ERR_INVALID_ARG, "NULL argument");
-  if (h->format != QG_FMT_UNIFORM) return fail(QG_ERR_INVALID_ARG, "debug_unpack takes a uniform-code handle");
+  if (!coded(h)) return fail(QG_ERR_INVALID_ARG, "debug_unpack takes a uniform-code or MXFP4 handle");
   for (const auto& s : h->segs) {
-    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq};
+    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq, s.mx};
     QG_HIP(launch_debug_uniform(sd, h->col_map, h->G, h->G4, h->K, 0, codes, nullptr, nullptr, (hipStream_t)stream));
   }
   return QG_OK;
@@ -1125,7 +1145,7 @@ qg_status qgemv_debug_dequant(qg_handle h, float* w, uint16_t* q16, void* stream
     return QG_OK;
   }
   for (const auto& s : h->segs) {
-    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq};
+    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq, s.mx};
     QG_HIP(launch_debug_uniform(sd, h->col_map, h->G, h->G4, h->K, 0, nullptr, w, q16, st));
   }
   return QG_OK;
@@ -1134,9 +1154,9 @@ qg_status qgemv_debug_dequant(qg_handle h, float* w, uint16_t* q16, void* stream
 qg_status qgemv_debug_operand(qg_handle h, int32_t* codes, uint16_t* b16, float* w, void* stream) {
   g_err.clear();
   if (!h || (!codes && !b16 && !w)) return fail(QG_ERR_INVALID_ARG, "NULL argument");
-  if (h->format != QG_FMT_UNIFORM) return fail(QG_ERR_INVALID_ARG, "debug_operand takes a uniform-code handle");
+  if (!coded(h)) return fail(QG_ERR_INVALID_ARG, "debug_operand takes a uniform-code or MXFP4 handle");
   for (const auto& s : h->segs) {
-    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq};
+    const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq, s.mx};
     QG_HIP(launch_debug_uniform(sd, h->col_map, h->G, h->G4, h->K, 1, codes, w, b16, (hipStream_t)stream));
   }
   return QG_OK;

@@ -91,7 +91,15 @@ typedef enum {
   QG_ERR_OOM = -4           /* device allocation failed                                          */
 } qg_status;
 
-typedef enum { QG_FMT_UNIFORM = 0, QG_FMT_TRELLIS3 = 1 } qg_format;
+/* QG_FMT_MXFP4 ("The Rock8", format table, MXFP4 row: OCP microscaling, E2M1
+ * elements -- sign, 2 exponent bits with bias 1, 1 mantissa bit -- nibble-
+ * packed, one UE8M0 scale byte 2^(e - 127) per 32 elements along K; 255 is
+ * NaN): codes in the 4-bit canonical layout below (element j of a row at bits
+ * [4j, 4j + 4) of its stream), `scales` points at uint8 exponent bytes
+ * [N][K/32], group_size 32, bits 0 or 4.  The verify GEMM (2..32 rows) runs
+ * each 128-group at its largest exponent: the other 32-blocks' elements are
+ * exact while within 2^9 of it and are rounded once to fp16 beyond that. */
+typedef enum { QG_FMT_UNIFORM = 0, QG_FMT_TRELLIS3 = 1, QG_FMT_MXFP4 = 2 } qg_format;
 
 enum {
   QG_FLAG_X_PREROTATED = 1u << 0, /* TRELLIS3: x already rotated, skip the Walsh-Hadamard step */
