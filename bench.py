@@ -65,11 +65,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def src_hash() -> str:
+# the sources the per-group M = 1 GEMV (the roofline entry's kernel) is built from
+GEMV_SOURCES = ("k_m1q.hip", "qg_gemv.h", "qg_stage.h", "qg_decode.h", "qg_common.h", "qg_args.h", "qg_launch.h")
+
+
+def src_hash(files=None) -> str:
+    """sha256 prefix over the library sources (all of them, or the named ones)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "bit_weight_only_packed_amd", "csrc")
     for f in sorted(os.listdir(d)):
-        if not f.endswith((".h", ".hip")):
+        if not f.endswith((".h", ".hip")) or (files is not None and f not in files):
             continue
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
@@ -239,7 +244,7 @@ def main():
         print(json.dumps({"profile": f"{'gemv' if Mp == 1 else 'verify gemm'} M={Mp} 5120x17408",
                           "launches": args.profile_gate * R,
                           "graph_us_per_launch": round(us, 3), "copy_bytes_each_way": 4 * n,
-                          "src_hash": src_hash()}), flush=True)
+                          "src_hash": src_hash(), "gemv_src_hash": src_hash(GEMV_SOURCES)}), flush=True)
         return
 
     # ---------------- the timed step: layer set at M = 1 ----------------
@@ -436,13 +441,13 @@ def main():
     if os.path.exists(tpath):
         with open(tpath) as f:
             tj = json.load(f)
-        if tj.get("src_hash") == src_hash():
+        if tj.get("gemv_src_hash") == src_hash(GEMV_SOURCES):
             traffic = tj.get("bytes_per_launch")
     result["roofline"] = {"bound": "hbm", "kernel": "qg::k_gemv_q (M=1 GEMV, 5120x17408, 3-bit)",
                           "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                           "algorithmic_bytes_per_launch": gate_bytes, "avg_launch_us": gate_us,
-                          "src_hash": src_hash()}
+                          "src_hash": src_hash(), "gemv_src_hash": src_hash(GEMV_SOURCES)}
 
     # ---------------- fused MLP, mixed widths ----------------
     if not args.quick:
