@@ -146,12 +146,13 @@ struct TbArgs {
   const uint32_t* codes;   // [U][64][3]
   const uint16_t* scales;  // [U][16]
   const uint16_t* cb;      // [65536] fp16
-  const uint16_t* x;       // [M][K] fp16, rotated
+  const uint16_t* x;       // [M][K] fp16: rotated already (rot 0) or as given (rot 1)
   uint16_t* y;             // [M][N] fp16
   float* partial;          // [RB][maxseg][M][16] (S > 1, acc NULL)
   int* counters;           // [RB], zero between launches
   unsigned long long* acc; // [M][N] fixed-point output words (S > 1), zero between launches; or NULL
   int M, K, N, G, RB, maxseg, S;
+  int rot;                 // rotate each group of x in the kernel (Walsh-Hadamard, 2^-3.5)
 };
 
 }  // namespace qg

@@ -425,18 +425,39 @@ __global__ __launch_bounds__(64 * TbShape<MT>::NW) void k_trellis_band(TbArgs a)
                                                16, (uint32_t)(ci * 1024 + lane * 16), 0, 0, 0);
   }
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(a.x), (uint32_t)a.M * a.K * 2u);
-  // step i's x fragment (group g0 + i) into slot sl: rows m = XRD * wave + r, the
-  // 16-byte chunk p of a row at position p ^ (m & 15); rows past M and steps past
-  // the slice read zeros
-  auto copy_x = [&](int i, int sl) {
+  // Step i's x fragment (group g0 + i): this wave's rows m = XRD * wave + r, lane
+  // l holding elements 2l and 2l + 1 of a row (rows past M and steps past the
+  // slice read zeros), loaded PD steps ahead into register set i % PD; one step
+  // before use it is rotated in registers (the Walsh-Hadamard matrix is the same
+  // under one bit permutation of both its indices, so the butterflies work on
+  // this pairing: the local stage pairs index bit 0, the lane stages bits 1..6)
+  // and written to its slot, the 16-byte chunk p of row m at position p ^ (m & 15).
+  uint32_t xr[PD][XRD];
+  auto load_x = [&](int i, uint32_t (&v)[XRD]) {
     const int g = g0 + i;
 #pragma unroll
     for (int r = 0; r < XRD; ++r) {
       const int m = XRD * wave + r;
+      const uint32_t voff = (m < a.M && i < ng) ? (uint32_t)(((size_t)m * a.K + (size_t)g * 128 + 2 * lane) * 2) : 0xFFFFFFF0u;
+      v[r] = __builtin_amdgcn_raw_buffer_load_b32(rx, voff, 0, 0);
+    }
+  };
+  auto put_x = [&](const uint32_t (&v)[XRD], int sl) {
+#pragma unroll
+    for (int r = 0; r < XRD; ++r) {
+      const int m = XRD * wave + r;
+      uint32_t out = v[r];
+      if (a.rot) {
+        float p0 = h2f((uint16_t)(v[r] & 0xFFFFu)), p1 = h2f((uint16_t)(v[r] >> 16));
+        const float sum = p0 + p1, dif = p0 - p1;
+        p0 = sum;
+        p1 = dif;
+        fwht_lanes(p0, p1, lane);
+        const float f = 0.08838834764831845f;  // 2^-3.5
+        out = (uint32_t)f2h(p0 * f) | ((uint32_t)f2h(p1 * f) << 16);
+      }
       const int pc = (lane >> 2) ^ (m & 15);
-      const uint32_t voff =
-          (m < a.M && i < ng) ? (uint32_t)(((size_t)m * a.K + (size_t)g * 128 + pc * 8 + (lane & 3) * 2) * 2) : 0xFFFFFFF0u;
-      lds_copy4(rx, xl + (size_t)sl * SLOT + (size_t)m * 256, voff);
+      *reinterpret_cast<uint32_t*>(xl + (size_t)sl * SLOT + (size_t)m * 256 + pc * 16 + (lane & 3) * 4) = out;
     }
   };
   auto load_unit = [&](TbUnit& t, int i) {
@@ -450,10 +471,13 @@ __global__ __launch_bounds__(64 * TbShape<MT>::NW) void k_trellis_band(TbArgs a)
   TbUnit c[PD];
 #pragma unroll
   for (int i = 0; i < PD; ++i) {
-    copy_x(i, i);
+    load_x(i, xr[i]);
     load_unit(c[i], i);
     __builtin_amdgcn_sched_barrier(0);
   }
+  tb_vm_wait<2 + (PD - 1) * (XRD + 2)>();  // step 0's x
+  put_x(xr[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
   const char* cbl = smem;
   const int kq = lane >> 4, m16 = lane & 15;
   int xa[MT][4];  // this lane's A-fragment offsets within a slot
@@ -468,13 +492,16 @@ __global__ __launch_bounds__(64 * TbShape<MT>::NW) void k_trellis_band(TbArgs a)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
   int sl = 0;  // slot of the step being computed
-  // one step: wait for this wave's copies of the step's x, meet the other waves
-  // (the fragment is then whole, and the slot the next copy overwrites is
-  // free), compute the unit, then issue the copies and loads PD steps ahead.
-  // Every step issues the same loads (past the slice through empty ranges), so
-  // the wait count is the same in every step.
-  auto step = [&](TbUnit& cu, int i) {
-    tb_vm_wait<2 + (PD - 1) * (XRD + 2)>();
+  // one step: wait for the next step's x (and so for this step's unit, loaded
+  // before it), meet the other waves (this step's fragment, written one step
+  // ago by each wave, is then whole), compute the unit, rotate the next step's
+  // x into its slot, then issue the x and code loads PD steps ahead.  Every step issues
+  // the same loads (past the slice through empty ranges), so the wait count is
+  // the same in every step.
+  // (li = i % PD, a constant once the loop below is unrolled: the register sets
+  // are indexed by it)
+  auto step = [&](TbUnit& cu, int i, int li) {
+    tb_vm_wait<2 + (PD - 2) * (XRD + 2)>();
     lds_barrier();
     if (mine && i < ng) {
       const uint32_t z2 = cu.z.x, z1 = cu.z.y, z0 = cu.z.z;
@@ -496,16 +523,18 @@ __global__ __launch_bounds__(64 * TbShape<MT>::NW) void k_trellis_band(TbArgs a)
         for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(sc, cg[e], acc[mt][e]);
       }
     }
+    // the next step's x into its slot, behind this step's MFMAs (every wave
+    // has passed this step's barrier, so none still reads that slot)
+    put_x(xr[(li + 1) % PD], sl + 1 == XB ? 0 : sl + 1);
     __builtin_amdgcn_sched_barrier(0);
-    const int sl_next = sl == 0 ? XB - 1 : sl - 1;  // (i + PD) % XB = (i - 1) % XB
-    copy_x(i + PD, sl_next);
+    load_x(i + PD, xr[li]);
     load_unit(cu, i + PD);
     __builtin_amdgcn_sched_barrier(0);
     sl = sl + 1 == XB ? 0 : sl + 1;
   };
   for (int u = 0; u < ng; u += PD) {
 #pragma unroll
-    for (int i = 0; i < PD; ++i) step(c[i], u + i);
+    for (int i = 0; i < PD; ++i) step(c[i], u + i, i);
   }
   if (!mine) return;
   // ---- results of this row block over the slice

@@ -451,9 +451,20 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
 
 // M = 1 GEMV that rotates x itself into LDS (no separate rotation launch):
 // room for the rotated x beside the codebook up to K = 16384
+// x rotated inside the run kernel.  2..32 rows: each band workgroup rotates the
+// groups of its K slice as it stages them, so every group is rotated once per
+// band; measured (same-box A/B, 8 rows): k/v (160 band-groups) 13.2 -> 11.8 us,
+// q/o (800) 19.0 -> 18.5, but gate/up and down (2,720) 39.5 -> 41.1 and
+// 35.1 -> 35.9, where one rotation launch is cheaper.  One row: where the
+// rotated x fits the GEMV's LDS.
 bool trellis_xl(const qg_plan* h, int M) {
+  if (M > 1) {
+    const int nw = M > 16 ? TbShape<2>::NW : TbShape<1>::NW;
+    const int64_t bands = (h->N / 16 + nw - 1) / nw;
+    return !(h->flags & QG_FLAG_X_PREROTATED) && bands * h->G <= 2000;
+  }
   if (h->pins & QG_PIN_TRELLIS_ROT_LAUNCH) return false;
-  return M == 1 && !(h->flags & QG_FLAG_X_PREROTATED) && (size_t)h->K * 2 <= (size_t)TR_XL_BYTES &&
+  return !(h->flags & QG_FLAG_X_PREROTATED) && (size_t)h->K * 2 <= (size_t)TR_XL_BYTES &&
          h->G <= TR_XL_GMAX * TR_NW;
 }
 
@@ -473,6 +484,7 @@ qg_status run_trellis(const qg_plan* h, const Work& w, const uint16_t* x, int M,
     b.scales = h->tscales;
     b.cb = h->codebook;
     b.x = xr;
+    b.rot = xl ? 1 : 0;
     b.y = y;
     b.partial = w.partial;
     b.counters = w.counters;
