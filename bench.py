@@ -4,8 +4,10 @@
 A step is one decode pass of a 27B-class dense layer's linear set -- q, k, v, o
 (5120x5120, 5120x1024 x2, 5120x5120), gate, up (5120x17408) and down
 (17408x5120), K x N = in x out -- at M = 1 activation row, 3-bit codes with one
-fp16 scale per 128 weights, fp16 activations, one launch per matrix.  All
-inputs are seeded and synthetic and already resident in HBM.  The weights
+fp16 scale per 128 weights, fp16 activations, in decode order with the
+siblings that read one input batched into one launch (qgemv_run_batch): q,k,v
+| o | gate,up | down, four launches.  All inputs are seeded and synthetic and
+already resident in HBM.  The weights
 exist in R distinct copies (>= 1 GiB in total, four times the 256 MB Infinity
 Cache) and consecutive steps use consecutive copies, so every step streams its
 weights from HBM.  Steps are replayed from captured HIP graphs (no host launch
@@ -15,9 +17,9 @@ trials of exactly --steps steps each; the line reports the median trial.
 Printed (one JSON line): effective weight GB/s of the step (value), per-shape
 us/call at M = 1, 8, 16, 32 and the M=32 / M=1 ratio, each M = 1 call against
 the measured streaming read of the same bytes, the fused MLP with mixed widths,
-the trellis format, the roofline entry of the dominant kernel (the M = 1 GEMV
-on the 5120x17408 gate/up shape) and the CPU oracle on bounded samples of every
-workload.
+the trellis format, the roofline entry of the dominant kernel (the batched
+M = 1 GEMV over the gate and up matrices, 2 x 5120x17408, one launch) and the
+CPU oracle on bounded samples of every workload.
 """
 from __future__ import annotations
 
@@ -50,6 +52,10 @@ def parse():
     p.add_argument("--profile-gate", type=int, default=0, metavar="REPS",
                    help="profiling mode: REPS graph replays of the M=1 GEMV on the 5120x17408 shape over all "
                         "weight copies, then a 256 MiB device copy (the counter calibration), then exit")
+    p.add_argument("--profile-gateup", type=int, default=0, metavar="REPS",
+                   help="profiling mode: REPS graph replays of the step's dominant launch -- the M=1 GEMV over "
+                        "the gate and up matrices batched into one launch -- over all weight copies, then a "
+                        "256 MiB device copy (the counter calibration), then exit")
     p.add_argument("--profile-rows", type=int, default=1, choices=(1, 8, 16, 32), metavar="M",
                    help="rows of the profiled gate/up product (1 = the GEMV, more = the verify GEMM)")
     p.add_argument("--profile-mlp", type=int, default=0, metavar="REPS",
@@ -217,10 +223,59 @@ def main():
     # distinct x rows per K (contiguous [M][K] views)
     xk = {(M, K): xin(M, K).contiguous() for M in (1, 8, 16, 32) for K in (5120, 17408)}
 
-    def layer_step(r, M=1):
+    def layer_step_each(r, M=1):
+        """the layer set, one launch per matrix"""
         for i, sh in enumerate(shapes):
             lins[r][i].run(xk[(M, sh["K"])], out=ys[M][:, : sh["N"]] if sh["N"] == 17408 else
                            ys[M].view(-1)[: M * sh["N"]].view(M, sh["N"]))
+
+    # M = 1 outputs of the batched launches, one tensor per matrix
+    yb = [torch.empty((1, sh["N"]), dtype=torch.float16, device=dev) for sh in shapes]
+
+    def batch_siblings(r):
+        """decode order, siblings that read one x batched: q,k,v | o | gate,up | down"""
+        L, x5, x17 = lins[r], xk[(1, 5120)], xk[(1, 17408)]
+        Q.run_batch([L[0], L[1], L[2]], [x5, x5, x5], yb[0:3])
+        L[3].run(x5, out=yb[3])
+        Q.run_batch([L[4], L[5]], [x5, x5], yb[4:6])
+        L[6].run(x17, out=yb[6])
+
+    def batch_gateup(r):
+        L, x5 = lins[r], xk[(1, 5120)]
+        Q.run_batch([L[4], L[5]], [x5, x5], yb[4:6])
+
+    def layer_step(r, M=1):
+        """the timed step: at M = 1 the batched decode order, else one launch per matrix"""
+        if M == 1:
+            batch_siblings(r)
+        else:
+            layer_step_each(r, M)
+
+    def calibration_copies():
+        n = 64 << 20
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return 4 * n
+
+    if args.profile_gateup:
+        # the step's dominant launch alone, launched exactly as the timed step
+        # launches it, then plain copies of known size for the HBM counter scale
+        def gateup_all():
+            for r in range(R):
+                batch_gateup(r)
+        g = capture(gateup_all)
+        time_graph(g, 2)
+        t = time_graph(g, args.profile_gateup)
+        us = t / (args.profile_gateup * R) * 1e6
+        cb = calibration_copies()
+        print(json.dumps({"profile": "gemv batch M=1 gate,up 2 x 5120x17408 (one launch)",
+                          "launches": args.profile_gateup * R, "graph_us_per_launch": round(us, 3),
+                          "copy_bytes_each_way": cb, "src_hash": src_hash(),
+                          "gemv_src_hash": src_hash(GEMV_SOURCES)}), flush=True)
+        return
 
     if args.profile_gate:
         # the dominant kernel alone, launched exactly as the per-shape timing below
@@ -235,24 +290,21 @@ def main():
         time_graph(g, 2)
         t = time_graph(g, args.profile_gate)
         us = t / (args.profile_gate * R) * 1e6
-        n = 64 << 20
-        src = torch.ones(n, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        cb = calibration_copies()
         print(json.dumps({"profile": f"{'gemv' if Mp == 1 else 'verify gemm'} M={Mp} 5120x17408",
                           "launches": args.profile_gate * R,
-                          "graph_us_per_launch": round(us, 3), "copy_bytes_each_way": 4 * n,
+                          "graph_us_per_launch": round(us, 3), "copy_bytes_each_way": cb,
                           "src_hash": src_hash(), "gemv_src_hash": src_hash(GEMV_SOURCES)}), flush=True)
         return
 
     # ---------------- the timed step: layer set at M = 1 ----------------
-    def steps_graph(n, M=1):
+    def steps_graph(n, M=1, step=None):
         """One graph of n consecutive steps, on weight copies 0 .. n-1."""
+        step = step or layer_step
+
         def f():
             for r in range(n):
-                layer_step(r, M)
+                step(r, M)
         return capture(f)
 
     def run_steps(n, g_full, g_rem):
@@ -296,7 +348,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode GEMV, M=1, 27B-class layer set q,k,v,o,gate,up,down "
                                "(5120x5120 x2, 5120x1024 x2, 5120x17408 x2, 17408x5120), 3-bit codes, "
-                               "fp16 scale per 128, fp16 x, one launch per matrix", "M": 1,
+                               "fp16 scale per 128, fp16 x, decode order with siblings batched "
+                               "(q,k,v | o | gate,up | down: 4 launches)", "M": 1,
                    "weight_bytes_per_step": per_copy, "weight_copies": R,
                    "pct_of_8TBs": round(100 * value / HBM_PEAK_GBS, 2)},
         "trials": {"n": len(trial_s), "us_per_step": [round(t * 1e6 / K_steps, 3) for t in trial_s]},
@@ -358,40 +411,31 @@ def main():
     result["stream_read_layer_set_us"] = round(ls_stream, 3)
     result["pct_of_stream_read"] = round(100 * ls_stream * R / (t_s * 1e6 / K_steps * R), 1)
 
+    # the layer set with one launch per matrix at every row count (the verify
+    # steps; at M = 1 beside the batched step above)
     layer_us = {}
     for M in (1, 8, 16, 32):
-        layer_us[M] = graph_us(steps_graph(R, M), R, reps=3)
-    result["layer_set_us"] = {f"M{M}": round(v, 3) for M, v in layer_us.items()}
-    result["layer_set_ratio_M32_M1"] = round(layer_us[32] / layer_us[1], 3)
-    result["layer_set_ratio_M8_M1"] = round(layer_us[8] / layer_us[1], 3)
-    log("layer set us", result["layer_set_us"])
+        layer_us[M] = graph_us(steps_graph(R, M, layer_step_each), R, reps=3)
+    result["layer_set_each_us"] = {f"M{M}": round(v, 3) for M, v in layer_us.items()}
+    result["layer_set_each_ratio_M32_M1"] = round(layer_us[32] / layer_us[1], 3)
+    result["layer_set_each_ratio_M8_M1"] = round(layer_us[8] / layer_us[1], 3)
+    result["layer_set_ratio_M32_vs_batched_M1"] = round(layer_us[32] / (t_s * 1e6 / K_steps), 3)
+    log("layer set, one launch per matrix, us", result["layer_set_each_us"])
 
-    # ---------------- the layer set through qgemv_run_batch ----------------
-    # all seven products in one launch (independent inputs, as in the timed
-    # step), and in decode order with siblings batched: q|k|v (one x), o,
-    # gate|up (one x), down -- 4 launches
-    yb = {M: [torch.empty((M, sh["N"]), dtype=torch.float16, device=dev) for sh in shapes] for M in (1,)}
+    # ---------------- the layer set in one qgemv_run_batch launch ----------------
+    # all seven products in one launch (independent inputs): the floor of the
+    # batched launch path, beside the 4-launch decode order of the timed step
+    def batch_all(r):
+        Q.run_batch(lins[r], [xk[(1, sh["K"])] for sh in shapes], yb)
 
-    def batch_all(r, M=1):
-        Q.run_batch(lins[r], [xk[(M, sh["K"])] for sh in shapes], yb[M])
-
-    def batch_siblings(r, M=1):
-        L, x5, x17 = lins[r], xk[(M, 5120)], xk[(M, 17408)]
-        Q.run_batch([L[0], L[1], L[2]], [x5, x5, x5], yb[M][0:3])
-        L[3].run(x5, out=yb[M][3])
-        Q.run_batch([L[4], L[5]], [x5, x5], yb[M][4:6])
-        L[6].run(x17, out=yb[M][6])
-
-    for name, fn in (("layer_set_one_launch", batch_all), ("layer_set_siblings_batched", batch_siblings)):
-        def f(fn=fn):
-            for r in range(R):
-                fn(r)
-        us = graph_us(capture(f), R, reps=5)
-        result[name] = {"us_M1": round(us, 3), "GBs_M1": round(per_copy / us / 1e3, 1),
-                        "pct_8TBs_M1": round(100 * per_copy / us / 1e3 / HBM_PEAK_GBS, 2),
-                        "pct_of_stream_read": round(100 * ls_stream / us, 1),
-                        "launches": 1 if name == "layer_set_one_launch" else 4}
-        log(name, result[name])
+    def f_all():
+        for r in range(R):
+            batch_all(r)
+    us = graph_us(capture(f_all), R, reps=5)
+    result["layer_set_one_launch"] = {"us_M1": round(us, 3), "GBs_M1": round(per_copy / us / 1e3, 1),
+                                      "pct_8TBs_M1": round(100 * per_copy / us / 1e3 / HBM_PEAK_GBS, 2),
+                                      "pct_of_stream_read": round(100 * ls_stream / us, 1), "launches": 1}
+    log("layer_set_one_launch", result["layer_set_one_launch"])
 
     # ---------------- the same layer set with sibling projections fused ----------------
     # q|k|v and gate|up read the same input: each pair of siblings runs as one
@@ -432,22 +476,32 @@ def main():
                 l.close()
         del flins
 
-    # ---------------- roofline entry: M=1 GEMV on the gate/up shape ----------------
-    gate_us = per_shape["gateup"]["us_M1"]
-    gate_bytes = per_shape["gateup"]["weight_bytes"]
-    achieved = gate_bytes / gate_us / 1e3
+    # ---------------- roofline entry: the step's dominant launch ----------------
+    # the batched M = 1 GEMV over gate and up (one launch, 2 x 5120x17408),
+    # timed live like the step: a graph of its launches over every weight copy
+    def f_gu():
+        for r in range(R):
+            batch_gateup(r)
+    gu_us = graph_us(capture(f_gu), R, reps=20)
+    gu_bytes = lins[0][4].weight_bytes() + lins[0][5].weight_bytes()
+    achieved = gu_bytes / gu_us / 1e3
+    gu_stream = stream_us(gu_bytes)
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", "traffic_gemv_m1_gateup.json")
+    tpath = os.path.join(ROOT, "profiles", "traffic_gemv_batch_gateup.json")
     if os.path.exists(tpath):
         with open(tpath) as f:
             tj = json.load(f)
         if tj.get("gemv_src_hash") == src_hash(GEMV_SOURCES):
             traffic = tj.get("bytes_per_launch")
-    result["roofline"] = {"bound": "hbm", "kernel": "qg::k_gemv_q (M=1 GEMV, 5120x17408, 3-bit)",
+    result["roofline"] = {"bound": "hbm",
+                          "kernel": "qg::k_gemv_batch (M=1 GEMV, gate and up 2 x 5120x17408 in one launch, 3-bit)",
                           "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                          "algorithmic_bytes_per_launch": gate_bytes, "avg_launch_us": gate_us,
+                          "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3),
+                          "stream_read_us": round(gu_stream, 3),
+                          "pct_of_stream_read": round(100 * gu_stream / gu_us, 1),
                           "src_hash": src_hash(), "gemv_src_hash": src_hash(GEMV_SOURCES)}
+    log("roofline", result["roofline"])
 
     # ---------------- fused MLP, mixed widths ----------------
     if not args.quick:
