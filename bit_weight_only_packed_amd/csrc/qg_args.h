@@ -79,7 +79,8 @@ struct SkArgs {
 // fp16) and their quarter sums
 __host__ __device__ constexpr size_t sk_lds_bytes(int NW, int runq) { return (size_t)NW * runq * 1088; }
 
-constexpr int XS_PD = 3;  // units whose code loads are in flight per wave
+constexpr int XS_PD = 2;    // code buffers per wave: units in flight while one is computed, plus it
+constexpr int XS_LEAD = 1;  // units whose loads are issued before the x slice is waited for
 
 struct XsArgs {
   WSet w[2];                  // w[1]: up matrix of the fused gate/up pass

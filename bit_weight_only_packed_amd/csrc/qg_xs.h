@@ -229,14 +229,19 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
   // ---- this wave's tile group tgb + wave: its units are the slice's quads
   const int tg = tgb + wave;
   const bool mine = tg < tge;
+  // Only XS_LEAD units' code loads go out before the x slice is waited for:
+  // a wave that issues more stalls at the issue once the compute unit's
+  // outstanding loads fill up, and cannot reach its first compute until the
+  // whole batch has streamed in.
+  static_assert(XS_LEAD >= 1 && XS_LEAD <= XS_PD, "lead units");
   XsUnit<B, T, ND> c[XS_PD];
 #pragma unroll
-  for (int i = 0; i < XS_PD; ++i) {
+  for (int i = 0; i < XS_LEAD; ++i) {
     xs_load<B, T, ND, SQ>(c[i], sd, tg, q0 + i, mine && i < nq, G4, (uint32_t)lane);
     __builtin_amdgcn_sched_barrier(0);  // unit by unit, in order of use
   }
   {
-    constexpr int n = XS_PD * xs_loads<B, T, ND>();  // issued after the x copy
+    constexpr int n = XS_LEAD * xs_loads<B, T, ND>();  // issued after the x copy
     static_assert(n < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
   }
@@ -248,33 +253,6 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
     }
   }
   lds_barrier();  // every wave's share of the slice has landed
-  // ---- group sums of x: lane gl of a wave sums group gl of one row, its 16
-  // chunks in the order (cc + gl) & 15 of their place in the row (so 16 lanes
-  // hit 16 bank groups); the order depends on the group only, never on the
-  // row's place in the batch (the row swizzle is undone on the address), so a
-  // row's sums round the same at every row count
-  if constexpr (!SQ) {
-    const uint32_t ones = 0x3C003C00u;
-    const int gl = lane & 31;
-    for (int mb = 2 * wave; mb < M; mb += 2 * NW) {
-      const int m = mb + (lane >> 5);
-      if (m < M && gl < 4 * nq) {
-        const char* rp = xl + (size_t)m * RS + gl * 256;
-        float acc = 0.0f;
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) {
-          const uint4 v = *reinterpret_cast<const uint4*>(rp + (((cc + gl) & 15) ^ (m & 15)) * 16);
-          acc = dot2(v.x, ones, acc);
-          acc = dot2(v.y, ones, acc);
-          acc = dot2(v.z, ones, acc);
-          acc = dot2(v.w, ones, acc);
-        }
-        xsum[gl * (16 * MT) + m] = acc;
-      }
-    }
-  }
-  lds_barrier();
-  if (!mine) return;
   // this lane's A-fragment addresses (group 0): row 16 mt + m16 (rows past M
   // repeat row M - 1, never stored), chunk 4 kq + v at its swizzled position
   const char* xa[MT][4];
@@ -287,6 +265,25 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
       for (int v = 0; v < 4; ++v) xa[mt][v] = xl + (size_t)row * RS + (((4 * kq + v) ^ (row & 15)) * 16);
     }
   }
+  // ---- group sums of x on the matrix cores: group gl's A fragments against
+  // an all-ones B operand, chained over the group's four 32-k blocks like the
+  // products; lane (kq, n) gets the sums of rows 16 mt + 4 kq + e in every
+  // column n, and the lanes of column 0 store them.  A row's sum depends on
+  // that row's values only, so it rounds the same at every row count.
+  if constexpr (!SQ) {
+    const h8_t ones = as_h8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+    for (int gl = wave; gl < 4 * nq; gl += NW) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f4_t cc = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) cc = mfma16(*reinterpret_cast<const h8_t*>(xa[mt][v] + gl * 256), ones, cc);
+        if ((lane & 15) == 0) *reinterpret_cast<f4_t*>(xsum + gl * (16 * MT) + 16 * mt + 4 * (lane >> 4)) = cc;
+      }
+    }
+  }
+  lds_barrier();
+  if (!mine) return;
   // ---- units
   f4_t R[ND][T][MT];
 #pragma unroll
@@ -298,15 +295,19 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
   // Straight-line code over NQ units (a slice has nq <= NQ; units past nq are
   // skipped, their loads go through empty ranges): no loop carries the ring,
   // so no register copy waits for a load in flight, and the loads are issued
-  // in the same order on every path, so each wait counts exactly.
+  // in the same order on every path, so each wait counts exactly.  Before
+  // unit i is computed, the loads of every unit up to i + XS_PD - 1 are out
+  // (unit i + XS_PD - 1 into the buffer unit i - 1 has just freed).
   // (scheduling barriers keep each unit's work after the previous unit's: the
   // scheduler would otherwise pull the next unit's decode forward, and with
   // it the wait for that unit's codes)
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    if (i < nq) xs_unit<B, T, MT, ND, XSC, SQ, MX>(c[i % XS_PD], xa, xsum, xfac, 4 * i, min(4, G - 4 * (q0 + i)), lane, R);
+#pragma unroll
+    for (int u = i == 0 ? XS_LEAD : i + XS_PD - 1; u <= i + XS_PD - 1; ++u)
+      if (u < NQ) xs_load<B, T, ND, SQ>(c[u % XS_PD], sd, tg, q0 + u, u < nq, G4, (uint32_t)lane);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + XS_PD < NQ) xs_load<B, T, ND, SQ>(c[i % XS_PD], sd, tg, q0 + i + XS_PD, i + XS_PD < nq, G4, (uint32_t)lane);
+    if (i < nq) xs_unit<B, T, MT, ND, XSC, SQ, MX>(c[i % XS_PD], xa, xsum, xfac, 4 * i, min(4, G - 4 * (q0 + i)), lane, R);
     __builtin_amdgcn_sched_barrier(0);
   }
   // ---- results: stored directly (one slice), or added to the fixed-point
@@ -400,46 +401,44 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
     }
     return;
   }
-  // partials in the fp32 workspace, coherent at device scope (sc1); then one arrival
-  // per wave at the tile group's counter
+  // partials in the fp32 workspace, one block per (tile group, slice, matrix):
+  // [T * MT quarter tiles][64 lanes][4] fp32, so each quarter tile is one
+  // contiguous 1 KiB store, written through to the device coherence point
+  // (sc1); then one arrival per wave at the tile group's counter.  Rows past M
+  // and tiles past the segment are stored too (never read as outputs).
+  constexpr int NQT = T * MT;
+  constexpr uint32_t kSc1 = 16;  // cache policy: device-coherent access
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(uniform_ptr(a.partial) + (size_t)(tgbase + tg) * S * ND * NQT * 256,
+                                              (uint32_t)S * ND * NQT * 1024u);
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int tile = tg * T + t;
-    if (tile >= sd[0].tiles) continue;
-    const int pc = 16 * (sd[0].tile0 + tile) + j;
+  for (int d = 0; d < ND; ++d)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 16 * mt + 4 * mq + e;
-        if (m >= M) continue;
-#pragma unroll
-        for (int d = 0; d < ND; ++d)
-          st_partial(a.partial + ((size_t)(d * S + s) * M + m) * a.NP + pc, R[d][t][mt][e] * kOut);
+      for (int mt = 0; mt < MT; ++mt) {
+        const f4_t v = R[d][t][mt] * kOut;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), rp,
+                                               (uint32_t)(((s * ND + d) * NQT + t * MT + mt) * 1024 + lane * 16), 0, kSc1);
       }
-  }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
   int old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(a.counters + tgbase + tg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
   if (old != S - 1) return;
   if (lane == 0) __hip_atomic_store(a.counters + tgbase + tg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // the last slice to arrive: every partial of the group, XS_KB slices at a time
-  // with all their loads in flight, summed in slice order 0..S-1
+  // the last slice to arrive: the other slices' blocks, KB slices at a time
+  // with all their loads in flight, summed in slice order 0..S-1 (its own
+  // slice from registers, the same values it stored)
   constexpr int KB = ND == 2 ? 2 : 4;
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(uniform_ptr(a.partial), (uint32_t)((size_t)ND * S * M * a.NP * 4u));
-  float acc[ND][T][MT][4];
+  f4_t acc[ND][T][MT];
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[d][t][mt][e] = 0.0f;
-  const int pc0 = 16 * (sd[0].tile0 + tg * T) + j;
+      for (int mt = 0; mt < MT; ++mt) acc[d][t][mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
   for (int k0 = 0; k0 < S; k0 += KB) {
-    float v[KB][ND][T][MT][4];
+    f4_t v[KB][ND][T][MT];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -447,28 +446,26 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
 #pragma unroll
         for (int t = 0; t < T; ++t)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt) {
+            const int k = k0 + kb;
+            // slices past S, and its own, read outside the range: zeros, and
+            // are not added from memory
+            const uint32_t vo = (k < S && k != s) ? (uint32_t)(((k * ND + d) * NQT + t * MT + mt) * 1024 + lane * 16)
+                                                  : 0xFFFFFFF0u;
+            v[kb][d][t][mt] = __builtin_bit_cast(f4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, vo, 0, kSc1));
+          }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int m = min(16 * mt + 4 * mq + e, M - 1);
-              const int k = k0 + kb;
-              // slices past S read past the range: zeros, and are not added
-              const uint32_t off = k < S ? (uint32_t)((((size_t)(d * S + k) * M + m) * a.NP + pc0 + 16 * t) * 4u)
-                                         : 0xFFFFFFF0u;
-              v[kb][d][t][mt][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, 16));
-            }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      if (k0 + kb < S) {
+    for (int kb = 0; kb < KB; ++kb) {
+      const int k = k0 + kb;
+      if (k < S) {
 #pragma unroll
         for (int d = 0; d < ND; ++d)
 #pragma unroll
           for (int t = 0; t < T; ++t)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[d][t][mt][e] += v[kb][d][t][mt][e];
+            for (int mt = 0; mt < MT; ++mt) acc[d][t][mt] += k == s ? R[d][t][mt] * kOut : v[kb][d][t][mt];
       }
+    }
   }
 #pragma unroll
   for (int t = 0; t < T; ++t) {

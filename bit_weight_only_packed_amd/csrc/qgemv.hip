@@ -337,6 +337,12 @@ size_t partial_need(const qg_plan* h, int S, int M, int nd) {
   return S <= 1 ? 0 : (size_t)nd * S * M * (size_t)(16 * h->total_tiles);
 }
 
+// the verify GEMM's partials: per (tile group, slice, matrix) a block of T * MT
+// quarter tiles of 64 lanes x 4 fp32
+size_t xs_partial_need(const XsPlan& p, int nd) {
+  return p.S <= 1 ? 0 : (size_t)nd * p.S * (size_t)p.tg_prefix[MAX_SEG] * p.T * p.MT * 256;
+}
+
 // M = 1 K slices of one matrix meet in fixed-point words unless pinned to partials
 bool m1_fx(const qg_plan* h, int S) { return S > 1 && S <= 63 && !(h->pins & QG_PIN_PARTIALS); }
 
@@ -355,7 +361,7 @@ qg_status size_workspace(qg_plan* h, size_t* floats) {
       const XsPlan p = xs_plan(h, M, dual, xsc);
       if (p.NQ == 0 || p.lds > kLdsMax)
         return fail(QG_ERR_INVALID_ARG, "verify GEMM: an x slice of %d quads at M=%d does not fit LDS", p.nq, M);
-      if (!p.fx) need = std::max(need, partial_need(h, p.S, M, dual ? 2 : 1));
+      if (!p.fx) need = std::max(need, xs_partial_need(p, dual ? 2 : 1));
     }
   *floats = need;
   return QG_OK;
@@ -691,7 +697,7 @@ qg_status run_xs(const qg_plan* h, const Work& w, const qg_plan* h2, const uint1
   const XsPlan p = xs_plan(h, M, dual, xsc);
   if (p.NQ == 0 || p.lds > kLdsMax)
     return fail(QG_ERR_INVALID_ARG, "x slice of %d quads at M=%d does not fit LDS", p.nq, M);
-  if (!p.fx && partial_need(h, p.S, M, dual ? 2 : 1) > w.partial_floats)
+  if (!p.fx && xs_partial_need(p, dual ? 2 : 1) > w.partial_floats)
     return fail(QG_ERR_INVALID_ARG, "workspace too small for %d K-slices at M=%d", p.S, M);
   if ((size_t)p.tg_prefix[MAX_SEG] > w.ncounters) return fail(QG_ERR_INVALID_ARG, "more tile groups than counters");
   XsArgs a{};
@@ -804,7 +810,7 @@ Work run_need(const qg_plan* h, int M) {
   }
   const XsPlan p = xs_plan(h, M, false, false);
   if (p.fx) n.acc64_words = (size_t)M * NP;
-  else n.partial_floats = partial_need(h, p.S, M, 1);
+  else n.partial_floats = xs_partial_need(p, 1);
   return n;
 }
 
