@@ -86,7 +86,6 @@ template <int B, int T, int MT, int ND, bool XSC, bool SQ, bool MX>
 __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* const (&xa)[MT][4], const float* xsum,
                                         const float* xfac, int gl0, int ngr, int lane, f4_t (&R)[ND][T][MT]) {
   const int kq = lane >> 4;
-  const float ko = off1_ko<B>();  // -o * 2^-23
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
     if (gi >= ngr) break;
@@ -98,7 +97,7 @@ __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* c
 #pragma unroll
       for (int v = 0; v < 4; ++v) A[mt][v] = *reinterpret_cast<const h8_t*>(xa[mt][v] + gl * 256);
       // chain start: rows 16 mt + 4 kq + e (sums past M are never stored either)
-      if constexpr (!SQ) C0[mt] = *reinterpret_cast<const f4_t*>(xsum + gl * (16 * MT) + 16 * mt + 4 * kq) * ko;
+      if constexpr (!SQ) C0[mt] = *reinterpret_cast<const f4_t*>(xsum + gl * (16 * MT) + 16 * mt + 4 * kq);
       if constexpr (XSC) F[mt] = *reinterpret_cast<const f4_t*>(xfac + gl * (16 * MT) + 16 * mt + 4 * kq);
     }
     if constexpr (MX) {
@@ -268,17 +267,19 @@ __device__ __forceinline__ void xs_body(const XsArgs& a, const SegDev (&sd)[2], 
   // ---- group sums of x on the matrix cores: group gl's A fragments against
   // an all-ones B operand, chained over the group's four 32-k blocks like the
   // products; lane (kq, n) gets the sums of rows 16 mt + 4 kq + e in every
-  // column n, and the lanes of column 0 store them.  A row's sum depends on
-  // that row's values only, so it rounds the same at every row count.
+  // column n, and the lanes of column 0 store them times -o * 2^-23 (the
+  // chain start of the group's products).  A row's sum depends on that row's
+  // values only, so it rounds the same at every row count.
   if constexpr (!SQ) {
     const h8_t ones = as_h8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+    const float ko = off1_ko<B>();  // -o * 2^-23
     for (int gl = wave; gl < 4 * nq; gl += NW) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f4_t cc = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int v = 0; v < 4; ++v) cc = mfma16(*reinterpret_cast<const h8_t*>(xa[mt][v] + gl * 256), ones, cc);
-        if ((lane & 15) == 0) *reinterpret_cast<f4_t*>(xsum + gl * (16 * MT) + 16 * mt + 4 * (lane >> 4)) = cc;
+        if ((lane & 15) == 0) *reinterpret_cast<f4_t*>(xsum + gl * (16 * MT) + 16 * mt + 4 * (lane >> 4)) = cc * ko;
       }
     }
   }

@@ -322,12 +322,11 @@ XsPlan xs_plan(const qg_plan* h, int M, bool dual, bool xsc) {
   }
   p.grid = (unsigned)wgs * (unsigned)p.S;
   p.lds = xs_lds_bytes(M, p.MT, p.NQ, p.GPW, p.T, xsc);
-  // fixed-point words when the atomics are few (measured: they win at 8 rows
-  // on every decode shape, the partials at 32 rows on the widest), or when many
-  // slices would make the last one read its partials in several round trips
-  // (measured: down at 24-32 rows, 9 slices, gains; gate/up, 3 slices, loses)
+  // fixed-point words when the atomics are few (measured: they win at 8 and 16
+  // rows on every decode shape, the partial blocks at 32 rows on gate/up and
+  // down -- down at 32 rows 22.9 -> 20.6 us with 9 slices)
   const int64_t atomics = (int64_t)Mp * 16 * h->total_tiles * p.S;
-  p.fx = p.S > 1 && p.S <= 63 && (atomics <= (int64_t)1 << 20 || (p.S >= 6 && atomics <= (int64_t)1 << 22));
+  p.fx = p.S > 1 && p.S <= 63 && atomics <= (int64_t)1 << 20;
   if (h->pins & QG_PIN_PARTIALS) p.fx = false;
   if (h->pins & QG_PIN_WORDS) p.fx = p.S > 1 && p.S <= 63;
   return p;
