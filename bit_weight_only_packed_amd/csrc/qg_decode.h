@@ -157,28 +157,15 @@ typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u3_t __attribute__((ext_vector_type(3)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
-// B words at byte offset voff + soff of the resource (voff per lane, soff uniform)
-template <int B>
-__device__ __forceinline__ void buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t (&w)[B]) {
-  if constexpr (B == 2) {
-    const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-    w[0] = v.x; w[1] = v.y;
-  } else if constexpr (B == 3) {
-    const u3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z;
-  } else {
-    const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  }
-}
-
 // A lane's quad (4 groups, 4*B words) through a buffer resource whose byte 0 is
-// part 0 of the wave's first quad; `qu` is the quad index relative to it.
+// part 0 of the wave's first quad; `qu` is the quad index relative to it.  The
+// whole byte offset goes into the per-lane offset, which the range check of a
+// raw buffer access covers, so a quad past the resource's range reads nothing.
 template <int B>
 __device__ __forceinline__ void buffer_quad(__amdgpu_buffer_rsrc_t r, uint32_t lane, int qu, uint32_t (&w)[4 * B]) {
 #pragma unroll
   for (int p = 0; p < B; ++p) {
-    const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, (uint32_t)(qu * B + p) * 1024u, 0);
+    const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u + (uint32_t)(qu * B + p) * 1024u, 0, 0);
     w[4 * p + 0] = v.x; w[4 * p + 1] = v.y; w[4 * p + 2] = v.z; w[4 * p + 3] = v.w;
   }
 }
@@ -251,19 +238,6 @@ __device__ __forceinline__ void decode_group_classes(const uint32_t (&w)[4 * B],
 __device__ __forceinline__ size_t code_word_index(int t, int G4, int g, int lane, int u, int B) {
   const int qu = g >> 2, wi = (g & 3) * B + u;  // word within the lane's quad
   return ((((size_t)t * G4 + qu) * B + (wi >> 2)) * 64 + lane) * 4 + (wi & 3);
-}
-
-template <int B> __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[B]) {
-  if constexpr (B == 2) {
-    uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
-  } else if constexpr (B == 3) {
-    // 12-byte aligned-to-4 load
-    w[0] = p[0]; w[1] = p[1]; w[2] = p[2];
-  } else {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  }
 }
 
 }  // namespace qg

@@ -69,7 +69,7 @@ __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, 
     const uint32_t slane = scale_lane_byte(sq, (uint32_t)lane);
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, slane, (uint32_t)u * sqb, 0);
+      const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, slane + (uint32_t)u * sqb, 0, 0);
       sc[u] = make_uint2(v.x, v.y);
       buffer_quad<B>(rc, (uint32_t)lane, u, cw[u]);
     }
