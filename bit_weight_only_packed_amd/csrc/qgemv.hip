@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -1079,6 +1080,17 @@ namespace {
 constexpr size_t kPrefillGemmWs = (size_t)32 << 20;  // hipBLASLt workspace at the front of the caller's
 }
 
+// Rows up to which qgemv_run_prefill runs the verify GEMM in chunks of up to
+// 32 rows instead of dequantising the matrix: measured on MI355X (3-bit,
+// group 128), the chunks win up to 192 rows on 5120x17408, 256 on 17408x5120,
+// 128 on 5120x5120 and 64 on 5120x1024 -- the dequantisation's fixed cost
+// grows with the matrix, a chunk's cost with its bytes.  32 rows per 1280 of
+// sqrt(N K), at most 256; 0 below about 1.6 M weights.
+static int prefill_chunk_rows(const qg_plan* h) {
+  const int c = (int)(std::sqrt((double)h->N * (double)h->K) / 1280.0);
+  return 32 * std::min(c, 8);
+}
+
 qg_status qgemv_prefill_workspace(qg_handle h, size_t* min_bytes, size_t* full_bytes) {
   g_err.clear();
   if (!h || !min_bytes || !full_bytes) return fail(QG_ERR_INVALID_ARG, "NULL argument");
@@ -1105,6 +1117,20 @@ qg_status qgemv_run_prefill(qg_handle h, const uint16_t* x, int32_t M, uint16_t*
   QG_HIP(hipGetDevice(&dev));
   if (dev != h->device) return fail(QG_ERR_INVALID_ARG, "the handle lives on device %d, the current one is %d", h->device, dev);
   hipStream_t st = (hipStream_t)stream;
+  // below the crossover: the verify GEMM, 32 rows (or the handle's max_M of at
+  // least 16) at a time, on the handle's own workspace; the caller's is unused
+  const int cm = std::min(32, h->max_M);
+  if (cm >= 16 && M <= prefill_chunk_rows(h)) {
+    for (int r0 = 0; r0 < M; r0 += cm) {
+      const int m = std::min(cm, M - r0);
+      const uint16_t* xr = x + (size_t)r0 * h->K;
+      uint16_t* yr = y + (size_t)r0 * h->N;
+      const qg_status r = (m == 1 && !invariant(h)) ? run_m1(h, h->ws, nullptr, xr, false, yr, false, st)
+                                                   : run_xs(h, h->ws, nullptr, xr, nullptr, m, yr, false, h->N, st);
+      if (r != QG_OK) return r;
+    }
+    return QG_OK;
+  }
   const size_t row = (size_t)h->K * sizeof(uint16_t);
   const int nc = (int)std::min<size_t>((size_t)h->N, (ws_bytes - kPrefillGemmWs) / row) / 16 * 16;
   uint16_t* wbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kPrefillGemmWs);

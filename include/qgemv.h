@@ -236,11 +236,17 @@ qg_status qgemv_run_noalloc(qg_handle h, const uint16_t* x, int32_t M, uint16_t*
 qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t* x, int32_t M, uint16_t* out,
                    void* stream);
 
-/* Prefill-size products (any M >= 1; the route pays off from tens of rows up):
- * y = x * W^T by the route the pages give for prompt processing ("The Rock8",
- * "Per-format hipBLASLt routes" and the route-crossover paragraph): the
- * weights are dequantised to fp16 -- each w = (c - o) * s rounded once (RNE)
- * -- and multiplied by a plain fp16 GEMM with fp32 accumulation (hipBLASLt).
+/* Prefill-size products (any M >= 1): y = x * W^T, with the route chosen by
+ * row count as the pages describe for prompt processing ("The Rock8",
+ * "Per-format hipBLASLt routes" and the route-crossover paragraph, which
+ * moves with the model shape).  Above the crossover the weights are
+ * dequantised to fp16 -- each w = (c - o) * s rounded once (RNE) -- and
+ * multiplied by a plain fp16 GEMM with fp32 accumulation (hipBLASLt).  Up to
+ * it -- 32 rows per 1280 of sqrt(N K), at most 256 rows (measured on the
+ * 27B-class shapes: 192 rows on 5120x17408, 256 on 17408x5120, 128 on
+ * 5120x5120, 64 on 5120x1024; none below about 1.6 M weights) -- the rows go
+ * through the verify GEMM of qgemv_run, 32 at a time (max_M of at least 16
+ * at a time), on the handle's own workspace and without rounding the weights.
  * x: device fp16 [M][K]; y: device fp16 [M][N]; both 16-byte aligned.
  * workspace: device, 256-byte aligned, ws_bytes long, caller-owned: its first
  * 32 MiB are the GEMM's workspace, the rest holds fp16 weight rows of a chunk
@@ -250,8 +256,10 @@ qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t*
  * Enqueues on `stream` and returns; allocates no device memory.  The first
  * call on a device creates the library's hipBLASLt handle, and the first call
  * for a problem shape plans it (host work; warm a shape before capturing it).
- * UNIFORM handles only (QG_ERR_UNSUPPORTED otherwise); errors of the GEMM
- * return QG_ERR_DEVICE with hipBLASLt's reason. */
+ * The chunked rows use the handle's workspace, so calls on one handle are
+ * ordered like qgemv_run's.  UNIFORM and MXFP4 handles (QG_ERR_UNSUPPORTED
+ * otherwise); errors of the GEMM return QG_ERR_DEVICE with hipBLASLt's
+ * reason. */
 qg_status qgemv_run_prefill(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* workspace, size_t ws_bytes,
                             void* stream);
 

@@ -122,3 +122,26 @@ def test_bad_arguments():
     t = Q.QLinear(dtw, dev_f16(S.scales(64, 256, cfg_id=185)), 256, 64, trellis=True, codebook=cbk, max_M=8)
     with pytest.raises(Q.QGError):
         t.prefill_workspace()
+
+
+@pytest.mark.parametrize("N,K,M", [(17408, 5120, 64), (5120, 5120, 100), (5120, 17408, 33)])
+def test_chunked_rows_below_the_crossover(N, K, M):
+    """Up to the crossover (32 rows per 1280 of sqrt(N K)) the rows run as the
+    verify GEMM, 32 at a time: the result equals qgemv_run on each 32-row
+    block bit for bit (the last block ragged), matches the oracle on sampled
+    columns, and leaves the caller's workspace untouched."""
+    m = Uniform(N, K, 3, cfg_id=185, tid=M)
+    x_np = S.activations(M, K, cfg_id=185, tensor_id=M)
+    x = dev_f16(x_np)
+    lo, _ = m.lin.prefill_workspace()
+    ws = torch.full((lo,), 0x5A, dtype=torch.uint8, device="cuda")
+    say("chunked prefill", N, K, M)
+    y = m.lin.run_prefill(x, workspace=ws)
+    parts = [m.lin.run(x[r0:r0 + 32]) for r0 in range(0, M, 32)]
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), torch.cat(parts).view(torch.int16))
+    assert bool((ws == 0x5A).all())
+    rows = np.random.default_rng(M).choice(N, 64, replace=False)
+    err = O.normwise_rel_err(y.cpu().numpy().astype(np.float64)[:, rows], m.ref(x_np, rows))
+    say("err", err)
+    assert err <= TOL, err
