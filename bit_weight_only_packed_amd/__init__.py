@@ -29,7 +29,7 @@ FLAG_BATCH_INVARIANT = 2
 GROUP = 128
 # pins (include/qgemv.h): force a kernel or hand-over
 PIN_M1_PERGROUP, PIN_M1_RUNS, PIN_PARTIALS, PIN_WORDS = 1 << 0, 1 << 1, 1 << 2, 1 << 3
-PIN_XS_T1, PIN_XS_T2, PIN_TRELLIS_ROT_LAUNCH = 1 << 4, 1 << 5, 1 << 6
+PIN_XS_T1, PIN_XS_T2, PIN_TRELLIS_ROT_LAUNCH, PIN_TRELLIS_BAND = 1 << 4, 1 << 5, 1 << 6, 1 << 7
 
 
 class QGError(RuntimeError):

@@ -18,6 +18,11 @@ hipError_t launch_trellis_band(const TbArgs& a, int MT, unsigned grid, hipStream
   return hipGetLastError();
 }
 
+hipError_t launch_trellis_bx(const TbArgs& a, unsigned grid, hipStream_t st) {
+  k_trellis_bx<<<grid, 64 * TbShape<1>::NW, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwht(const uint16_t* x, uint16_t* xr, int M, int K, hipStream_t st) {
   const int waves = M * (K / 128);
   k_fwht<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, xr, M, K);

@@ -143,6 +143,12 @@ template <int MT> struct TbShape {
   static constexpr int SLOT = MR * 256;        // bytes per x slot
 };
 
+// trellis GEMM for 2..8 rows with the K slice's x in LDS beside the codebook
+constexpr int TBX_MAXM = 8;                           // rows
+constexpr int TBX_XBYTES = 160 * 1024 - TR_CB_BYTES;  // LDS for the slice of x: 128 (group, row) pieces
+constexpr int TBX_XPW = TBX_XBYTES / 256 / 16;        // pieces per wave (16 waves)
+constexpr int TBX_PD = 3;                             // groups whose code loads are in flight
+
 struct TbArgs {
   const uint32_t* codes;   // [U][64][3]
   const uint16_t* scales;  // [U][16]

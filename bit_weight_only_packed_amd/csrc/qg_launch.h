@@ -29,6 +29,7 @@ hipError_t xs2_allow_lds();
 // trellis (k_trellis.hip)
 hipError_t launch_trellis_gemv(const TrArgs& a, bool xl, unsigned grid, hipStream_t st);
 hipError_t launch_trellis_band(const TbArgs& a, int MT, unsigned grid, hipStream_t st);
+hipError_t launch_trellis_bx(const TbArgs& a, unsigned grid, hipStream_t st);  // 2..8 rows, x slice staged once
 hipError_t launch_fwht(const uint16_t* x, uint16_t* xr, int M, int K, hipStream_t st);
 hipError_t launch_repack_trellis(const uint16_t* tiles, const uint16_t* scales, int KT, int G, int64_t units,
                                  uint32_t* dcodes, uint16_t* dscales, hipStream_t st);

@@ -595,6 +595,166 @@ __global__ __launch_bounds__(64 * TbShape<MT>::NW) void k_trellis_band(TbArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Trellis GEMM for 2..8 rows with the K slice's x staged once: a workgroup
+// of 16 waves (one row block each, as k_trellis_band) copies the codebook and
+// its slice of x -- each (group, row) piece rotated by one wave in registers
+// unless x comes rotated -- into LDS behind one barrier; then each wave walks
+// its row block's groups on its own, with the code loads of the next TBX_PD
+// groups in flight.  No workgroup barrier per group, so the waves' gathers and
+// matrix-core work spread over the launch instead of meeting in lockstep.  The
+// slice of x takes M * (groups) * 256 bytes beside the 128 KiB codebook: at
+// most TBX_XBYTES, TBX_XPW pieces per wave.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * TbShape<1>::NW) void k_trellis_bx(TbArgs a) {
+  constexpr int NW = TbShape<1>::NW, PD = TBX_PD;
+  __shared__ __align__(16) char smem[TR_CB_BYTES + TBX_XBYTES];
+  char* const xs = smem + TR_CB_BYTES;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = a.S, M = a.M;
+  const int s = blockIdx.x % S, band = blockIdx.x / S;
+  const int rb = band * NW + wave;
+  const bool mine = rb < a.RB;
+  const int g0 = (int)((int64_t)s * a.G / S), g1 = (int)((int64_t)(s + 1) * a.G / S), ng = g1 - g0;
+  // codebook -> LDS (1 KiB per wave instruction)
+  {
+    const __amdgpu_buffer_rsrc_t rcb = make_rsrc(uniform_ptr(a.cb), TR_CB_BYTES);
+    for (int ci = wave; ci < TR_CB_BYTES / 1024; ci += NW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rcb, (__attribute__((address_space(3))) void*)(smem + (size_t)ci * 1024),
+                                               16, (uint32_t)(ci * 1024 + lane * 16), 0, 0, 0);
+  }
+  auto load_unit = [&](TbUnit& t, int i) {
+    const bool live = mine && i < ng;
+    const int64_t u = live ? (int64_t)rb * a.G + g0 + i : 0;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(uniform_ptr(a.codes) + u * 192, live ? 768u : 0u);
+    t.z = __builtin_amdgcn_raw_buffer_load_b96(rc, (uint32_t)lane * 12u, 0, 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(a.scales) + u * 16, live ? 32u : 0u);
+    t.s = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(lane & 14) * 2u, 0, 0);
+  };
+  TbUnit c[PD];
+#pragma unroll
+  for (int i = 0; i < PD; ++i) load_unit(c[i], i);
+  // the slice of x: piece (group i, row m) holds the group's 128 values of
+  // row m, lane l holding values 2l and 2l + 1 (the pairing k_trellis_band
+  // rotates), at xs + (i * M + m) * 256 with the 16-byte chunk p at position
+  // p ^ (m & 15); this wave takes pieces wave, wave + 16, ...
+  {
+    const int np = M * ng;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(a.x), (uint32_t)M * a.K * 2u);
+    uint32_t xv[TBX_XPW];
+#pragma unroll
+    for (int j = 0; j < TBX_XPW; ++j) {
+      const int pc = wave + NW * j, i = pc / M, m = pc - i * M;
+      const uint32_t voff = pc < np ? (uint32_t)(((size_t)m * a.K + (size_t)(g0 + i) * 128 + 2 * lane) * 2) : 0xFFFFFFF0u;
+      xv[j] = __builtin_amdgcn_raw_buffer_load_b32(rx, voff, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < TBX_XPW; ++j) {
+      const int pc = wave + NW * j, i = pc / M, m = pc - i * M;
+      if (pc >= np) break;  // uniform across the wave
+      uint32_t out = xv[j];
+      if (a.rot) {
+        float p0 = h2f((uint16_t)(out & 0xFFFFu)), p1 = h2f((uint16_t)(out >> 16));
+        const float sum = p0 + p1, dif = p0 - p1;
+        p0 = sum;
+        p1 = dif;
+        fwht_lanes(p0, p1, lane);
+        const float f = 0.08838834764831845f;  // 2^-3.5
+        out = (uint32_t)f2h(p0 * f) | ((uint32_t)f2h(p1 * f) << 16);
+      }
+      const int ch = (lane >> 2) ^ (m & 15);
+      *reinterpret_cast<uint32_t*>(xs + (size_t)pc * 256 + ch * 16 + (lane & 3) * 4) = out;
+    }
+  }
+  tb_vm_wait<0>();  // the codebook copies (and the first units) have landed
+  __syncthreads();  // every wave's codebook part and x pieces are in LDS
+  if (!mine) return;
+  const char* cbl = smem;
+  const int kq = lane >> 4, m16 = lane & 15;
+  int xa[4];  // this lane's A-fragment offsets within a group's pieces (rows past M repeat row M - 1)
+  {
+    const int row = min(m16, M - 1);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xa[v] = row * 256 + (((4 * kq + v) ^ (row & 15)) * 16);
+  }
+  f4_t acc = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // one group: its codes (loaded PD groups ahead: every group issues the same
+  // two loads, past the slice through empty ranges, so the wait count is the
+  // same in every group), gathers, four MFMAs against the staged x, then the
+  // loads of group i + PD into the freed register set
+  auto step = [&](TbUnit& cu, int i) {
+    tb_vm_wait<2 * (PD - 1)>();
+    if (i < ng) {
+      const uint32_t z2 = cu.z.x, z1 = cu.z.y, z0 = cu.z.z;
+      const uint32_t nz2 = tr_from_next_row_lane(z2), nz1 = tr_from_next_row_lane(z1);
+      uint32_t addr[32];
+      tr_addrs(z2, z1, z0, nz2, nz1, addr);
+      uint32_t pr[16];
+      tr_gather(cbl, addr, pr);
+      const float sc = h2f((uint16_t)((lane & 1) ? (cu.s >> 16) : (cu.s & 0xFFFFu)));
+      const char* xg = xs + (size_t)i * M * 256;
+      f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        cg = mfma16(*reinterpret_cast<const h8_t*>(xg + xa[v]), as_h8(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]), cg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, cg[e], acc[e]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_unit(cu, i + PD);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int u = 0; u < ng; u += PD) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) step(c[i], u + i);
+  }
+  tb_vm_wait<0>();  // the loads past the slice (empty ranges) retire
+  // ---- results of this row block over the slice (as k_trellis_band)
+  const int n = lane & 15, mq = lane >> 4;
+  if (S == 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * mq + e;
+      if (m < M) a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(acc[e]);
+    }
+    return;
+  }
+  if (a.acc) {
+    unsigned long long mw[4], before[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * mq + e;
+      mw[e] = fx_word(acc[e]);
+      before[e] = m < M ? fx_add(a.acc + (size_t)m * a.N + (size_t)rb * 16 + n, mw[e]) : 0ull;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * mq + e;
+      if (m >= M || fx_count(before[e]) != S - 1) continue;
+      unsigned long long* w = a.acc + (size_t)m * a.N + (size_t)rb * 16 + n;
+      a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(fx_value(before[e] + mw[e]));
+      fx_rearm(w);
+    }
+    return;
+  }
+  float* base = a.partial + ((size_t)rb * a.maxseg) * M * 16;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m = 4 * mq + e;
+    if (m < M) st_partial(base + ((size_t)s * M + m) * 16 + n, acc[e]);
+  }
+  if (tr_arrive_last(a.counters + rb, S, lane)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * mq + e;
+      if (m >= M) continue;
+      const float t = sum_partials(base + (size_t)m * 16 + n, (size_t)M * 16, S, s, acc[e]);
+      a.y[(size_t)m * a.N + (size_t)rb * 16 + n] = f2h(t);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // checking kernel: states (and cb[state] * s in fp32) of every weight, through
 // the same decode as the run kernels.  One wave per unit.
 // ---------------------------------------------------------------------------

@@ -455,6 +455,15 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   return QG_OK;
 }
 
+// 2..8 rows: the banded GEMM that stages its K slice's x once (and rotates
+// it there) where M x (groups per slice) pieces of 256 bytes fit beside the
+// codebook; the band kernel's K slices, so the workspace is the same
+bool trellis_bx(const qg_plan* h, int M) {
+  if (M < 2 || M > TBX_MAXM || (h->pins & QG_PIN_TRELLIS_BAND)) return false;
+  const int S = tb_slices(h, TbShape<1>::NW);
+  return (int64_t)M * ((h->G + S - 1) / S) <= TBX_XBYTES / 256;
+}
+
 // M = 1 GEMV that rotates x itself into LDS (no separate rotation launch):
 // room for the rotated x beside the codebook up to K = 16384
 // x rotated inside the run kernel.  2..32 rows: each band workgroup rotates the
@@ -464,6 +473,7 @@ qg_status create_trellis(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
 // 35.1 -> 35.9, where one rotation launch is cheaper.  One row: where the
 // rotated x fits the GEMV's LDS.
 bool trellis_xl(const qg_plan* h, int M) {
+  if (trellis_bx(h, M)) return !(h->flags & QG_FLAG_X_PREROTATED);
   if (M > 1) {
     const int nw = M > 16 ? TbShape<2>::NW : TbShape<1>::NW;
     const int64_t bands = (h->N / 16 + nw - 1) / nw;
@@ -507,6 +517,7 @@ qg_status run_trellis(const qg_plan* h, const Work& w, const uint16_t* x, int M,
     const bool fx = b.S > 1 && b.S <= 63 && (int64_t)M * h->N * b.S <= (1 << 20) && !(h->pins & QG_PIN_PARTIALS);
     b.acc = fx ? w.acc64 : nullptr;
     const unsigned grid = (unsigned)(((b.RB + nw - 1) / nw) * b.S);
+    if (trellis_bx(h, M)) return after_launch(h, launch_trellis_bx(b, grid, st), st);
     return after_launch(h, launch_trellis_band(b, MT, grid, st), st);
   }
   TrArgs a{};

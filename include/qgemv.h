@@ -129,7 +129,10 @@ enum {
                                    at most 63 slices meet                                            */
   QG_PIN_XS_T1 = 1u << 4,       /* UNIFORM, M >= 2: one 16-column tile per tile group               */
   QG_PIN_XS_T2 = 1u << 5,       /* UNIFORM, M >= 2: two tiles per tile group                        */
-  QG_PIN_TRELLIS_ROT_LAUNCH = 1u << 6 /* TRELLIS3, M = 1: rotate x in a launch of its own            */
+  QG_PIN_TRELLIS_ROT_LAUNCH = 1u << 6, /* TRELLIS3, M = 1: rotate x in a launch of its own           */
+  QG_PIN_TRELLIS_BAND = 1u << 7 /* TRELLIS3, 2..8 rows: the band kernel that stages x group by group
+                                   behind a workgroup barrier (default: the K slice's x staged once,
+                                   where it fits in LDS)                                            */
 };
 
 enum { QG_GROUP = 128, QG_MAX_M = 32 };

@@ -172,3 +172,34 @@ def test_gemv_rotation_in_kernel(N, K, codebook):
         err = O.normwise_rel_err(y_kernel, t.ref(x))
         say("err", err)
         assert err <= TOL, err
+
+
+@pytest.mark.parametrize("handover", ["words", "partials"])
+@pytest.mark.parametrize("M", [2, 3, 5, 8])
+@pytest.mark.parametrize("N,K", [(48, 128), (48, 384), (400, 2560), (24576, 1280), (5120, 17408)])
+def test_staged_slice_kernel_matches_band(handover, M, N, K, codebook):
+    """2..8 rows: the kernel that stages its K slice's x once (no per-group
+    barrier) gives the same bits as the band kernel (pinned), which stages x
+    group by group, on the same rotated x: both sum the same MFMA products in
+    group order.  With x as given, it rotates x in LDS and matches the oracle.
+    Shapes: one group (a single K slice, direct stores), one group per slice,
+    5 groups per slice (two K slices) and 11 or 12 (12 slices, x slices of up
+    to 96 pieces at 8 rows); the largest checked on sampled row blocks."""
+    hp = Q.PIN_PARTIALS if handover == "partials" else 0
+    x = S.activations(M, K, cfg_id=89, tensor_id=800 + M)
+    xr = O.rotate(x).astype(np.float16)
+    say("trellis staged slice", handover, M, N, K)
+    tp = Trellis(N, K, codebook, cfg_id=89, max_M=8, prerotated=True, pins=hp)
+    tbp = Trellis(N, K, codebook, cfg_id=89, max_M=8, prerotated=True, pins=hp | Q.PIN_TRELLIS_BAND)
+    assert np.array_equal(_run(tp.lin, xr), _run(tbp.lin, xr))
+    del tp, tbp
+    t = Trellis(N, K, codebook, cfg_id=89, max_M=8, pins=hp)
+    y = _run(t.lin, x)
+    if N * K <= (1 << 22):
+        err = O.normwise_rel_err(y, t.ref(x))
+    else:
+        blocks = np.unique(np.concatenate([[0, N // 16 - 1], np.random.default_rng(9).choice(N // 16, 4, replace=False)]))
+        rows = (16 * blocks[:, None] + np.arange(16)[None, :]).reshape(-1)
+        err = O.normwise_rel_err(y[:, rows], O.gemv_trellis_rows(x, t.words, t.cb, t.scales, N, K, rows))
+    say("err", err)
+    assert err <= TOL, err
