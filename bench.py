@@ -726,12 +726,12 @@ def cpu_baseline():
     # tiny reference (all of it)
     r, nb = uniform_case(512, 512, (1,), 512, cfg=S.CFG_TINY)
     report["tiny_512x512"] = fmt(r, nb)
-    # decode and verify: the four distinct layer shapes, 512 sampled columns each
+    # decode and verify: the four distinct layer shapes, 8192 sampled columns each
     ls_us = {M: 0.0 for M in (1, 8, 16, 32)}
     ls_bytes = 0
     for name, (K, N, mult) in {"qo": (5120, 5120, 2), "kv": (5120, 1024, 2), "gateup": (5120, 17408, 2),
                                "down": (17408, 5120, 1)}.items():
-        r, nb = uniform_case(N, K, (1, 8, 16, 32), 2048)
+        r, nb = uniform_case(N, K, (1, 8, 16, 32), 8192)
         report[name] = fmt(r, nb)
         ls_bytes += mult * nb
         for M, (dq, mm) in r.items():
@@ -739,11 +739,11 @@ def cpu_baseline():
     report["layer_set"] = {f"M{M}": {"us": round(v, 1), "weight_GBs": round(ls_bytes / v / 1e3, 4)}
                            for M, v in ls_us.items()}
     # fused MLP (mixed widths counted at 3 bits: the oracle's work per weight is the same)
-    gu, nbg = uniform_case(17408, 5120, (1, 8, 32), 1024, tid=1)
-    dn, nbd = uniform_case(5120, 17408, (1, 8, 32), 1024, tid=2)
+    gu, nbg = uniform_case(17408, 5120, (1, 8, 32), 4096, tid=1)
+    dn, nbd = uniform_case(5120, 17408, (1, 8, 32), 4096, tid=2)
     report["mlp"] = {f"M{M}": {"us": round(2 * sum(gu[M]) + sum(dn[M]), 1)} for M in (1, 8, 32)}
     # trellis, gate/up shape
-    r, nb = trellis_case(17408, 5120, (1, 8), 512)
+    r, nb = trellis_case(17408, 5120, (1, 8), 2048)
     report["trellis_gateup"] = fmt(r, nb)
     t_all = time.perf_counter() - t_start
     # one thread: the layer set at M = 1
@@ -753,15 +753,15 @@ def cpu_baseline():
             us1 = 0.0
             for name, (K, N, mult) in {"qo": (5120, 5120, 2), "kv": (5120, 1024, 2), "gateup": (5120, 17408, 2),
                                        "down": (17408, 5120, 1)}.items():
-                r, nb = uniform_case(N, K, (1,), 1024)
+                r, nb = uniform_case(N, K, (1,), 2048)
                 us1 += mult * sum(r[1])
         one = {"us": round(us1, 1), "weight_GBs": round(ls_bytes / us1 / 1e3, 4)}
     v = ls_bytes / ls_us[1] / 1e3
     log(f"cpu oracle: layer set M=1 {ls_us[1]:.0f} us = {v:.3f} GB/s ({cores} threads), 1 thread "
         f"{one}; sampled in {t_all:.1f} s")
     return {"value": round(v, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "the first 2048 output columns of each distinct 27B-class layer shape (1024 at one thread "
-                      "and for the MLP, 512 rows of the trellis shape), scaled to whole matrices; the value is the "
+            "sample": "the first 8192 output columns of each distinct 27B-class layer shape (all 5120 or 1024 "
+                      "where it has fewer; 2048 at one thread, 4096 for the MLP, 2048 rows of the trellis shape), scaled to whole matrices; the value is the "
                       "layer set q,k,v,o,gate,up,down at M=1",
             "seconds": round(t_all, 1), "one_thread_layer_set_M1": one, "per_workload": report}
 
