@@ -41,6 +41,14 @@ bit layout, so the conventions below are this library's, stated once here:
   w = e2m1(c) * 2**(e - 127).  E2M1 read as a binary float with exponent bias
   1: sign bit 3, exponent bits 2..1, mantissa bit 0; exponent 0 is subnormal
   (0.5 * m).  E8M0 = 255 is NaN.
+* MXFP6 ("The Rock8", format table, MXFP6 row: blocks of 32 elements in 25
+  bytes, OCP E3M2 leaves -- 3 exponent bits, 2 mantissa bits -- four values per
+  three bytes, one UE8M0 scale byte per block): element codes in the 6-bit
+  canonical stream (the uniform stream above with b = 6: 24 words per row and
+  group, element j at stream bits [6j, 6j + 6), so bytes 3i..3i+2 hold elements
+  4i..4i+3), scales uint8 [N][K/32]; w = e3m2(c) * 2**(e - 127).  E3M2 read as
+  a binary float with exponent bias 3: sign bit 5, exponent bits 4..2, mantissa
+  bits 1..0; exponent 0 is subnormal (m / 16); no infinities or NaN.
 
 All floating point is fp64 and no intermediate is rounded.  Dequantised weights
 are exact (fp16 scale times a code offset has at most 15 significant bits), and
@@ -69,7 +77,7 @@ def _stream_bits_lsb(words: np.ndarray) -> np.ndarray:
 
 def unpack_uniform(words: np.ndarray, N: int, K: int, bits: int) -> np.ndarray:
     """Canonical packed stream -> codes int64[N][K] (every column ``bits`` wide)."""
-    assert K % GROUP == 0 and bits in (2, 3, 4)
+    assert K % GROUP == 0 and bits in (2, 3, 4, 6)
     G = K // GROUP
     words = np.asarray(words, dtype=np.uint32).reshape(-1)
     assert words.size == N * G * 4 * bits
@@ -216,6 +224,37 @@ def gemv_mxfp4(x, words, e8, N: int, K: int, rows=None) -> np.ndarray:
     words = np.asarray(words, dtype=np.uint32).reshape(N, -1)
     codes = unpack_uniform(words[rows].reshape(-1), len(rows), K, 4)
     return matmul(x, dequant_mxfp4(codes, np.asarray(e8).reshape(N, -1)[rows]))
+
+
+# ---------------------------------------------------------------------------
+# MXFP6: E3M2 elements, UE8M0 block scales (blocks of 32 along k)
+# ---------------------------------------------------------------------------
+def e3m2_value(code: int) -> float:
+    """An E3M2 element: sign bit 5, three exponent bits (bias 3), two mantissa bits."""
+    code = int(code)
+    sign = -1.0 if (code >> 5) & 1 else 1.0
+    e, m = (code >> 2) & 7, code & 3
+    if e == 0:
+        return sign * 2.0 ** (1 - 3) * (m / 4.0)   # subnormal
+    return sign * 2.0 ** (e - 3) * (1.0 + m / 4.0)
+
+
+def dequant_mxfp6(codes: np.ndarray, e8: np.ndarray) -> np.ndarray:
+    """w[n][k] = e3m2(c[n][k]) * 2^(e8[n][k // 32] - 127) in fp64 (exact)."""
+    codes = np.asarray(codes, dtype=np.int64)
+    N, K = codes.shape
+    lut = np.array([e3m2_value(c) for c in range(64)])
+    sc = np.array([e8m0_value(e) for e in range(256)])
+    s = np.repeat(sc[np.asarray(e8, dtype=np.int64).reshape(N, K // MX_BLOCK)], MX_BLOCK, axis=1)
+    return lut[codes] * s
+
+
+def gemv_mxfp6(x, words, e8, N: int, K: int, rows=None) -> np.ndarray:
+    """y = x * dequant(W)^T for MXFP6 weights (optionally some output columns)."""
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    words = np.asarray(words, dtype=np.uint32).reshape(N, -1)
+    codes = unpack_uniform(words[rows].reshape(-1), len(rows), K, 6)
+    return matmul(x, dequant_mxfp6(codes, np.asarray(e8).reshape(N, -1)[rows]))
 
 
 # ---------------------------------------------------------------------------

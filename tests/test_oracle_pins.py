@@ -276,6 +276,84 @@ def test_mxfp4_dequant_blocks_and_brute_force():
 
 
 # ---------------------------------------------------------------------------
+# MXFP6 ("The Rock8", format table: OCP E3M2 leaves, 3 exponent / 2 mantissa
+# bits, four values per three bytes, UE8M0 scale 2^(e-127) per 32 elements,
+# 25 bytes per block)
+# ---------------------------------------------------------------------------
+def test_e3m2_values():
+    vals = [O.e3m2_value(c) for c in range(64)]
+    # the 32 magnitudes of a 3-exponent-bit, 2-mantissa-bit float with bias 3:
+    # exponent 0 subnormal in steps of 1/16, then each binade of four values
+    mags = [Fraction(m, 16) for m in range(4)]
+    for e in range(1, 8):
+        mags += [Fraction(2) ** (e - 3) * (1 + Fraction(m, 4)) for m in range(4)]
+    assert [Fraction(v) for v in vals[:32]] == mags
+    assert vals[31] == 28.0 and vals[1] == 0.0625 and vals[4] == 0.25  # largest, smallest subnormal, smallest normal
+    for c in range(32):
+        assert vals[c | 32] == -vals[c]  # bit 5 only negates (-0 for code 32)
+    assert math.copysign(1.0, vals[32]) == -1.0
+    # binary-float structure: each exponent step doubles, the subnormal step
+    # equals the first normal binade's step, values increase with the code
+    for c in range(4, 28):
+        assert vals[c + 4] == 2 * vals[c]
+    assert vals[1] == vals[5] - vals[4]
+    assert all(vals[c] < vals[c + 1] for c in range(31))
+    # 6 bits per element: 32 elements in 24 bytes plus the scale byte = the
+    # format's 25-byte block
+    assert 32 * 6 // 8 + 1 == 25
+
+
+def test_mxfp6_stream_four_values_per_three_bytes():
+    """Elements 4i..4i+3 of the 6-bit stream fill bytes 3i..3i+2 (LSB first),
+    checked against a Python-integer reference; pack/unpack are inverses."""
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 64, size=(3, 256))
+    words = O.pack_uniform(codes, 6)
+    assert words.size == 3 * 2 * 24
+    raw = np.asarray(words, dtype="<u4").tobytes()
+    for n in range(3):
+        for i in range(64):  # byte triple i of row n
+            v = int.from_bytes(raw[n * 192 + 3 * i: n * 192 + 3 * i + 3], "little")
+            assert [(v >> (6 * j)) & 63 for j in range(4)] == list(codes[n, 4 * i: 4 * i + 4])
+    for n in range(3):
+        for g in range(2):
+            assert bigint_unpack_group(words[(n * 2 + g) * 24:(n * 2 + g + 1) * 24], 6) == list(codes[n, 128 * g: 128 * g + 128])
+    assert np.array_equal(O.unpack_uniform(words, 3, 256, 6), codes)
+
+
+def test_mxfp6_dequant_blocks_and_brute_force():
+    """Each scale byte covers exactly 32 consecutive k of its row; products
+    against exact rationals."""
+    N, K, M = 3, 256, 2
+    rng = np.random.default_rng(6)
+    codes = rng.integers(0, 64, size=(N, K))
+    e8 = rng.integers(118, 132, size=(N, K // 32)).astype(np.uint8)
+    w = O.dequant_mxfp6(codes, e8)
+    base = O.dequant_mxfp6(codes, np.full_like(e8, 127))
+    for n0, i in ((0, 0), (2, 7), (1, 3)):
+        e2 = np.full_like(e8, 127)
+        e2[n0, i] = 126
+        changed = np.argwhere(O.dequant_mxfp6(codes, e2) != base)
+        nz = [k for k in range(i * 32, (i + 1) * 32) if codes[n0, k] & 31]
+        assert sorted(changed[:, 1]) == nz and set(changed[:, 0]) <= {n0}
+    words = O.pack_uniform(codes, 6)
+    x = S.activations(M, K, cfg_id=98)
+    y = O.gemv_mxfp6(x, words, e8, N, K)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(x[m, k])) * Fraction(O.e3m2_value(codes[n, k])) * Fraction(2) ** (int(e8[n, k // 32]) - 127)
+            assert abs(y[m, n] - float(acc)) <= 1e-12 * max(1.0, abs(float(acc)))
+    assert np.all(w == base * np.repeat(2.0 ** (e8.astype(np.float64) - 127), 32, axis=1))
+    # a NaN scale byte makes exactly its block NaN
+    e3 = e8.copy()
+    e3[1, 2] = 255
+    nan = np.isnan(O.dequant_mxfp6(codes, e3))
+    assert nan[1, 64:96].all() and nan.sum() == 32
+
+
+# ---------------------------------------------------------------------------
 # contraction: brute force with exact rationals
 # ---------------------------------------------------------------------------
 def brute_gemv(x16, words, s16, N, K, bits):
