@@ -603,29 +603,31 @@ def main():
             for l in fl:
                 l.close()
             del fl, dwf, dsf
-        # MXFP4 (E2M1 elements, one UE8M0 byte per 32) on the same shape
+        # MXFP4 (E2M1 elements) and MXFP6 (E3M2 elements), one UE8M0 byte per 32, on the same shape
         e8 = S.mx_scales(N, K, cfg_id=S.CFG_DECODE, tensor_id=S.T_SCALE + 600)
-        wb = w4.nbytes + e8.nbytes
-        Rf = int(np.ceil((1 << 30) / wb))
-        dwf, def8 = dw(w4), torch.from_numpy(e8.copy()).to(dev)
-        fl = [Q.QLinear(dwf, def8, K, N, mxfp4=True, max_M=32) for _ in range(Rf)]
-        row = {"weight_bytes": wb, "copies": Rf}
-        for M in (1, 8, 32):
-            xf = xk[(M, K)]
-            out = ys[M][:, :N]
+        w6 = S.uniform_code_words(N, K, 6, cfg_id=S.CFG_DECODE, tensor_id=S.T_CODES + 600)
+        for name, wmx in (("mxfp4", w4), ("mxfp6", w6)):
+            wb = wmx.nbytes + e8.nbytes
+            Rf = int(np.ceil((1 << 30) / wb))
+            dwf, def8 = dw(wmx), torch.from_numpy(e8.copy()).to(dev)
+            fl = [Q.QLinear(dwf, def8, K, N, max_M=32, **{name: True}) for _ in range(Rf)]
+            row = {"weight_bytes": wb, "copies": Rf}
+            for M in (1, 8, 32):
+                xf = xk[(M, K)]
+                out = ys[M][:, :N]
 
-            def f(fl=fl, xf=xf, out=out):
-                for l in fl:
-                    l.run(xf, out=out)
-            us = graph_us(capture(f), Rf, reps=10, trials=3)
-            row[f"us_M{M}"] = round(us, 3)
-            row[f"GBs_M{M}"] = round(wb / us / 1e3, 1)
-        row["ratio_M32_M1"] = round(row["us_M32"] / row["us_M1"], 3)
-        fres["mxfp4"] = row
-        log("mxfp4", row)
-        for l in fl:
-            l.close()
-        del fl, dwf, def8
+                def f(fl=fl, xf=xf, out=out):
+                    for l in fl:
+                        l.run(xf, out=out)
+                us = graph_us(capture(f), Rf, reps=10, trials=3)
+                row[f"us_M{M}"] = round(us, 3)
+                row[f"GBs_M{M}"] = round(wb / us / 1e3, 1)
+            row["ratio_M32_M1"] = round(row["us_M32"] / row["us_M1"], 3)
+            fres[name] = row
+            log(name, row)
+            for l in fl:
+                l.close()
+            del fl, dwf, def8
         result["w4a16_gateup"] = fres
 
     # ---------------- prefill route: dequantise to fp16, then a plain fp16 GEMM ----------------

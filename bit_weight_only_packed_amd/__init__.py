@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qgemv.h")
 
 QG_OK, QG_ERR_INVALID_ARG, QG_ERR_UNSUPPORTED, QG_ERR_DEVICE, QG_ERR_OOM = 0, -1, -2, -3, -4
-FMT_UNIFORM, FMT_TRELLIS3, FMT_MXFP4 = 0, 1, 2
+FMT_UNIFORM, FMT_TRELLIS3, FMT_MXFP4, FMT_MXFP6 = 0, 1, 2, 3
 FLAG_X_PREROTATED = 1
 FLAG_BATCH_INVARIANT = 2
 GROUP = 128
@@ -122,23 +122,25 @@ class QLinear:
     group_size: the scale group, 128 (scales [N][K/128]) or, for uniform
     codes, 64 or 32 (scales [N][K/64] or [N][K/32]).  mxfp4: codes are E2M1
     elements in the 4-bit stream, scales a CUDA uint8 tensor of UE8M0 bytes
-    [N][K/32].
+    [N][K/32].  mxfp6: codes are E3M2 elements in the 6-bit stream, scales as
+    for mxfp4.
     """
 
     def __init__(self, codes, scales, K: int, N: int, bits: int = 3, col_bits=None, max_M: int = 32,
                  trellis: bool = False, codebook=None, prerotated: bool = False, stream=None,
                  pins: int = 0, launch=None, batch_invariant: bool = False, group_size: int = GROUP,
-                 mxfp4: bool = False):
+                 mxfp4: bool = False, mxfp6: bool = False):
         d = _Desc()
-        d.K, d.N, d.group_size = int(K), int(N), 32 if mxfp4 else int(group_size)
-        d.format = FMT_TRELLIS3 if trellis else (FMT_MXFP4 if mxfp4 else FMT_UNIFORM)
+        mx = mxfp4 or mxfp6
+        d.K, d.N, d.group_size = int(K), int(N), 32 if mx else int(group_size)
+        d.format = FMT_TRELLIS3 if trellis else (FMT_MXFP4 if mxfp4 else (FMT_MXFP6 if mxfp6 else FMT_UNIFORM))
         self._cb_host = None
         if not trellis and col_bits is not None:
             self._cb_host = np.ascontiguousarray(np.asarray(col_bits, dtype=np.uint8))
             d.bits = 0
             d.col_bits = self._cb_host.ctypes.data
         else:
-            d.bits = 0 if trellis else (4 if mxfp4 else int(bits))
+            d.bits = 0 if trellis else (4 if mxfp4 else (6 if mxfp6 else int(bits)))
         d.codes = _ptr(codes)
         d.scales = _ptr(scales)
         d.codebook = _ptr(codebook) if codebook is not None else None

@@ -11,12 +11,15 @@ void lq(const GvArgs& a, int NW, size_t lds, unsigned grid, hipStream_t st) {
   k_gemv_q<NQ, BF, XF><<<grid, NW * 64, lds, st>>>(a);
 }
 
-// bf: the single code width, 0 for several, 5 for MXFP4 (fp16 x only)
+// bf: the single code width, 0 for several, 5 for MXFP4, 6 for MXFP6 (fp16 x only)
 template <int NQ, bool XF>
 void lq_b(const GvArgs& a, int NW, size_t lds, unsigned grid, int bf, hipStream_t st) {
   switch (bf) {
     case 5:
       if constexpr (!XF) lq<NQ, 5, XF>(a, NW, lds, grid, st);
+      break;
+    case 6:
+      if constexpr (!XF) lq<NQ, 6, XF>(a, NW, lds, grid, st);
       break;
     case 2: lq<NQ, 2, XF>(a, NW, lds, grid, st); break;
     case 3: lq<NQ, 3, XF>(a, NW, lds, grid, st); break;

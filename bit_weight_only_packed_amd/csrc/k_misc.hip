@@ -23,6 +23,13 @@ hipError_t launch_repack_mx_scales(const uint8_t* e8, const int32_t* cols, int t
   return hipGetLastError();
 }
 
+hipError_t launch_repack_mx6(const uint32_t* canon, const int32_t* cols, int tiles, int G, int G4, uint32_t* dcodes,
+                             hipStream_t st) {
+  const size_t nslot = (size_t)tiles * G4 * 64;
+  k_repack_mx6<<<(unsigned)((nslot + 255) / 256), 256, 0, st>>>(canon, cols, tiles, G, G4, dcodes);
+  return hipGetLastError();
+}
+
 hipError_t launch_debug_uniform(const SegDev& sg, const int32_t* col_map, int G, int G4, int K, int mode,
                                 int32_t* codes, float* w, uint16_t* q16, hipStream_t st) {
   const int64_t n = (int64_t)sg.tiles * G * 64;

@@ -23,6 +23,10 @@ void l_b(const XsArgs& a, int bf, bool sq, int NW, size_t lds, unsigned grid, hi
     if constexpr (!DUAL && !XSC) l<MT, T, DUAL, 5, NQ, XSC, false>(a, NW, lds, grid, st);
     return;
   }
+  if (bf == 6) {  // MXFP6: one matrix, fp16 x
+    if constexpr (!DUAL && !XSC) l<MT, T, DUAL, 6, NQ, XSC, false>(a, NW, lds, grid, st);
+    return;
+  }
   if (sq) {
     l<MT, T, DUAL, 0, NQ, XSC, true>(a, NW, lds, grid, st);
     return;
@@ -90,7 +94,8 @@ hipError_t allow() {
   hipError_t e = hipSuccess;
   const hipError_t r[] = {allow_b<MT, 0, false>(), allow_b<MT, 2, false>(), allow_b<MT, 3, false>(),
                           allow_b<MT, 4, false>(), allow_b<MT, 0, true>(), allow_one<MT, 1, false, 5, false, false>(),
-                          allow_one<MT, 2, false, 5, false, false>()};
+                          allow_one<MT, 2, false, 5, false, false>(), allow_one<MT, 1, false, 6, false, false>(),
+                          allow_one<MT, 2, false, 6, false, false>()};
   for (hipError_t x : r)
     if (x != hipSuccess) e = x;
   return e;

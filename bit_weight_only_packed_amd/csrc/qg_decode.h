@@ -217,6 +217,33 @@ __device__ __forceinline__ void decode_group_mx(const uint32_t (&w)[16], int gi,
   }
 }
 
+// MXFP6 elements (E3M2: sign bit 5, exponent bits 4..2, mantissa bits 1..0) in
+// two planes of a 6-word lane quad (B = 6 in the load layout): words 0..15 the
+// low nibbles (exponent bits 1..0 and the mantissa) in the 4-bit pair layout,
+// words 16..23 the top two bits (exponent bit 2, sign) in the 2-bit pair
+// layout, group gi at words 4 gi .. 4 gi + 3 and 16 + 2 gi .. 16 + 2 gi + 1.
+// Each element of a pair becomes the fp16 with the sign at bit 15 and the five
+// magnitude bits at bits 12..8 -- exponent field e, mantissa m/4, and e = 0
+// the subnormal m 2^-16 -- which is exactly the element times 2^-12.
+__device__ __forceinline__ void decode_group_mx6(const uint32_t (&w)[24], int gi, uint32_t (&r)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t lo = w[4 * gi + (i >> 2)], hi = w[16 + 2 * gi + (i >> 3)];
+    const int o4 = 4 * (i & 3), o2 = 2 * (i & 7);  // bit offsets of the pair's fields
+    const uint32_t nib = (o4 <= 8 ? lo << (8 - o4) : lo >> (o4 - 8)) & 0x0F000F00u;
+    const uint32_t e2 = (o2 <= 12 ? hi << (12 - o2) : hi >> (o2 - 12)) & 0x10001000u;
+    const uint32_t sg = (hi << (14 - o2)) & 0x80008000u;
+    r[i] = nib | e2 | sg;
+  }
+}
+
+// fp16 bits of 2^(15 - de): an MXFP6 element decoded at 2^-12 times it is the
+// element times 2^(3 - de), exact for de <= 23 (its lowest bit stays at or
+// above 2^-24), rounded once (RNE) beyond; 0 past fp16's range
+__device__ __forceinline__ uint32_t mx6_operand_factor(uint32_t de) {
+  return de <= 29u ? (30u - de) << 10 : (de <= 39u ? 1u << (39u - de) : 0u);
+}
+
 // fp32 2^(e - 127) of an E8M0 byte (e = 0: 2^-127; 255: NaN), times 2^k
 // (|k| small; the result clamps to the fp32 range ends)
 __device__ __forceinline__ float e8m0_scale(uint32_t e, int k) {

@@ -25,9 +25,10 @@ namespace qg {
 // one wave's quads: returns this lane's partial (column j = lane & 15, quarter
 // lane >> 4) over them, scaled back to true units (times 2^24 for the
 // reduction's convention: the caller multiplies nothing more)
-// MX: MXFP4 elements (B = 4 layout): decoded to fp16 values of their own
-// (times 2^-14), x staged with its block exponent only, no offset term, and
-// each group's E8M0 scale applied as an exact fp32 power of two.
+// MX: MXFP4 elements (B = 4 layout) or MXFP6 elements (B = 6, two planes):
+// decoded to fp16 values of their own (times 2^-14, or 2^-12), x staged with
+// its block exponent only, no offset term, and each group's E8M0 scale
+// applied as an exact fp32 power of two.
 template <int B, int NQ, bool XF, bool MX = false>
 __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, int tile, int qw0, int q_end,
                                              char* wsm) {
@@ -80,7 +81,7 @@ __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, 
   const int q = lane >> 4;
   float R = 0.0f;
   if constexpr (MX) {
-    static_assert(B == 4 && !XF, "MXFP4 takes fp16 x and the 4-bit layout");
+    static_assert((B == 4 || B == 6) && !XF, "MXFP4 / MXFP6 take fp16 x (4-bit layout / two-plane 6-bit layout)");
     const int e = stage_wave_plain<NQ>(xv, xl, lane, nvalid);
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
@@ -95,7 +96,8 @@ __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, 
           xp[4 * v + 0] = u4.x; xp[4 * v + 1] = u4.y; xp[4 * v + 2] = u4.z; xp[4 * v + 3] = u4.w;
         }
         uint32_t r[16];
-        decode_group_mx(cw[u], gi, r);
+        if constexpr (B == 6) decode_group_mx6(cw[u], gi, r);
+        else decode_group_mx(cw[u], gi, r);
         float e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -107,7 +109,7 @@ __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, 
         R = __builtin_fmaf(e8m0_scale(eq, 0), e0 + e1, R);
       }
     }
-    return R * pow2f(14 - e);  // the products carry 2^(e - 14)
+    return R * pow2f((B == 6 ? 12 : 14) - e);  // the products carry 2^(e - 14) (E2M1) or 2^(e - 12) (E3M2)
   }
   const int e = stage_wave<B, XF, NQ>(xv, xl, xq, lane, nvalid);
   // ---- compute
@@ -184,6 +186,7 @@ __device__ __forceinline__ void gemv_q_block(const GvArgs& a, int bid, char* sme
   float R;
   const int bits = sd.bits;
   if constexpr (BF == 5) R = gemv_q_wave<4, NQ, XF, true>(a, sd, tile, qw0, q_end, wsm);  // MXFP4
+  else if constexpr (BF == 6) R = gemv_q_wave<6, NQ, XF, true>(a, sd, tile, qw0, q_end, wsm);  // MXFP6
   else if (BF == 2 || (BF == 0 && bits == 2)) R = gemv_q_wave<2, NQ, XF>(a, sd, tile, qw0, q_end, wsm);
   else if (BF == 3 || (BF == 0 && bits == 3)) R = gemv_q_wave<3, NQ, XF>(a, sd, tile, qw0, q_end, wsm);
   else R = gemv_q_wave<4, NQ, XF>(a, sd, tile, qw0, q_end, wsm);

@@ -41,6 +41,9 @@ hipError_t launch_repack_uniform(const uint32_t* canon, const int64_t* row_off, 
                                  const int32_t* cols, int bits, int tiles, int G, int G4, int gs, uint32_t* dcodes,
                                  uint16_t* dscales, hipStream_t st);
 // MXFP4 exponent bytes [N][K/32] -> the per-quarter scale entries (own | group max << 8)
+// MXFP6 codes: canonical 6-bit stream -> the two-plane quad layout
+hipError_t launch_repack_mx6(const uint32_t* canon, const int32_t* cols, int tiles, int G, int G4, uint32_t* dcodes,
+                             hipStream_t st);
 hipError_t launch_repack_mx_scales(const uint8_t* e8, const int32_t* cols, int tiles, int G, int G4, uint16_t* dscales,
                                    hipStream_t st);
 // mode 0: the GEMV class decode; mode 1: the verify GEMM's operand decode

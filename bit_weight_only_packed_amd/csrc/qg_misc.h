@@ -92,6 +92,44 @@ __global__ void k_repack_mx_scales(const uint8_t* __restrict__ e8, const int32_t
   }
 }
 
+// MXFP6 codes: canonical 6-bit stream -> the two-plane quad layout of
+// decode_group_mx6 (low nibbles in the 4-bit pair layout, top two bits in the
+// 2-bit pair layout).  One thread per (tile, quad, lane); padding gets 0.
+__global__ void k_repack_mx6(const uint32_t* __restrict__ canon, const int32_t* __restrict__ cols, int tiles, int G,
+                             int G4, uint32_t* __restrict__ dcodes) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)tiles * G4 * 64) return;
+  const int lane = (int)(gid & 63);
+  const int64_t tq = gid >> 6;
+  const int qu = (int)(tq % G4), t = (int)(tq / G4);
+  const int j = lane & 15, q = lane >> 4;
+  const int n = cols[16 * t + j];
+  uint32_t out[24];
+  for (int u = 0; u < 24; ++u) out[u] = 0u;
+  for (int gi = 0; gi < 4; ++gi) {
+    const int g = 4 * qu + gi;
+    if (n < 0 || g >= G) continue;
+    // the lane's 32 codes: 192 stream bits, words 6q .. 6q + 5 of the group's 24
+    const uint32_t* src = canon + ((int64_t)n * G + g) * 24 + 6 * q;
+    uint32_t in[6];
+    for (int u = 0; u < 6; ++u) in[u] = src[u];
+    for (int i = 0; i < 16; ++i) {
+      uint32_t c[2];
+      for (int h = 0; h < 2; ++h) {
+        const int b0 = 6 * (2 * i + h);
+        const uint64_t two = (uint64_t)in[b0 >> 5] | ((b0 >> 5) + 1 < 6 ? ((uint64_t)in[(b0 >> 5) + 1] << 32) : 0ull);
+        c[h] = (uint32_t)(two >> (b0 & 31)) & 63u;
+      }
+      const int o4 = 4 * (i & 3), o2 = 2 * (i & 7);
+      out[4 * gi + (i >> 2)] |= ((c[0] & 15u) << o4) | ((c[1] & 15u) << (16 + o4));
+      out[16 + 2 * gi + (i >> 3)] |= ((c[0] >> 4) << o2) | ((c[1] >> 4) << (16 + o2));
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(dcodes);
+  for (int p = 0; p < 6; ++p)
+    dst[((size_t)tq * 6 + p) * 64 + lane] = make_uint4(out[4 * p], out[4 * p + 1], out[4 * p + 2], out[4 * p + 3]);
+}
+
 // ---------------------------------------------------------------------------
 // checking kernels: one thread per (tile, group, lane); the lane's quad is
 // loaded as the run kernels hold it and group g of it is decoded by the run
@@ -156,6 +194,36 @@ __device__ __forceinline__ void debug_slot(const SegDev& sg, const int32_t* col_
       return;
     }
   }
+  if constexpr (B == 6) {
+    // MXFP6.  MODE 0: the GEMVs' element decode -- codes (read back out of the
+    // decoded fp16: sign bit 15, magnitude bits 12..8), w exact in fp32
+    // (element * 2^(e - 127)) and q16 the element's fp16 value.  MODE 1: the
+    // verify GEMM's operand -- its fp16 bits (element * 2^(3 - (e_max - e)),
+    // rounded once) and w = operand * 2^(e_max - 130).
+    decode_group_mx6(cw, g & 3, r);
+    const uint32_t eq = s16 & 0xFFu, emax = (uint32_t)s16 >> 8;
+    const uint32_t f = mx6_operand_factor(emax - eq);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t op2 = MODE == 1 ? pk_mul_f16(r[i], f | (f << 16)) : r[i];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = g * 128 + 32 * q + 2 * i + h;
+        const int64_t at = (int64_t)n * K + k;
+        const uint32_t d = r[i] >> (16 * h);
+        if (codes) codes[at] = (int32_t)((((d >> 15) & 1u) << 5) | ((d >> 8) & 31u));
+        const uint16_t el = (uint16_t)(op2 >> (16 * h));
+        if constexpr (MODE == 0) {
+          if (q16) q16[at] = f2h(h2f(el) * 4096.0f);            // the element (exact)
+          if (w) w[at] = h2f(el) * 4096.0f * e8m0_scale(eq, 0);  // exact in fp32
+        } else {
+          if (q16) q16[at] = el;
+          if (w) w[at] = h2f(el) * e8m0_scale(emax, -3);
+        }
+      }
+    }
+    return;
+  } else {
   if constexpr (MODE == 0) decode_group_classes<B>(cw, g & 3, r);
   else decode_group_off1<B>(cw, g & 3, r);
   if (MODE == 1 && sg.sq) decode_group_scaled<B>(cw, g & 3, (uint32_t)s16 | ((uint32_t)s16 << 16), rs);
@@ -185,6 +253,7 @@ __device__ __forceinline__ void debug_slot(const SegDev& sg, const int32_t* col_
       }
     }
   }
+  }
 }
 
 template <int MODE>
@@ -195,6 +264,7 @@ __global__ void k_debug_uniform(SegDev sg, const int32_t* col_map, int G, int G4
   switch (sg.bits) {
     case 2: debug_slot<2, MODE>(sg, col_map, G, G4, K, gid, codes, w, q16); break;
     case 3: debug_slot<3, MODE>(sg, col_map, G, G4, K, gid, codes, w, q16); break;
+    case 6: debug_slot<6, MODE>(sg, col_map, G, G4, K, gid, codes, w, q16); break;
     default: debug_slot<4, MODE>(sg, col_map, G, G4, K, gid, codes, w, q16); break;
   }
 }

@@ -49,6 +49,26 @@ __device__ __forceinline__ void dq_quad(const SegDev& sg, const int32_t* col_map
       return;
     }
   }
+  if constexpr (B == 6) {  // MXFP6: element * 2^(e - 127), rounded once to fp16
+    uint16_t* row = out + (size_t)(n - n0) * K + 32 * q;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int g = 4 * qu + gi;
+      if (g >= G) break;
+      uint32_t r[16];
+      decode_group_mx6(cw, gi, r);
+      const uint32_t s2 = gi < 2 ? sw.x : sw.y;
+      const float s = e8m0_scale(((gi & 1) ? (s2 >> 16) : s2) & 0xFFu, 12);  // also undoes the 2^-12
+      uint32_t h[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        h[i] = (uint32_t)f2h(h2f((uint16_t)r[i]) * s) | ((uint32_t)f2h(h2f((uint16_t)(r[i] >> 16)) * s) << 16);
+      uint4* dst = reinterpret_cast<uint4*>(row + (size_t)g * 128);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[v] = make_uint4(h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]);
+    }
+    return;
+  } else {
   const float o = 0.5f * (float)((1 << B) - 1);
   uint16_t* row = out + (size_t)(n - n0) * K + 32 * q;
 #pragma unroll
@@ -71,6 +91,7 @@ __device__ __forceinline__ void dq_quad(const SegDev& sg, const int32_t* col_map
 #pragma unroll
     for (int v = 0; v < 4; ++v) dst[v] = make_uint4(h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]);
   }
+  }
 }
 
 __global__ __launch_bounds__(256) void k_dequant_f16(SegDev sg, const int32_t* col_map, int G, int G4, int K, int tl0,
@@ -83,6 +104,7 @@ __global__ __launch_bounds__(256) void k_dequant_f16(SegDev sg, const int32_t* c
   switch (sg.bits) {
     case 2: dq_quad<2>(sg, col_map, G, G4, K, tl, qu, lane, n0, n1, out); break;
     case 3: dq_quad<3>(sg, col_map, G, G4, K, tl, qu, lane, n0, n1, out); break;
+    case 6: dq_quad<6>(sg, col_map, G, G4, K, tl, qu, lane, n0, n1, out); break;
     default: dq_quad<4>(sg, col_map, G, G4, K, tl, qu, lane, n0, n1, out); break;
   }
 }

@@ -32,7 +32,10 @@
 // the four lane quarters of a group carry E8M0 exponents of their own, so each
 // quarter's operand is multiplied by 2^-(e_max - e) (exact while it stays in
 // fp16's range, else rounded once) and the group's chain by 2^(e_max - 113),
-// e_max the largest of the four (kept beside each exponent at create).
+// e_max the largest of the four (kept beside each exponent at create).  MXFP6
+// likewise, its E3M2 elements decoded at 2^-12 and multiplied by 2^(15 - de)
+// (the operand is the element times 2^(3 - de), exact for de <= 23), the chain
+// by 2^(e_max - 130).
 //
 // K slices meet in one of two ways, both independent of the order of arrival.
 // Few outputs: in fixed-point words (see fx_word), one integer atomic per
@@ -101,18 +104,21 @@ __device__ __forceinline__ void xs_unit(const XsUnit<B, T, ND>& c, const char* c
       if constexpr (XSC) F[mt] = *reinterpret_cast<const f4_t*>(xfac + gl * (16 * MT) + 16 * mt + 4 * kq);
     }
     if constexpr (MX) {
-      static_assert(B == 4 && ND == 1 && !XSC, "MXFP4: one matrix, fp16 x");
+      static_assert((B == 4 || B == 6) && ND == 1 && !XSC, "MXFP4 / MXFP6: one matrix, fp16 x");
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const uint32_t sw = (gi < 2) ? c.sc[0][t].x : c.sc[0][t].y;
         const uint32_t ent = ((gi & 1) ? (sw >> 16) : sw) & 0xFFFFu;
         const uint32_t eq = ent & 0xFFu, emax = ent >> 8, de = emax - eq;
-        const uint32_t f = de <= 14u ? (15u - de) << 10 : (de <= 24u ? 1u << (24u - de) : 0u);  // fp16 2^-de
+        // fp16 2^-de (E2M1 at 2^-14), or 2^(15 - de) (E3M2 at 2^-12: the operand is the element times 2^(3 - de))
+        const uint32_t f = B == 6 ? mx6_operand_factor(de)
+                                  : (de <= 14u ? (15u - de) << 10 : (de <= 24u ? 1u << (24u - de) : 0u));
         uint32_t r[16];
-        decode_group_mx(c.cw[0][t], gi, r);
+        if constexpr (B == 6) decode_group_mx6(c.cw[0][t], gi, r);
+        else decode_group_mx(c.cw[0][t], gi, r);
 #pragma unroll
         for (int i = 0; i < 16; ++i) r[i] = pk_mul_f16(r[i], f | (f << 16));
-        const float s = e8m0_scale(emax, 14);
+        const float s = e8m0_scale(emax, B == 6 ? -3 : 14);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           f4_t cc = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -506,6 +512,8 @@ __global__ __launch_bounds__(512) void k_gemm_xs(XsArgs a) {
   const int bits = sd[0].bits;
   if constexpr (BF == 5) {  // MXFP4 (per-quarter scale entries, the 4-bit layout)
     if constexpr (!DUAL && !XSC) xs_body<4, T, MT, ND, NQ, XSC, true, true>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
+  } else if constexpr (BF == 6) {  // MXFP6 (per-quarter scale entries, the two-plane 6-bit layout)
+    if constexpr (!DUAL && !XSC) xs_body<6, T, MT, ND, NQ, XSC, true, true>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
   } else if (BF == 2 || (BF == 0 && bits == 2))
     xs_body<2, T, MT, ND, NQ, XSC, SQ>(a, sd, s, q0, q1 - q0, tgb, tge, a.tg_prefix[si], smem);
   else if (BF == 3 || (BF == 0 && bits == 3))

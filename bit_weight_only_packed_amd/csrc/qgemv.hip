@@ -62,7 +62,7 @@ struct Work {
 struct HostSeg {
   int bits, tiles, tile0, ncols;
   int sq = 0;  // scale group 64 or 32 (per-lane-quarter scale layout)
-  int mx = 0;  // MXFP4 elements
+  int mx = 0;  // 1: MXFP4 elements; 2: MXFP6 elements (bits 6, the two-plane layout)
   uint32_t* codes = nullptr;
   uint16_t* scales = nullptr;
 };
@@ -124,13 +124,16 @@ WSet wset_of(const qg_plan* h) {
   return w;
 }
 
-// the kernels' width argument: the single code width, 0 for several, 5 for MXFP4
+// the kernels' width argument: the single code width, 0 for several, 5 for
+// MXFP4, 6 for MXFP6
 int single_bits(const qg_plan* h) {
   if (h->format == QG_FMT_MXFP4) return 5;
+  if (h->format == QG_FMT_MXFP6) return 6;
   return h->segs.size() == 1 ? h->segs[0].bits : 0;
 }
-// uniform codes and MXFP4 share the code layout and the GEMV / verify GEMM
-bool coded(const qg_plan* h) { return h->format == QG_FMT_UNIFORM || h->format == QG_FMT_MXFP4; }
+// uniform codes and the MX formats share the tile layout and the GEMV / verify GEMM
+bool mxfmt(int f) { return f == QG_FMT_MXFP4 || f == QG_FMT_MXFP6; }
+bool coded(const qg_plan* h) { return h->format == QG_FMT_UNIFORM || mxfmt(h->format); }
 
 // ---- M = 1 plans -------------------------------------------------------------
 // quads-per-wave counts the per-group GEMV is compiled for
@@ -190,7 +193,7 @@ bool sk_fits(const qg_plan* h) { return h->G4 <= 63 * SK_UPW; }
 // M = 1 kernel choice, measured on the decode shapes: the per-group kernel
 // from 256 tiles up, the per-tile-run kernel for narrower matrices.
 bool use_sk(const qg_plan* h) {
-  if (!sk_fits(h) || h->format == QG_FMT_MXFP4) return false;  // MXFP4: the per-group GEMV only
+  if (!sk_fits(h) || mxfmt(h->format)) return false;  // MX formats: the per-group GEMV only
   if (h->pins & QG_PIN_M1_PERGROUP) return false;
   if (h->pins & QG_PIN_M1_RUNS) return true;
   return h->total_tiles < 256;
@@ -543,9 +546,10 @@ qg_status run_trellis(const qg_plan* h, const Work& w, const uint16_t* x, int M,
 qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   const int N = d->N, K = d->K, G = K / QG_GROUP, G4 = (G + 3) / 4;
   h->col_bits.resize(N);
-  const bool mx = d->format == QG_FMT_MXFP4;
+  const bool mx = mxfmt(d->format), mx6 = d->format == QG_FMT_MXFP6;
   if (mx) {
-    std::fill(h->col_bits.begin(), h->col_bits.end(), (uint8_t)4);  // E2M1 elements in 4-bit fields
+    // E2M1 elements in 4-bit fields, E3M2 elements in 6-bit fields
+    std::fill(h->col_bits.begin(), h->col_bits.end(), (uint8_t)(mx6 ? 6 : 4));
   } else if (d->bits == 0) {
     if (!d->col_bits) return fail(QG_ERR_INVALID_ARG, "bits == 0 needs col_bits (host, N entries)");
     for (int n = 0; n < N; ++n) {
@@ -567,11 +571,11 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
   }
   const int gs = d->group_size, sq = gs < QG_GROUP ? 1 : 0;
   h->group_size = gs;
-  h->weight_bytes = acc * 4 + (int64_t)N * (K / gs) * (mx ? 1 : 2);  // MXFP4: one exponent byte per block
+  h->weight_bytes = acc * 4 + (int64_t)N * (K / gs) * (mx ? 1 : 2);  // MX: one exponent byte per block
   // widest codes first: their workgroups (the longest) are dispatched first,
   // so the tail of a launch is the lighter widths'
   int tile0 = 0;
-  for (int b = 4; b >= 2; --b) {
+  for (int b = 6; b >= 2; --b) {
     std::vector<int32_t> cols;
     for (int n = 0; n < N; ++n)
       if (h->col_bits[n] == b) cols.push_back(n);
@@ -579,7 +583,7 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
     HostSeg s;
     s.bits = b;
     s.sq = sq;
-    s.mx = mx ? 1 : 0;
+    s.mx = mx ? (mx6 ? 2 : 1) : 0;
     s.ncols = (int)cols.size();
     s.tiles = (s.ncols + 15) / 16;
     s.tile0 = tile0;
@@ -603,8 +607,11 @@ qg_status create_uniform(qg_plan* h, const qg_weight_desc* d, hipStream_t st) {
       hipFree(d_off);
       return fail(QG_ERR_OOM, "device allocation for the weight layout failed");
     }
-    e = launch_repack_uniform((const uint32_t*)d->codes, d_off, d->scales, h->col_map + 16 * s.tile0, s.bits, s.tiles,
-                              G, G4, gs, s.codes, mx ? nullptr : s.scales, st);
+    if (mx6)
+      e = launch_repack_mx6((const uint32_t*)d->codes, h->col_map + 16 * s.tile0, s.tiles, G, G4, s.codes, st);
+    else
+      e = launch_repack_uniform((const uint32_t*)d->codes, d_off, d->scales, h->col_map + 16 * s.tile0, s.bits, s.tiles,
+                                G, G4, gs, s.codes, mx ? nullptr : s.scales, st);
     if (e == hipSuccess && mx)
       e = launch_repack_mx_scales(reinterpret_cast<const uint8_t*>(d->scales), h->col_map + 16 * s.tile0, s.tiles, G,
                                   G4, s.scales, st);
@@ -920,6 +927,9 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   if (d->format == QG_FMT_MXFP4) {
     if (d->group_size != 32) return fail(QG_ERR_INVALID_ARG, "MXFP4: group_size must be 32 (got %d)", d->group_size);
     if (d->bits != 0 && d->bits != 4) return fail(QG_ERR_INVALID_ARG, "MXFP4: bits must be 0 or 4 (got %d)", d->bits);
+  } else if (d->format == QG_FMT_MXFP6) {
+    if (d->group_size != 32) return fail(QG_ERR_INVALID_ARG, "MXFP6: group_size must be 32 (got %d)", d->group_size);
+    if (d->bits != 0 && d->bits != 6) return fail(QG_ERR_INVALID_ARG, "MXFP6: bits must be 0 or 6 (got %d)", d->bits);
   } else if (d->group_size != QG_GROUP &&
              !(d->format == QG_FMT_UNIFORM && (d->group_size == 64 || d->group_size == 32))) {
     return fail(QG_ERR_INVALID_ARG, "group_size must be 128 (uniform codes: 128, 64 or 32; got %d)", d->group_size);
@@ -929,7 +939,7 @@ qg_status qgemv_create(qg_handle* out, const qg_weight_desc* d, int32_t max_M, v
   if (max_M < 1 || max_M > QG_MAX_M) return fail(QG_ERR_INVALID_ARG, "max_M = %d is not in [1, 32]", max_M);
   if (!d->codes || !d->scales) return fail(QG_ERR_INVALID_ARG, "codes and scales must be device pointers");
   if (!aligned16(d->codes) || !aligned16(d->scales)) return fail(QG_ERR_INVALID_ARG, "codes/scales must be 16-byte aligned");
-  if (d->format != QG_FMT_UNIFORM && d->format != QG_FMT_TRELLIS3 && d->format != QG_FMT_MXFP4)
+  if (d->format != QG_FMT_UNIFORM && d->format != QG_FMT_TRELLIS3 && !mxfmt(d->format))
     return fail(QG_ERR_INVALID_ARG, "unknown format %d", d->format);
   if (d->format == QG_FMT_TRELLIS3) {
     if (!d->codebook || !aligned16(d->codebook)) return fail(QG_ERR_INVALID_ARG, "trellis needs a 16-byte aligned codebook");

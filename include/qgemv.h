@@ -99,7 +99,17 @@ typedef enum {
  * [N][K/32], group_size 32, bits 0 or 4.  The verify GEMM (2..32 rows) runs
  * each 128-group at its largest exponent: the other 32-blocks' elements are
  * exact while within 2^9 of it and are rounded once to fp16 beyond that. */
-typedef enum { QG_FMT_UNIFORM = 0, QG_FMT_TRELLIS3 = 1, QG_FMT_MXFP4 = 2 } qg_format;
+/* QG_FMT_MXFP6 ("The Rock8", format table, MXFP6 row: OCP microscaling, E3M2
+ * elements -- sign, 3 exponent bits with bias 3, 2 mantissa bits, no inf or
+ * NaN -- four per three bytes, one UE8M0 scale byte per 32 elements along K):
+ * codes in the 6-bit canonical layout below (element j of a row at bits
+ * [6j, 6j + 6) of its stream, 24 words per row and group of 128), `scales`
+ * points at uint8 exponent bytes [N][K/32], group_size 32, bits 0 or 6.  The
+ * verify GEMM runs each 128-group at its largest exponent: the other
+ * 32-blocks' elements are exact while within 2^23 of it and are rounded once to
+ * fp16 beyond that.  The fused MLP and the one-launch batch take uniform codes
+ * only (MX handles in qgemv_run_batch run one launch per entry). */
+typedef enum { QG_FMT_UNIFORM = 0, QG_FMT_TRELLIS3 = 1, QG_FMT_MXFP4 = 2, QG_FMT_MXFP6 = 3 } qg_format;
 
 enum {
   QG_FLAG_X_PREROTATED = 1u << 0, /* TRELLIS3: x already rotated, skip the Walsh-Hadamard step */

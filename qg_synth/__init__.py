@@ -61,8 +61,9 @@ def code_words(n_words: int, *, seed: int = 0, cfg_id: int = 0, tensor_id: int =
 
 
 def uniform_code_words(N: int, K: int, bits: int, **kw) -> np.ndarray:
-    """Code stream for an N x K matrix with ``bits`` bits for every column."""
-    assert K % GROUP == 0 and bits in (2, 3, 4)
+    """Code stream for an N x K matrix with ``bits`` bits for every column
+    (6: the MXFP6 element stream)."""
+    assert K % GROUP == 0 and bits in (2, 3, 4, 6)
     return code_words(N * K * bits // 32, **kw)
 
 
