@@ -748,18 +748,23 @@ qg_status run_xs(const qg_plan* h, const Work& w, const qg_plan* h2, const uint1
 }
 
 // Several independent M = 1 products (uniform handles, distinct) in one
-// launch of the per-group GEMV: one plan shape for all (2 quads per wave, NW
+// launch of the per-group GEMV: one plan shape for all (NQ quads per wave, NW
 // waves per workgroup covering the longest K slice), each matrix cut into as
 // many K slices as that takes, slices meeting in fixed-point words (or, with
-// the partials pinned, in the handle's partials when they fit).
+// the partials pinned, in the handle's partials when they fit).  Measured
+// (same-box A/B, palindrome order): 2 quads per wave in slices of at most 10
+// quads (5 waves) for narrow batches (q,k,v: 448 tiles, 7.0 us against 7.5
+// with 3 quads); 3 quads per wave in slices of at most 12 (4 waves) from 1024
+// tiles and 9 quads up (gate,up: 2,176 tiles, 18.95 us against 19.74).
 qg_status run_batch_m1(int n, const qg_plan* const* hs, const uint16_t* const* xs, uint16_t* const* ys, hipStream_t st) {
-  constexpr int NQ = 2;
-  int maxg4 = 1, bf = single_bits(hs[0]);
+  int maxg4 = 1, bf = single_bits(hs[0]), tiles = 0;
   for (int i = 0; i < n; ++i) {
     maxg4 = std::max(maxg4, hs[i]->G4);
+    tiles += hs[i]->total_tiles;
     if (single_bits(hs[i]) != bf) bf = 0;
   }
-  const int NW = (std::min(10, maxg4) + NQ - 1) / NQ;  // slices of at most 10 quads (5 waves)
+  const int NQ = (tiles >= 1024 && maxg4 >= 9) ? 3 : 2;
+  const int NW = (std::min(NQ == 3 ? 12 : 10, maxg4) + NQ - 1) / NQ;
   GvBatch b{};
   b.n = n;
   int wg = 0;

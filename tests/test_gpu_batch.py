@@ -115,3 +115,32 @@ def test_full_size_layer_set_sampled():
                                  O.gemv_uniform_rows(xs_np[i], w, sc, N, K, 3, rows))
         say(S.LAYER_SET[i]["name"], err)
         assert err <= TOL, (i, err)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 0])
+def test_wide_batch_three_quads_per_wave(bits):
+    """From 1024 tiles in one batch the launch runs 3 quads per wave: two wide
+    matrices (one K slice with a ragged last quad; two K slices meeting in
+    fixed-point words), every code width and several widths mixed, against the
+    oracle on sampled columns (first and last tiles included)."""
+    shapes = [(8192, 4736), (8192, 7168)]  # 37 groups (ragged quad), 56 groups (2 slices)
+    mats, xs_np = [], []
+    for i, (N, K) in enumerate(shapes):
+        if bits == 0:
+            cb = S.column_bits(N, 0.3, 2 + 2 * i, cfg_id=167, tensor_id=S.T_MASK + i)
+            mats.append(Uniform(N, K, col_bits=cb, cfg_id=167, tid=i))
+        else:
+            mats.append(Uniform(N, K, bits, cfg_id=167, tid=i))
+        xs_np.append(S.activations(1, K, cfg_id=167, tensor_id=10 + i))
+    xs = [dev_f16(x) for x in xs_np]
+    say("wide batch", bits)
+    ys = Q.run_batch([m.lin for m in mats], xs)
+    ys2 = Q.run_batch([m.lin for m in mats], xs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(167 + bits)
+    for i, (m, (N, K)) in enumerate(zip(mats, shapes)):
+        assert sha(ys[i]) == sha(ys2[i])
+        rows = np.unique(np.concatenate([np.arange(32), np.arange(N - 32, N), rng.choice(N, 64, replace=False)]))
+        err = O.normwise_rel_err(ys[i].cpu().numpy().astype(np.float64)[:, rows], m.ref(xs_np[i], rows))
+        say(i, err)
+        assert err <= TOL, (i, err)
