@@ -71,8 +71,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# the sources the per-group M = 1 GEMV (the roofline entry's kernel) is built from
-GEMV_SOURCES = ("k_m1q.hip", "qg_gemv.h", "qg_stage.h", "qg_decode.h", "qg_common.h", "qg_args.h", "qg_launch.h")
+# the sources the per-group M = 1 GEMV (the roofline entry's kernel) is built
+# from, and the host code that plans its launch (quads per wave, waves, slices)
+GEMV_SOURCES = ("k_m1q.hip", "qg_gemv.h", "qg_stage.h", "qg_decode.h", "qg_common.h", "qg_args.h", "qg_launch.h",
+                "qgemv.hip")
 
 
 def src_hash(files=None) -> str:
@@ -494,7 +496,7 @@ def main():
         if tj.get("gemv_src_hash") == src_hash(GEMV_SOURCES):
             traffic = tj.get("bytes_per_launch")
     result["roofline"] = {"bound": "hbm",
-                          "kernel": "qg::k_gemv_batch (M=1 GEMV, gate and up 2 x 5120x17408 in one launch, 3-bit)",
+                          "kernel": "qg::k_gemv_batch<3, 3> (M=1 GEMV, gate and up 2 x 5120x17408 in one launch, 3-bit, 3 quads per wave)",
                           "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                           "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3),
