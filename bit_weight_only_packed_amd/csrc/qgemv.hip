@@ -152,21 +152,35 @@ struct M1Plan {
 // K slice.  Measured on the decode shapes: 2 quads per wave is fastest, then
 // 3, then 1 (more quads per wave lengthen the serial load-to-use chain, fewer
 // add per-wave fixed cost); take the first of that order that fits in 16 waves
-// with <= 1/8 dead quads (the fused gate/up pass: at most 2 quads per wave).
+// with <= 1/8 dead quads (the fused gate/up pass: at most 2 quads per wave
+// on this path).
 // K slices (one matrix; measured): up to K = 8192 and 1024 tiles, of about 2
 // quads (a one-wave workgroup per slice: q/o 6.4 us against 7.0 in one slice,
 // q|k|v stacked 7.1 against 7.2; wider matrices gain nothing: gate/up
 // 10.4-10.9 either way, gate|up stacked 16.7 in one slice against 16.9-18.8);
 // beyond K = 8192 of about 7 quads (down: 10.6-10.8 against 14.7 in one slice;
 // with 2- and 3-bit columns 11.8 against 12.9 in 4).
+// Several widths beyond K = 8192 (the fused MLP's down pass), and the fused
+// gate/up pass, take 3 quads per wave (measured, same-box A/B in palindrome
+// order, the MLP 5120 -> 17408 -> 5120 at one row: with mixed widths 36.0 ->
+// 32.0 us from the gate/up pass, 31.3 us with the down pass in slices of 12
+// quads; with one width 29.1 -> 28.2 us from the gate/up pass, while the
+// one-width down pass is faster as it was).
 M1Plan m1_plan(const qg_plan* h, bool dual) {
   const Launch& L = h->over[0];
   M1Plan p;
   const int G4 = h->G4;
-  p.S = L.S > 0 ? L.S : (dual ? 1 : (G4 > 16 ? (G4 + 6) / 8 : (h->total_tiles <= 1024 ? (G4 + 1) / 2 : 1)));
+  const bool several = h->segs.size() > 1;
+  p.S = L.S > 0 ? L.S
+                : (dual ? 1
+                        : (G4 > 16 ? (several ? (G4 + 11) / 12 : (G4 + 6) / 8)
+                                   : (h->total_tiles <= 1024 ? (G4 + 1) / 2 : 1)));
   p.S = std::min(p.S, G4);
   const int g4s = (G4 + p.S - 1) / p.S;
-  if (L.NW <= 0) {
+  if (L.NW <= 0 && (dual || (several && G4 > 16)) && g4s >= 9 && (g4s + 2) / 3 <= 16) {
+    p.NQ = 3;
+    p.NW = (g4s + 2) / 3;
+  } else if (L.NW <= 0) {
     static const int order[] = {2, 3, 1, 4, 5};
     int best_nw = std::min(16, g4s), best_nq = (g4s + best_nw - 1) / best_nw;
     for (int nq : order) {

@@ -84,3 +84,31 @@ def test_mlp_shape_mismatch_rejected():
     assert e.value.status == Q.QG_ERR_INVALID_ARG
     with pytest.raises(Q.QGError):
         Q.mlp(g.lin, u.lin, g.lin, x)                  # down's K must be gate's N
+
+
+@pytest.mark.parametrize("mixed", [False, True])
+def test_three_quad_plans(mixed):
+    """The fused gate/up pass at K = 5120 and a several-width matrix at
+    K = 17408 run 3 quads per wave: the MLP (one width and mixed widths)
+    against the oracle, and the several-width long-K GEMV on its own."""
+    H, I = 5120, 1024
+    if mixed:
+        cb_gu = S.column_bits(I, 0.25, 4, cfg_id=171, tensor_id=S.T_MASK)
+        g = Uniform(I, H, col_bits=cb_gu, cfg_id=171, tid=0)
+        u = Uniform(I, H, col_bits=cb_gu, cfg_id=171, tid=1)
+        d = Uniform(H, I, col_bits=S.column_bits(H, 0.25, 2, cfg_id=171, tensor_id=S.T_MASK + 1), cfg_id=171, tid=2)
+    else:
+        g, u, d = (Uniform(I, H, 3, cfg_id=172, tid=0), Uniform(I, H, 3, cfg_id=172, tid=1),
+                   Uniform(H, I, 3, cfg_id=172, tid=2))
+    x_np = S.activations(1, H, cfg_id=173 + mixed)
+    y = Q.mlp(g.lin, u.lin, d.lin, dev_f16(x_np)).cpu().numpy().astype(np.float64)
+    ref = O.mlp(x_np, g.w(), u.w(), d.w())
+    err = O.normwise_rel_err(y, ref)
+    say("mlp 3-quad", mixed, err)
+    assert err <= TOL, err
+    if mixed:
+        cb = S.column_bits(640, 0.3, 4, cfg_id=175, tensor_id=S.T_MASK)
+        m = Uniform(640, 17408, col_bits=cb, cfg_id=175, tid=3)
+        xl = S.activations(1, 17408, cfg_id=175)
+        yl = m.lin.run(dev_f16(xl)).cpu().numpy().astype(np.float64)
+        assert O.normwise_rel_err(yl, m.ref(xl)) <= TOL
