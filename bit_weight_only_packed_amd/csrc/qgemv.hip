@@ -195,6 +195,14 @@ M1Plan m1_plan(const qg_plan* h, bool dual) {
     }
     p.NW = best_nw;
     p.NQ = nq_round_up(best_nq);
+    // more 2-quad waves than the chip holds at once (seven per SIMD): 3 quads
+    // per wave instead, as the batched launch measured (a stacked gate|up
+    // handle, 2,176 tiles: one and a half rounds of 5-wave workgroups)
+    const int64_t waves = (int64_t)h->total_tiles * p.S * p.NW;
+    if (p.NQ == 2 && waves > (int64_t)7 * 4 * std::max(1, h->cus) && g4s >= 9 && (g4s + 2) / 3 <= 16) {
+      p.NQ = 3;
+      p.NW = (g4s + 2) / 3;
+    }
   } else {
     p.NW = L.NW;
     p.NQ = nq_round_up((g4s + L.NW - 1) / L.NW);
