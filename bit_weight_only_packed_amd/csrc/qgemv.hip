@@ -1085,7 +1085,7 @@ qg_status qgemv_run_batch(int32_t n, const qg_handle* hs, const uint16_t* const*
     for (int k = 0; k < i; ++k)
       if (hs[k] == hs[i]) return fail(QG_ERR_INVALID_ARG, "entries %d and %d share a handle (and its workspace)", k, i);
     if (hs[i]->format != QG_FMT_UNIFORM || hs[i]->device != hs[0]->device || invariant(hs[i])) one_launch = false;
-    // (MXFP4 and trellis handles run entry by entry)
+    // (MX-format and trellis handles run entry by entry)
   }
   hipStream_t st = (hipStream_t)stream;
   if (one_launch) return run_batch_m1(n, hs, xs, ys, st);
@@ -1142,7 +1142,7 @@ static int prefill_chunk_rows(const qg_plan* h) {
 qg_status qgemv_prefill_workspace(qg_handle h, size_t* min_bytes, size_t* full_bytes) {
   g_err.clear();
   if (!h || !min_bytes || !full_bytes) return fail(QG_ERR_INVALID_ARG, "NULL argument");
-  if (!coded(h)) return fail(QG_ERR_UNSUPPORTED, "the prefill route takes uniform-code and MXFP4 handles");
+  if (!coded(h)) return fail(QG_ERR_UNSUPPORTED, "the prefill route takes uniform-code and MX-format handles");
   const size_t row = (size_t)h->K * sizeof(uint16_t);
   *full_bytes = kPrefillGemmWs + (size_t)h->N * row;
   *min_bytes = h->segs.size() == 1 ? kPrefillGemmWs + 16 * row : *full_bytes;
@@ -1219,7 +1219,7 @@ qg_status qg_stream_read(const void* buf, int64_t bytes, void* stream) {
 qg_status qgemv_debug_unpack(qg_handle h, int32_t* codes, void* stream) {
   g_err.clear();
   if (!h || !codes) return fail(QG_ERR_INVALID_ARG, "NULL argument");
-  if (!coded(h)) return fail(QG_ERR_INVALID_ARG, "debug_unpack takes a uniform-code or MXFP4 handle");
+  if (!coded(h)) return fail(QG_ERR_INVALID_ARG, "debug_unpack takes a uniform-code or MX-format handle");
   for (const auto& s : h->segs) {
     const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq, s.mx};
     QG_HIP(launch_debug_uniform(sd, h->col_map, h->G, h->G4, h->K, 0, codes, nullptr, nullptr, (hipStream_t)stream));
@@ -1245,7 +1245,7 @@ qg_status qgemv_debug_dequant(qg_handle h, float* w, uint16_t* q16, void* stream
 qg_status qgemv_debug_operand(qg_handle h, int32_t* codes, uint16_t* b16, float* w, void* stream) {
   g_err.clear();
   if (!h || (!codes && !b16 && !w)) return fail(QG_ERR_INVALID_ARG, "NULL argument");
-  if (!coded(h)) return fail(QG_ERR_INVALID_ARG, "debug_operand takes a uniform-code or MXFP4 handle");
+  if (!coded(h)) return fail(QG_ERR_INVALID_ARG, "debug_operand takes a uniform-code or MX-format handle");
   for (const auto& s : h->segs) {
     const SegDev sd{s.codes, s.scales, s.bits, s.tiles, s.tile0, s.sq, s.mx};
     QG_HIP(launch_debug_uniform(sd, h->col_map, h->G, h->G4, h->K, 1, codes, w, b16, (hipStream_t)stream));

@@ -270,8 +270,8 @@ qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t*
  * call on a device creates the library's hipBLASLt handle, and the first call
  * for a problem shape plans it (host work; warm a shape before capturing it).
  * The chunked rows use the handle's workspace, so calls on one handle are
- * ordered like qgemv_run's.  UNIFORM and MXFP4 handles (QG_ERR_UNSUPPORTED
- * otherwise); errors of the GEMM return QG_ERR_DEVICE with hipBLASLt's
+ * ordered like qgemv_run's.  UNIFORM, MXFP4 and MXFP6 handles
+ * (QG_ERR_UNSUPPORTED otherwise); errors of the GEMM return QG_ERR_DEVICE with hipBLASLt's
  * reason. */
 qg_status qgemv_run_prefill(qg_handle h, const uint16_t* x, int32_t M, uint16_t* y, void* workspace, size_t ws_bytes,
                             void* stream);
@@ -302,12 +302,13 @@ qg_status qg_stream_read(const void* buf, int64_t bytes, void* stream);
  *      written back per weight so tests can compare them bit for bit ---- */
 
 /* codes: device int32 [N][K], the unpacked code of every weight, as the M = 1
- * GEMVs decode it (UNIFORM). */
+ * GEMVs decode it (UNIFORM; MXFP4 / MXFP6: the element's 4- or 6-bit code). */
 qg_status qgemv_debug_unpack(qg_handle h, int32_t* codes, void* stream);
 
 /* w: device fp32 [N][K], exact dequantised weight (c - o_b) * s (UNIFORM, as
- * the M = 1 GEMVs decode it) or codebook[state] * s (TRELLIS3).  q16 (UNIFORM,
- * may be NULL): device fp16 bits [N][K] of c - o_b. */
+ * the M = 1 GEMVs decode it), element * 2^(e - 127) (MXFP4 / MXFP6) or
+ * codebook[state] * s (TRELLIS3).  q16 (may be NULL): device fp16 bits [N][K]
+ * of c - o_b (UNIFORM) or of the element's value (MX formats). */
 qg_status qgemv_debug_dequant(qg_handle h, float* w, uint16_t* q16, void* stream);
 
 /* The verify GEMM's (M >= 2) decode of UNIFORM codes into the matrix-core
@@ -315,7 +316,12 @@ qg_status qgemv_debug_dequant(qg_handle h, float* w, uint16_t* q16, void* stream
  * b16 (device fp16 bits [N][K]) the operand element itself (c * 2^-23, i.e. the
  * integer 2c as fp16 bits), and w (device fp32 [N][K]) the dequantised weight
  * rebuilt from the operand value and the kernel's offset constant,
- * (op - o_b * 2^-23) * 2^23 * s.  Each pointer may be NULL, not all three. */
+ * (op - o_b * 2^-23) * 2^23 * s.  Scale groups of 64 or 32: the operand is
+ * 2 (c - o_b) s rounded once to fp16 and w half its value.  MXFP4: the operand
+ * is element * 2^-14 * 2^-(e_max - e) (e_max the largest exponent of the
+ * 128-group), rounded once, and w = op * 2^(e_max - 113); MXFP6: element *
+ * 2^(3 - (e_max - e)), w = op * 2^(e_max - 130).  Each pointer may be NULL,
+ * not all three. */
 qg_status qgemv_debug_operand(qg_handle h, int32_t* codes, uint16_t* b16, float* w, void* stream);
 
 /* states: device uint16 [N][K], the trellis state of every weight (TRELLIS3). */

@@ -104,3 +104,28 @@ def test_bad_col_bits_rejected_before_device(L):
     st = L.qgemv_create(ctypes.byref(h), ctypes.byref(d), 8, None)
     # either the device check (no GPU here) or the width check rejects it; never OK
     assert st in (Q.QG_ERR_INVALID_ARG, Q.QG_ERR_UNSUPPORTED)
+
+
+def test_binding_constants_match_the_header():
+    """Every status code, format, flag and pin the binding passes to the
+    library has the value include/qgemv.h declares (read from the header's
+    enumerators, `1u << n` forms evaluated)."""
+    import re
+    text = open(Q.HEADER_PATH).read()
+    decl = {}
+    for name, expr in re.findall(r"\b(QG_[A-Z0-9_]+)\s*=\s*(-?\d+u?(?:\s*<<\s*\d+)?)", text):
+        m = re.fullmatch(r"(-?\d+)u?(?:\s*<<\s*(\d+))?", expr.strip())
+        decl[name] = int(m.group(1)) << int(m.group(2) or 0)
+    pairs = {"QG_OK": Q.QG_OK, "QG_ERR_INVALID_ARG": Q.QG_ERR_INVALID_ARG, "QG_ERR_UNSUPPORTED": Q.QG_ERR_UNSUPPORTED,
+             "QG_ERR_DEVICE": Q.QG_ERR_DEVICE, "QG_ERR_OOM": Q.QG_ERR_OOM,
+             "QG_FMT_UNIFORM": Q.FMT_UNIFORM, "QG_FMT_TRELLIS3": Q.FMT_TRELLIS3, "QG_FMT_MXFP4": Q.FMT_MXFP4,
+             "QG_FMT_MXFP6": Q.FMT_MXFP6, "QG_FLAG_X_PREROTATED": Q.FLAG_X_PREROTATED,
+             "QG_FLAG_BATCH_INVARIANT": Q.FLAG_BATCH_INVARIANT, "QG_PIN_M1_PERGROUP": Q.PIN_M1_PERGROUP,
+             "QG_PIN_M1_RUNS": Q.PIN_M1_RUNS, "QG_PIN_PARTIALS": Q.PIN_PARTIALS, "QG_PIN_WORDS": Q.PIN_WORDS,
+             "QG_PIN_XS_T1": Q.PIN_XS_T1, "QG_PIN_XS_T2": Q.PIN_XS_T2,
+             "QG_PIN_TRELLIS_ROT_LAUNCH": Q.PIN_TRELLIS_ROT_LAUNCH, "QG_PIN_TRELLIS_BAND": Q.PIN_TRELLIS_BAND,
+             "QG_GROUP": Q.GROUP}
+    for name, value in pairs.items():
+        assert decl.get(name) == value, (name, decl.get(name), value)
+    # every pin and flag the header declares is known to the binding
+    assert {n for n in decl if n.startswith(("QG_PIN_", "QG_FLAG_", "QG_FMT_"))} <= set(pairs)
