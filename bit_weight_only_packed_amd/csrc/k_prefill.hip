@@ -15,9 +15,9 @@ namespace qg {
 
 hipError_t launch_dequant_f16(const SegDev& sg, const int32_t* col_map, int G, int G4, int K, int tl0, int ntl, int n0,
                               int n1, uint16_t* out, hipStream_t st) {
-  const int64_t n = (int64_t)ntl * G4 * 64;
+  const int64_t n = (int64_t)ntl * G4;  // one wave per (tile, quad)
   if (n <= 0) return hipSuccess;
-  k_dequant_f16<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(sg, col_map, G, G4, K, tl0, ntl, n0, n1, out);
+  k_dequant_f16<<<(unsigned)n, 64, 0, st>>>(sg, col_map, G, G4, K, tl0, ntl, n0, n1, out);
   return hipGetLastError();
 }
 
