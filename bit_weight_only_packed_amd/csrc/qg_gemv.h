@@ -59,6 +59,10 @@ __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, 
       }
     }
   }
+  // the lane's row of the class-factor table, before the code loads
+  uint4 tf = make_uint4(0u, 0u, 0u, 0u), ti = tf;
+  if constexpr (!MX) stage_tab<B>(lane & 3, tf, ti);
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t cw[NQ][4 * B];
   uint2 sc[NQ];
   {
@@ -111,7 +115,7 @@ __device__ __forceinline__ float gemv_q_wave(const GvArgs& a, const SegDev& sd, 
     }
     return R * pow2f((B == 6 ? 12 : 14) - e);  // the products carry 2^(e - 14) (E2M1) or 2^(e - 12) (E3M2)
   }
-  const int e = stage_wave<B, XF, NQ>(xv, xl, xq, lane, nvalid);
+  const int e = stage_wave<B, XF, NQ>(xv, xl, xq, lane, nvalid, tf, ti);
   // ---- compute
 #pragma unroll
   for (int u = 0; u < NQ; ++u) {

@@ -85,25 +85,53 @@ __device__ __forceinline__ uint32_t sel4(int pos, uint32_t a, uint32_t b, uint32
   return b1 ? hi : lo;
 }
 
+// The fp16x2 class factors 2^-p and their inverses 2^p of pairs 4 pos + k
+// (pos = 0..3, k = 0..3) for codes of 2, 3 and 4 bits, as a table each lane
+// reads its position's row of (two 16-byte loads, issued with the weight
+// loads) instead of selecting among immediates.
+struct StageTab {
+  uint32_t v[3][2][4][4];  // [bits - 2][0: factor, 1: inverse][pos][k]
+};
+template <int B> constexpr void stage_tab_fill(StageTab& t) {
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t p = (uint32_t)Pair<B>::cls(i);
+    t.v[B - 2][0][i >> 2][i & 3] = ((15u - p) << 10) * 0x10001u;
+    t.v[B - 2][1][i >> 2][i & 3] = ((15u + p) << 10) * 0x10001u;
+  }
+}
+constexpr StageTab make_stage_tab() {
+  StageTab t{};
+  stage_tab_fill<2>(t);
+  stage_tab_fill<3>(t);
+  stage_tab_fill<4>(t);
+  return t;
+}
+static __constant__ __align__(16) StageTab kStageTab = make_stage_tab();
+
 // Per-thread constants of the staging: pos = the thread's 16-byte position
 // within its quarter (4 consecutive lanes hold one quarter, pos = 0..3 in lane
 // order), e = the workgroup's block exponent.
+// a lane's row of the table (pos = its position in the quarter).  Issued
+// before the wave's code loads, so waiting for it never waits for them.
+template <int B>
+__device__ __forceinline__ void stage_tab(int pos, uint4& fv, uint4& iv) {
+  constexpr int bi = (B >= 2 && B <= 4) ? B - 2 : 0;  // (other widths never stage classes)
+  fv = *reinterpret_cast<const uint4*>(&kStageTab.v[bi][0][pos][0]);
+  iv = *reinterpret_cast<const uint4*>(&kStageTab.v[bi][1][pos][0]);
+}
+
 template <int B>
 struct StageK {
   uint32_t f[4];    // fp16x2 class factors 2^(e - p) of the pairs 4 pos + k
   uint32_t inv[4];  // fp16x2 2^p of the same pairs
   int sh[4];        // e - p (the fp32 path)
-  __device__ __forceinline__ StageK(int pos, int e) {
+  __device__ __forceinline__ StageK(int pos, int e, const uint4& fv, const uint4& iv) {
     using P = Pair<B>;
+    const uint32_t de = (uint32_t)(e * 0x04000400);  // exponent field + e in both halves
+    f[0] = fv.x + de; f[1] = fv.y + de; f[2] = fv.z + de; f[3] = fv.w + de;
+    inv[0] = iv.x; inv[1] = iv.y; inv[2] = iv.z; inv[3] = iv.w;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      f[k] = sel4(pos, class_scale_pair<B>(k), class_scale_pair<B>(4 + k), class_scale_pair<B>(8 + k),
-                  class_scale_pair<B>(12 + k)) +
-             (uint32_t)(e * 0x04000400);  // exponent field + e in both halves
-      inv[k] = sel4(pos, class_unscale_pair<B>(k), class_unscale_pair<B>(4 + k), class_unscale_pair<B>(8 + k),
-                    class_unscale_pair<B>(12 + k));
-      sh[k] = e - (int)sel4(pos, P::cls(k), P::cls(4 + k), P::cls(8 + k), P::cls(12 + k));
-    }
+    for (int k = 0; k < 4; ++k) sh[k] = e - (int)sel4(pos, P::cls(k), P::cls(4 + k), P::cls(8 + k), P::cls(12 + k));
   }
 };
 
@@ -140,9 +168,11 @@ __device__ __forceinline__ uint4 stage8(const uint4 (&v)[XIn<XF>::W], const Stag
 
 // Stage a wave's nu units of 8 activations (v[r] = unit lane + 64 r of the
 // wave's region, quarter position lane & 3; nu <= NU, wave-uniform) into its LDS region: staged words at xl[unit], quarter sums at
-// xq[unit / 4].  Returns the block exponent e.  Every lane of the wave takes part.
+// xq[unit / 4]; fv, iv: the lane's row of the class-factor table (stage_tab).
+// Returns the block exponent e.  Every lane of the wave takes part.
 template <int B, bool XF, int NU>
-__device__ __forceinline__ int stage_wave(const uint4 (&v)[NU][XIn<XF>::W], uint4* xl, float* xq, int lane, int nu) {
+__device__ __forceinline__ int stage_wave(const uint4 (&v)[NU][XIn<XF>::W], uint4* xl, float* xq, int lane, int nu,
+                                          const uint4& fv, const uint4& iv) {
   uint32_t mx = 0;
 #pragma unroll
   for (int r = 0; r < NU; ++r) {
@@ -150,7 +180,7 @@ __device__ __forceinline__ int stage_wave(const uint4 (&v)[NU][XIn<XF>::W], uint
     mx = max(mx, maxbits8<XF>(v[r]));
   }
   const int e = block_exp<XF>(wave_max(mx));
-  const StageK<B> K(lane & 3, e);
+  const StageK<B> K(lane & 3, e, fv, iv);
 #pragma unroll
   for (int r = 0; r < NU; ++r) {
     if (r >= nu) break;

@@ -207,11 +207,15 @@ __device__ __forceinline__ void sk_body(const SkArgs& a, const SegDev (&sd)[2], 
       xv[r][k] = make_uint4(q.x, q.y, q.z, q.w);
     }
   }
+  // the lane's row of the class-factor table, before the code loads
+  uint4 tf, ti;
+  stage_tab<B>(lane & 3, tf, ti);
+  __builtin_amdgcn_sched_barrier(0);
   SkPipe<B, ND> pp;
   sk_prime<B, ND>(pp, sd, v0, v1, lane);
   uint4* xl = reinterpret_cast<uint4*>(wsm);
   float* xsl = reinterpret_cast<float*>(wsm + (size_t)a.runq * 1024);
-  const int e = stage_wave<B, XF, SK_UPW>(xv, xl, xsl, lane, nq);
+  const int e = stage_wave<B, XF, SK_UPW>(xv, xl, xsl, lane, nq, tf, ti);
   sk_run<B, ND, ONE>(a, pp, v0, v1, sd[0].tile0, xl, xsl, pow2f(24 - e), lane);
 }
 
