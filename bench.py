@@ -61,6 +61,12 @@ def parse():
     p.add_argument("--profile-mlp", type=int, default=0, metavar="REPS",
                    help="profiling mode: REPS graph replays of the fused mixed-width MLP at --profile-rows rows "
                         "(1, 8 or 32) over weight copies of >= 1 GiB, then exit")
+    p.add_argument("--profile-prefill", type=int, default=0, metavar="REPS",
+                   help="profiling mode: REPS graph replays of the prefill route (dequantise, then the fp16 "
+                        "GEMM) on the 5120x17408 shape at --prefill-rows rows over all weight copies, then a "
+                        "256 MiB device copy (the counter calibration), then exit")
+    p.add_argument("--prefill-rows", type=int, default=256, choices=(256, 1024, 2048), metavar="M",
+                   help="rows of the profiled prefill call")
     p.add_argument("--profile-trellis", type=int, default=0, metavar="REPS",
                    help="profiling mode: REPS graph replays of the trellis product on the 5120x17408 shape at "
                         "--profile-rows rows (1 or 8) over weight copies of >= 1 GiB, then exit")
@@ -297,6 +303,26 @@ def main():
                           "launches": args.profile_gate * R,
                           "graph_us_per_launch": round(us, 3), "copy_bytes_each_way": cb,
                           "src_hash": src_hash(), "gemv_src_hash": src_hash(GEMV_SOURCES)}), flush=True)
+        return
+
+    if args.profile_prefill:
+        # the prefill route alone, launched as the prefill timing below launches it
+        Mp = args.prefill_rows
+        wsb = torch.empty(lins[0][4].prefill_workspace()[1], dtype=torch.uint8, device=dev)
+        xp = df16(S.activations(Mp, 5120, cfg_id=S.CFG_DECODE, tensor_id=S.T_X + 1000 + Mp))
+        yp = torch.empty((Mp, shapes[4]["N"]), dtype=torch.float16, device=dev)
+
+        def prefill_all():
+            for r in range(R):
+                lins[r][4].run_prefill(xp, out=yp, workspace=wsb)
+        g = capture(prefill_all)
+        time_graph(g, 2)
+        t = time_graph(g, args.profile_prefill)
+        us = t / (args.profile_prefill * R) * 1e6
+        cb = calibration_copies()
+        print(json.dumps({"profile": f"prefill route M={Mp} 5120x17408 (dequantise + fp16 GEMM)",
+                          "calls": args.profile_prefill * R, "graph_us_per_call": round(us, 3),
+                          "copy_bytes_each_way": cb, "src_hash": src_hash()}), flush=True)
         return
 
     # ---------------- the timed step: layer set at M = 1 ----------------
