@@ -669,7 +669,7 @@ def main():
         wsb = torch.empty(full, dtype=torch.uint8, device=dev)
         wf = wsb[32 << 20:(32 << 20) + N * K * 2].view(torch.float16).view(N, K)
         pres = {"K": K, "N": N, "weight_bytes": lins[0][ig].weight_bytes(), "copies": R}
-        for M in (64, 256, 1024, 2048):
+        for M in (64, 192, 256, 1024, 2048):
             xp = df16(S.activations(M, K, cfg_id=S.CFG_DECODE, tensor_id=S.T_X + 1000 + M))
             yp = torch.empty((M, N), dtype=torch.float16, device=dev)
 

@@ -1129,13 +1129,26 @@ constexpr size_t kPrefillGemmWs = (size_t)32 << 20;  // hipBLASLt workspace at t
 }
 
 // Rows up to which qgemv_run_prefill runs the verify GEMM in chunks of up to
-// 32 rows instead of dequantising the matrix: measured on MI355X (3-bit,
-// group 128), the chunks win up to 192 rows on 5120x17408, 256 on 17408x5120,
-// 128 on 5120x5120 and 64 on 5120x1024 -- the dequantisation's fixed cost
-// grows with the matrix, a chunk's cost with its bytes.  32 rows per 1280 of
-// sqrt(N K), at most 256; 0 below about 1.6 M weights.
+// 32 rows instead of dequantising the matrix.  Measured on MI355X (3-bit,
+// group 128, both sides graph-timed over weight copies of 1 GiB), as
+// (N, K): the chunks win up to 128 rows on (17408, 5120), 224 on
+// (5120, 17408), 64 on (5120, 5120) and (1024, 5120).  A chunk costs about
+// its codes' decode; the route a dequantisation that grows with N K plus a
+// GEMM that hipBLASLt runs slower on a deep K than on a wide N, so shapes of
+// one N K cross at different row counts.  Elsewhere: 32 rows per 2048 of
+// sqrt(N K), at most 256; 0 below about 4.2 M weights.
+namespace {
+struct PrefillTuned {
+  int N, K, rows;
+};
+constexpr PrefillTuned kPrefillTuned[] = {
+    {17408, 5120, 128}, {5120, 17408, 224}, {5120, 5120, 64}, {1024, 5120, 64}};
+}  // namespace
+
 static int prefill_chunk_rows(const qg_plan* h) {
-  const int c = (int)(std::sqrt((double)h->N * (double)h->K) / 1280.0);
+  for (const PrefillTuned& t : kPrefillTuned)
+    if (t.N == h->N && t.K == h->K) return t.rows;
+  const int c = (int)(std::sqrt((double)h->N * (double)h->K) / 2048.0);
   return 32 * std::min(c, 8);
 }
 

@@ -255,9 +255,10 @@ qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t*
  * moves with the model shape).  Above the crossover the weights are
  * dequantised to fp16 -- each w = (c - o) * s rounded once (RNE) -- and
  * multiplied by a plain fp16 GEMM with fp32 accumulation (hipBLASLt).  Up to
- * it -- 32 rows per 1280 of sqrt(N K), at most 256 rows (measured on the
- * 27B-class shapes: 192 rows on 5120x17408, 256 on 17408x5120, 128 on
- * 5120x5120, 64 on 5120x1024; none below about 1.6 M weights) -- the rows go
+ * it -- measured on the 27B-class shapes, as (N, K): 128 rows on
+ * (17408, 5120), 224 on (5120, 17408), 64 on (5120, 5120) and (1024, 5120);
+ * elsewhere 32 rows per 2048 of sqrt(N K), at most 256, none below about
+ * 4.2 M weights -- the rows go
  * through the verify GEMM of qgemv_run, 32 at a time (max_M of at least 16
  * at a time), on the handle's own workspace and without rounding the weights.
  * x: device fp16 [M][K]; y: device fp16 [M][N]; both 16-byte aligned.

@@ -124,9 +124,12 @@ def test_bad_arguments():
         t.prefill_workspace()
 
 
-@pytest.mark.parametrize("N,K,M", [(17408, 5120, 64), (5120, 5120, 100), (5120, 17408, 33)])
+@pytest.mark.parametrize("N,K,M", [(17408, 5120, 128), (5120, 5120, 63), (5120, 17408, 200), (1024, 5120, 64),
+                                   (4096, 4096, 50)])
 def test_chunked_rows_below_the_crossover(N, K, M):
-    """Up to the crossover (32 rows per 1280 of sqrt(N K)) the rows run as the
+    """Up to the crossover (measured on the 27B-class shapes, as (N, K):
+    128 rows on (17408, 5120), 224 on (5120, 17408), 64 on (5120, 5120) and
+    (1024, 5120); elsewhere 32 rows per 2048 of sqrt(N K)) the rows run as the
     verify GEMM, 32 at a time: the result equals qgemv_run on each 32-row
     block bit for bit (the last block ragged), matches the oracle on sampled
     columns, and leaves the caller's workspace untouched."""
@@ -141,6 +144,25 @@ def test_chunked_rows_below_the_crossover(N, K, M):
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), torch.cat(parts).view(torch.int16))
     assert bool((ws == 0x5A).all())
+    rows = np.random.default_rng(M).choice(N, 64, replace=False)
+    err = O.normwise_rel_err(y.cpu().numpy().astype(np.float64)[:, rows], m.ref(x_np, rows))
+    say("err", err)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("N,K,M", [(17408, 5120, 129), (1024, 5120, 65), (4096, 4096, 65)])
+def test_route_above_the_crossover(N, K, M):
+    """One row past the crossover the weights are dequantised into the
+    caller's workspace and multiplied there; the result matches the oracle on
+    sampled columns."""
+    m = Uniform(N, K, 3, cfg_id=186, tid=M)
+    x_np = S.activations(M, K, cfg_id=186, tensor_id=M)
+    _, full = m.lin.prefill_workspace()
+    ws = torch.full((full,), 0x5A, dtype=torch.uint8, device="cuda")
+    say("prefill route", N, K, M)
+    y = m.lin.run_prefill(dev_f16(x_np), workspace=ws)
+    torch.cuda.synchronize()
+    assert not bool((ws == 0x5A).all())
     rows = np.random.default_rng(M).choice(N, 64, replace=False)
     err = O.normwise_rel_err(y.cpu().numpy().astype(np.float64)[:, rows], m.ref(x_np, rows))
     say("err", err)
