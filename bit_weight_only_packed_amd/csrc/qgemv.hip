@@ -1129,27 +1129,36 @@ constexpr size_t kPrefillGemmWs = (size_t)32 << 20;  // hipBLASLt workspace at t
 }
 
 // Rows up to which qgemv_run_prefill runs the verify GEMM in chunks of up to
-// 32 rows instead of dequantising the matrix.  Measured on MI355X (3-bit,
-// group 128, both sides graph-timed over weight copies of 1 GiB), as
-// (N, K): the chunks win up to 128 rows on (17408, 5120), 224 on
-// (5120, 17408), 64 on (5120, 5120) and (1024, 5120).  A chunk costs about
-// its codes' decode; the route a dequantisation that grows with N K plus a
-// GEMM that hipBLASLt runs slower on a deep K than on a wide N, so shapes of
-// one N K cross at different row counts.  Elsewhere: 32 rows per 2048 of
-// sqrt(N K), at most 256; 0 below about 4.2 M weights.
+// 32 rows instead of dequantising the matrix.  Measured on MI355X (both sides
+// graph-timed over weight copies of 1 GiB), as (N, K) and per format class
+// (uniform codes at group 128 of any width / groups of 64 or 32 / MXFP4 /
+// MXFP6): the chunks win up to 128 / 96 / 64 / 64 rows on (17408, 5120),
+// 224 / 160 / 128 / 96 on (5120, 17408), 64 on (5120, 5120) in every class,
+// and 64 on (1024, 5120) at group 128.  A chunk costs about its codes'
+// decode, dearer for the scale groups and MX elements; the route a
+// dequantisation that grows with N K plus a GEMM that hipBLASLt runs slower
+// on a deep K than on a wide N, so shapes of one N K cross at different row
+// counts.  Elsewhere: 32 rows per 2048 of sqrt(N K), at most 256, times 3/4
+// for groups of 64 or 32 and 1/2 for MX elements, rounded down to 32 rows
+// (0: the route from one row).
 namespace {
 struct PrefillTuned {
-  int N, K, rows;
+  int N, K;
+  int rows[4];  // per format class; -1: not measured (the rule above)
 };
-constexpr PrefillTuned kPrefillTuned[] = {
-    {17408, 5120, 128}, {5120, 17408, 224}, {5120, 5120, 64}, {1024, 5120, 64}};
+constexpr PrefillTuned kPrefillTuned[] = {{17408, 5120, {128, 96, 64, 64}},
+                                          {5120, 17408, {224, 160, 128, 96}},
+                                          {5120, 5120, {64, 64, 64, 64}},
+                                          {1024, 5120, {64, -1, -1, -1}}};
 }  // namespace
 
 static int prefill_chunk_rows(const qg_plan* h) {
+  const int f = h->format == QG_FMT_MXFP4 ? 2 : h->format == QG_FMT_MXFP6 ? 3 : (h->group_size < QG_GROUP ? 1 : 0);
   for (const PrefillTuned& t : kPrefillTuned)
-    if (t.N == h->N && t.K == h->K) return t.rows;
-  const int c = (int)(std::sqrt((double)h->N * (double)h->K) / 2048.0);
-  return 32 * std::min(c, 8);
+    if (t.N == h->N && t.K == h->K && t.rows[f] >= 0) return t.rows[f];
+  const int c = std::min(8, (int)(std::sqrt((double)h->N * (double)h->K) / 2048.0));
+  const int quarters = c * (f == 0 ? 4 : f == 1 ? 3 : 2);  // in quarters of 32 rows
+  return 32 * (quarters / 4);
 }
 
 qg_status qgemv_prefill_workspace(qg_handle h, size_t* min_bytes, size_t* full_bytes) {

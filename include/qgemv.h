@@ -255,10 +255,13 @@ qg_status qmlp_run(qg_handle gate, qg_handle up, qg_handle down, const uint16_t*
  * moves with the model shape).  Above the crossover the weights are
  * dequantised to fp16 -- each w = (c - o) * s rounded once (RNE) -- and
  * multiplied by a plain fp16 GEMM with fp32 accumulation (hipBLASLt).  Up to
- * it -- measured on the 27B-class shapes, as (N, K): 128 rows on
- * (17408, 5120), 224 on (5120, 17408), 64 on (5120, 5120) and (1024, 5120);
- * elsewhere 32 rows per 2048 of sqrt(N K), at most 256, none below about
- * 4.2 M weights -- the rows go
+ * it -- measured on the 27B-class shapes, as (N, K), for uniform codes at
+ * group 128 / groups of 64 or 32 / MXFP4 / MXFP6: 128 / 96 / 64 / 64 rows on
+ * (17408, 5120), 224 / 160 / 128 / 96 on (5120, 17408), 64 on (5120, 5120),
+ * 64 on (1024, 5120) at group 128; elsewhere 32 rows per 2048 of sqrt(N K),
+ * at most 256, times 3/4 for groups of 64 or 32 and 1/2 for MX elements,
+ * rounded down to a multiple of 32 (none below about 4.2 M weights) -- the
+ * rows go
  * through the verify GEMM of qgemv_run, 32 at a time (max_M of at least 16
  * at a time), on the handle's own workspace and without rounding the weights.
  * x: device fp16 [M][K]; y: device fp16 [M][N]; both 16-byte aligned.

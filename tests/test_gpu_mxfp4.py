@@ -161,3 +161,19 @@ def test_full_size_gate_shape(M):
     err = O.normwise_rel_err(y.cpu().numpy().astype(np.float64)[:, rows], m.ref(x_np, rows))
     say("mxfp4 full", M, err)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("M,chunked", [(32, True), (33, False)])
+def test_prefill_crossover(M, chunked):
+    """Outside the measured shapes the crossover is the generic rule halved for
+    MX elements: 32 rows on 4096x4096 (64 at group 128).  Up to it the rows run
+    as the verify GEMM and leave the caller's workspace untouched; past it they
+    are dequantised there.  Both match the oracle on sampled columns."""
+    m = MX(4096, 4096, tid=9)
+    x_np = S.activations(M, m.K, cfg_id=215, tensor_id=M)
+    ws = torch.full((m.lin.prefill_workspace()[1],), 0x5A, dtype=torch.uint8, device="cuda")
+    y = m.lin.run_prefill(dev_f16(x_np), workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((ws == 0x5A).all()) == chunked
+    rows = np.random.default_rng(M).choice(m.N, 64, replace=False)
+    assert O.normwise_rel_err(y.cpu().numpy().astype(np.float64)[:, rows], m.ref(x_np, rows)) <= TOL
